@@ -1,0 +1,272 @@
+"""Benchmark: causal self-attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+
+Workload (the one the headline metric is quoted on): B=2, H=32, S=32768, d=128,
+bf16, causal, one attn_fwd_partial call (balanced schedule) and one attn_bwd
+call per step.  A step is one forward + backward pass over one batch.
+Throughput counts 4*S*S*d per (b, h) for the forward, halved for causal, and
+2.5x that for the backward: 61.572 TFLOP per step.
+
+Prints one JSON line.  Besides the contract fields it carries:
+  roofline      the backward call (the dominant cost): algorithmic FLOPs per call
+                over its average duration, timed with HIP events on the stream it
+                runs on, against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  kernels       per-call timings (forward call, backward call);
+  secondary     the other workloads: the 128K sequence shard forward over 32
+                chunks, its backward, and split-KV GQA decode (GB/s of K/V);
+  cpu_baseline  the fp64 oracle on a bounded sample (one head, a 12288-token
+                causal prefix, forward + backward) on the host's cores.
+Inputs are seeded synthetic N(0,1) values generated on the device and rounded
+to bf16; they are resident in HBM before timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+
+
+def causal_flops(b, h, s, d):
+    return 4.0 * s * s * d * b * h / 2.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode"], default=None,
+                    help="run a single workload (for profiling)")
+    return ap.parse_args()
+
+
+def randn_bf16(shape, gen):
+    import torch
+
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def time_calls(fns, steps, warmup, stream):
+    """Run each step's calls in order; returns per-call average ms and the wall ms per step."""
+    import torch
+
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(fns))]
+    return per, wall
+
+
+def bench_main(args, stream):
+    import torch
+
+    from exact_blockwise_attention_attn_amd import shard
+
+    B, H, S, D = 2, 32, 32768, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    q, k, v, do = (randn_bf16((B, S, H, D), g) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.empty((B, S, H, D), dtype=torch.float32, device="cuda")
+    delta = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        shard.causal_attention_forward(q, k, v, balanced=True, o=o, lse=lse, stream=stream)
+
+    def bwd():
+        shard.causal_attention_backward(q, k, v, o, do, lse, balanced=True, stream=stream, dq=dq, dk=dk, dv=dv,
+                                        dq_acc=dq_acc, delta=delta)
+
+    (t_f, t_b), wall = time_calls([fwd, bwd], args.steps, args.warmup, stream)
+    f_fwd = causal_flops(B, H, S, D)
+    f_bwd = 2.5 * f_fwd
+    return {
+        "B": B, "H": H, "S": S, "D": D, "fwd_ms": t_f, "bwd_ms": t_b, "step_ms": wall, "event_ms": t_f + t_b,
+        "flops_step": f_fwd + f_bwd, "fwd_tflops": f_fwd / t_f / 1e9, "bwd_tflops": f_bwd / t_b / 1e9,
+        "tflops": (f_fwd + f_bwd) / wall / 1e9,
+    }
+
+
+def bench_shard(args, stream, do_bwd):
+    import torch
+
+    from exact_blockwise_attention_attn_amd import shard
+
+    H, D, SQ, SK, CH, QP = 32, 128, 4096, 131072, 4096, 65536
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    q = randn_bf16((1, SQ, H, D), g)
+    k = randn_bf16((1, SK, H, D), g)
+    v = randn_bf16((1, SK, H, D), g)
+    o_run = torch.empty((1, SQ, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, H, SQ), dtype=torch.float32, device="cuda")
+    o = torch.empty((1, SQ, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def fwd():
+        shard.shard_forward(q, k, v, CH, q_pos0=QP, causal=True, stream=stream, o_run=o_run, lse=lse, o_out=o)
+
+    f_fwd = 4.0 * SQ * SK * D * H / 2.0  # the stated convention: halved for causal
+    if not do_bwd:
+        (t,), _ = time_calls([fwd], max(3, args.steps), 1, stream)
+        return {"workload": "shard_fwd_128k", "ms": t, "tflops": f_fwd / t / 1e9,
+                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": 17}
+    fwd()
+    do = randn_bf16((1, SQ, H, D), g)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.empty((1, SQ, H, D), dtype=torch.float32, device="cuda")
+    delta = torch.empty((1, H, SQ), dtype=torch.float32, device="cuda")
+
+    def bwd():
+        shard.shard_backward(q, k, v, o, do, lse, CH, q_pos0=QP, causal=True, stream=stream, dq=dq, dk=dk, dv=dv,
+                             dq_acc=dq_acc, delta=delta)
+
+    (t,), _ = time_calls([bwd], max(3, args.steps), 1, stream)
+    f_bwd = 2.5 * f_fwd
+    return {"workload": "shard_bwd_128k", "ms": t, "tflops": f_bwd / t / 1e9,
+            "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+
+
+def bench_decode(args, stream):
+    import torch
+
+    from exact_blockwise_attention_attn_amd import binding
+
+    B, HQ, HKV, L, D, NS = 16, 32, 8, 131072, 128, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    q = randn_bf16((B, HQ, D), g)
+    kc = randn_bf16((B, L, HKV, D), g)
+    vc = randn_bf16((B, L, HKV, D), g)
+    o = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, HQ), dtype=torch.float32, device="cuda")
+    ws = torch.empty(binding.attn_decode_workspace_size(B, HQ, D, NS), dtype=torch.uint8, device="cuda")
+
+    def dec():
+        binding.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=NS, stream=stream)
+
+    (t,), _ = time_calls([dec], max(10, args.steps), 3, stream)
+    kv_bytes = 2.0 * B * L * HKV * D * 2
+    gbs = kv_bytes / t / 1e6
+    return {"workload": "decode_gqa_128k", "ms": t, "kv_bytes": kv_bytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
+def cpu_baseline():
+    """The fp64 oracle on a bounded sample: one (b, h), causal prefix of 12288 tokens, fwd + bwd."""
+    import numpy as np
+
+    import oracle
+    from seeded_inputs import bf16_bits_to_f32, normal_bf16
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    S, D = 12288, 128
+    x = [bf16_bits_to_f32(normal_bf16(5, t, 1, (S, 1, D))[0, :, 0]).astype(np.float64) for t in range(4)]
+    c = 1 / math.sqrt(D)
+    t0 = time.perf_counter()
+    O, L = oracle.attention_head(x[0], x[1], x[2], c, True)
+    oracle.attention_backward_head(x[0], x[1], x[2], O, x[3], L, c, True)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * causal_flops(1, 1, S, D)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one (batch, head), causal prefix of {S} tokens, d={D}, forward + backward, fp64 NumPy; "
+                      f"{dt:.1f} s for {flops / 1e9:.1f} GFLOP (same FLOP convention)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from exact_blockwise_attention_attn_amd import binding
+
+    binding.load(build_if_missing=False)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    if args.only == "shard_fwd":
+        print(json.dumps(bench_shard(args, stream, False)), flush=True)
+        return
+    if args.only == "shard_bwd":
+        print(json.dumps(bench_shard(args, stream, True)), flush=True)
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode(args, stream)), flush=True)
+        return
+
+    m = bench_main(args, stream)
+    print(f"# main: fwd {m['fwd_ms']:.2f} ms ({m['fwd_tflops']:.0f} TF/s), bwd {m['bwd_ms']:.2f} ms "
+          f"({m['bwd_tflops']:.0f} TF/s)", file=sys.stderr, flush=True)
+    secondary = {}
+    if not args.no_secondary and args.only is None:
+        torch.cuda.empty_cache()
+        secondary["shard_fwd_128k"] = bench_shard(args, stream, False)
+        torch.cuda.empty_cache()
+        secondary["shard_bwd_128k"] = bench_shard(args, stream, True)
+        torch.cuda.empty_cache()
+        secondary["decode_gqa_128k"] = bench_decode(args, stream)
+        torch.cuda.empty_cache()
+    cpu = None if (args.no_cpu_baseline or args.only) else cpu_baseline()
+    bwd_achieved = m["bwd_tflops"]
+    line = {
+        "metric": "attention TFLOP/s fwd+bwd (causal, d=128, bf16)",
+        "value": round(m["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["step_ms"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal_fwdbwd_32k", "batch": m["B"], "heads": m["H"], "seq_len": m["S"],
+                   "head_dim": m["D"], "causal": True, "schedule": "balanced", "parallelism": "single GPU"},
+        "frac_of_mfma_peak": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd call (delta + dK/dV + dQ kernels)",
+                     "achieved": round(bwd_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "kernels": {"fwd_call_ms": round(m["fwd_ms"], 3), "bwd_call_ms": round(m["bwd_ms"], 3),
+                    "fwd_tflops": round(m["fwd_tflops"], 2), "bwd_tflops": round(m["bwd_tflops"], 2),
+                    "event_ms_per_step": round(m["event_ms"], 3)},
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

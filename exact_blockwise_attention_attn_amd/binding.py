@@ -1,0 +1,294 @@
+"""Thin ctypes binding of libattn (include/attn.h).
+
+Argument marshalling only: each function takes PyTorch tensors (device memory
+and the current stream are PyTorch's), checks nothing beyond what is needed to
+fill the C argument struct, and calls the C entry point of the same name.  All
+arithmetic happens in the HIP kernels.  A nonzero status raises ``AttnError``
+carrying ``attn_last_error()``.
+
+The library is loaded from the package directory; if it has not been built
+yet it is built once.  There is no fallback: without the library every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+c_i32, c_u32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+I64x3 = c_i64 * 3
+I64x2 = c_i64 * 2
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_WORKSPACE = 3
+ATTN_ERR_HIP = 4
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+ATTN_FWD_ACCUMULATE = 1 << 0
+ATTN_FWD_BALANCED = 1 << 1
+ATTN_MERGE_SEQUENTIAL = 0
+ATTN_MERGE_TREE = 1
+ATTN_BWD_COMPUTE_DELTA = 1 << 0
+ATTN_BWD_DQ_OVERWRITE = 1 << 1
+ATTN_BWD_FINALIZE_DQ = 1 << 2
+ATTN_BWD_BALANCED = 1 << 3
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("dtype", c_u32),
+        ("batch", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32),
+        ("seqlen_q", c_i32), ("seqlen_k", c_i32), ("head_dim", c_i32),
+        ("q", c_vp), ("q_stride", I64x3),
+        ("k", c_vp), ("k_stride", I64x3),
+        ("v", c_vp), ("v_stride", I64x3),
+        ("o", c_vp), ("o_stride", I64x3), ("o_dtype", c_u32),
+        ("lse", c_vp),
+        ("o_final", c_vp), ("o_final_stride", I64x3),
+        ("q_pos0", c_i64), ("k_pos0", c_i64),
+        ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+    ]
+
+
+class MergeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("n_parts", c_i32),
+        ("batch", c_i32), ("seqlen", c_i32), ("heads", c_i32), ("head_dim", c_i32),
+        ("o_parts", c_vp), ("o_part_stride", c_i64), ("o_stride", I64x3),
+        ("lse_parts", c_vp), ("lse_part_stride", c_i64),
+        ("o_out", c_vp), ("o_out_stride", I64x3), ("o_out_dtype", c_u32),
+        ("lse_out", c_vp), ("mode", c_u32),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("dtype", c_u32),
+        ("batch", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32),
+        ("seqlen_q", c_i32), ("seqlen_k", c_i32), ("head_dim", c_i32),
+        ("q", c_vp), ("q_stride", I64x3),
+        ("k", c_vp), ("k_stride", I64x3),
+        ("v", c_vp), ("v_stride", I64x3),
+        ("o", c_vp), ("o_stride", I64x3),
+        ("dout", c_vp), ("do_stride", I64x3),
+        ("lse", c_vp), ("delta", c_vp), ("dq_acc", c_vp),
+        ("dq", c_vp), ("dq_stride", I64x3),
+        ("dk", c_vp), ("dk_stride", I64x3),
+        ("dv", c_vp), ("dv_stride", I64x3),
+        ("q_pos0", c_i64), ("k_pos0", c_i64),
+        ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32),
+        ("batch", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32), ("head_dim", c_i32),
+        ("cache_len", c_i64),
+        ("q", c_vp), ("q_stride", I64x2),
+        ("k_cache", c_vp), ("k_stride", I64x3),
+        ("v_cache", c_vp), ("v_stride", I64x3),
+        ("seqlens", c_vp), ("n_splits", c_i32), ("scale", c_f32),
+        ("o", c_vp), ("o_stride", I64x2),
+        ("lse", c_vp),
+        ("workspace", c_vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTED = [
+    "attn_fwd_partial",
+    "attn_merge_lse",
+    "attn_bwd",
+    "attn_decode_splitkv",
+    "attn_decode_workspace_size",
+    "attn_status_string",
+    "attn_last_error",
+    "attn_abi_version",
+]
+
+_lib = None
+_lock = threading.Lock()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _build.LIB_PATH
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load libattn.so (building it first if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            if not build_if_missing:
+                raise FileNotFoundError(f"{path} is not built")
+            _build.build()
+        lib = ctypes.CDLL(path)
+        for name, argt in (("attn_fwd_partial", [ctypes.POINTER(FwdArgs), c_vp]),
+                           ("attn_merge_lse", [ctypes.POINTER(MergeArgs), c_vp]),
+                           ("attn_bwd", [ctypes.POINTER(BwdArgs), c_vp]),
+                           ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp])):
+            fn = getattr(lib, name)
+            fn.argtypes = argt
+            fn.restype = ctypes.c_int
+        lib.attn_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
+        lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_abi_version.argtypes = []
+        lib.attn_abi_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        msg = load().attn_last_error().decode()
+        raise AttnError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _strides3(t: torch.Tensor | None):
+    if t is None:
+        return I64x3(0, 0, 0)
+    assert t.dim() == 4, "expected a [B, S, H, D] tensor"
+    if t.numel() == 0:  # nothing is read or written; strides of empty views are arbitrary
+        return I64x3(0, 0, 0)
+    assert t.stride(3) == 1, "expected a unit innermost stride"
+    return I64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def attn_abi_version() -> int:
+    return load().attn_abi_version()
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(status).decode()
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def attn_decode_workspace_size(batch: int, heads_q: int, head_dim: int, n_splits: int) -> int:
+    return load().attn_decode_workspace_size(batch, heads_q, head_dim, n_splits)
+
+
+def attn_fwd_partial(q, k, v, o, lse, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0,
+                     accumulate=False, balanced=False, o_final=None, stream=None) -> None:
+    """q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D], o [B,Sq,Hq,D] (fp32 or bf16), lse fp32 [B,Hq,Sq]."""
+    a = FwdArgs()
+    a.struct_size = ctypes.sizeof(FwdArgs)
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.heads_q, a.head_dim = q.shape
+    a.seqlen_k, a.heads_kv = k.shape[1], k.shape[2]
+    a.q, a.q_stride = _ptr(q), _strides3(q)
+    a.k, a.k_stride = _ptr(k), _strides3(k)
+    a.v, a.v_stride = _ptr(v), _strides3(v)
+    a.o, a.o_stride, a.o_dtype = _ptr(o), _strides3(o), _dtype_code(o)
+    a.lse = _ptr(lse)
+    a.o_final, a.o_final_stride = _ptr(o_final), _strides3(o_final)
+    a.q_pos0, a.k_pos0 = int(q_pos0), int(k_pos0)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = (ATTN_FWD_ACCUMULATE if accumulate else 0) | (ATTN_FWD_BALANCED if balanced else 0)
+    _check(load().attn_fwd_partial(ctypes.byref(a), _stream(stream)))
+
+
+def attn_merge_lse(o_parts, lse_parts, o_out, lse_out, *, tree=False, stream=None) -> None:
+    """o_parts fp32 [n,B,S,H,D], lse_parts fp32 [n,B,H,S] -> o_out [B,S,H,D], lse_out [B,H,S]."""
+    n, B, S, H, D = o_parts.shape
+    assert o_parts.stride(4) == 1 and lse_parts.is_contiguous()
+    a = MergeArgs()
+    a.struct_size = ctypes.sizeof(MergeArgs)
+    a.n_parts, a.batch, a.seqlen, a.heads, a.head_dim = n, B, S, H, D
+    a.o_parts, a.o_part_stride = _ptr(o_parts), o_parts.stride(0)
+    a.o_stride = I64x3(o_parts.stride(1), o_parts.stride(2), o_parts.stride(3))
+    a.lse_parts, a.lse_part_stride = _ptr(lse_parts), lse_parts.stride(0)
+    a.o_out, a.o_out_stride, a.o_out_dtype = _ptr(o_out), _strides3(o_out), _dtype_code(o_out)
+    a.lse_out = _ptr(lse_out)
+    a.mode = ATTN_MERGE_TREE if tree else ATTN_MERGE_SEQUENTIAL
+    _check(load().attn_merge_lse(ctypes.byref(a), _stream(stream)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq=None, q_pos0=0, k_pos0=0, causal=False,
+             scale=0.0, compute_delta=False, dq_overwrite=False, finalize_dq=False, balanced=False,
+             stream=None) -> None:
+    """Backward for one key chunk; see include/attn.h for the contract."""
+    a = BwdArgs()
+    a.struct_size = ctypes.sizeof(BwdArgs)
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.heads_q, a.head_dim = q.shape
+    a.seqlen_k, a.heads_kv = k.shape[1], k.shape[2]
+    a.q, a.q_stride = _ptr(q), _strides3(q)
+    a.k, a.k_stride = _ptr(k), _strides3(k)
+    a.v, a.v_stride = _ptr(v), _strides3(v)
+    a.o, a.o_stride = _ptr(o), _strides3(o)
+    a.dout, a.do_stride = _ptr(dout), _strides3(dout)
+    a.lse, a.delta, a.dq_acc = _ptr(lse), _ptr(delta), _ptr(dq_acc)
+    a.dq, a.dq_stride = _ptr(dq), _strides3(dq)
+    a.dk, a.dk_stride = _ptr(dk), _strides3(dk)
+    a.dv, a.dv_stride = _ptr(dv), _strides3(dv)
+    a.q_pos0, a.k_pos0 = int(q_pos0), int(k_pos0)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+    _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seqlens=None, scale=0.0,
+                        stream=None) -> None:
+    """q [B,Hq,D] bf16, caches [B,L,Hkv,D] bf16 -> o [B,Hq,D] bf16, lse [B,Hq] fp32."""
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.batch, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k_cache.shape[2]
+    a.cache_len = k_cache.shape[1]
+    assert q.stride(2) == 1 and o.stride(2) == 1
+    a.q, a.q_stride = _ptr(q), I64x2(q.stride(0), q.stride(1))
+    a.k_cache, a.k_stride = _ptr(k_cache), _strides3(k_cache)
+    a.v_cache, a.v_stride = _ptr(v_cache), _strides3(v_cache)
+    a.seqlens = _ptr(seqlens)
+    a.n_splits = int(n_splits)
+    a.scale = float(scale)
+    a.o, a.o_stride = _ptr(o), I64x2(o.stride(0), o.stride(1))
+    a.lse = _ptr(lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_decode_splitkv(ctypes.byref(a), _stream(stream)))

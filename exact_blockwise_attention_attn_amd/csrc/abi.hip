@@ -1,0 +1,343 @@
+// C ABI of libattn: argument validation on the host, then dispatch to the
+// kernels.  Validation makes no HIP call, so a failing call enqueues nothing
+// and touches no output, on any machine.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+size_t elem_size(uint32_t dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A [batch, seq, head, dim] view: pointer and strides must keep every row 16-byte aligned.
+int check_view(const char* name, const void* p, const int64_t* st, int n_st, uint32_t dtype, bool needed) {
+  if (!needed) return ATTN_OK;
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(ATTN_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < n_st; ++i) {
+    if (st[i] < 0) return fail(ATTN_ERR_INVALID_ARG, "%s stride[%d] = %lld is negative", name, i, (long long)st[i]);
+    if ((st[i] * (int64_t)elem_size(dtype)) % 16)
+      return fail(ATTN_ERR_UNSUPPORTED, "%s stride[%d] = %lld breaks 16-byte row alignment", name, i,
+                  (long long)st[i]);
+  }
+  return ATTN_OK;
+}
+
+int check_scale(float in, int head_dim, float* out) {
+  if (in == 0.0f) {
+    *out = 1.0f / sqrtf((float)head_dim);
+    return ATTN_OK;
+  }
+  if (!isfinite(in) || in < 0.0f)
+    return fail(ATTN_ERR_INVALID_ARG, "scale must be 0 (default) or finite and positive, got %g", (double)in);
+  *out = in;
+  return ATTN_OK;
+}
+
+int check_dims(int32_t batch, int32_t hq, int32_t hkv, int32_t sq, int32_t sk, int32_t d) {
+  if (batch < 1 || hq < 1 || hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "batch and head counts must be >= 1");
+  if (sq < 0 || sk < 0) return fail(ATTN_ERR_INVALID_ARG, "sequence lengths must be >= 0");
+  if (hq % hkv) return fail(ATTN_ERR_INVALID_ARG, "heads_q (%d) is not a multiple of heads_kv (%d)", hq, hkv);
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d);
+  return ATTN_OK;
+}
+
+#define TRY(x)              \
+  do {                      \
+    int rc_ = (x);          \
+    if (rc_) return rc_;    \
+  } while (0)
+
+attn::View view(const void* p, const int64_t* s) { return attn::View{p, s[0], s[1], s[2]}; }
+attn::MView mview(void* p, const int64_t* s) { return attn::MView{p, s[0], s[1], s[2]}; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_fwd_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_fwd_args));
+  if (a->dtype != ATTN_DTYPE_BF16 && a->dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported", a->dtype);
+  if (a->o_dtype != ATTN_DTYPE_BF16 && a->o_dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %u is not supported", a->o_dtype);
+  if (a->flags & ~(ATTN_FWD_ACCUMULATE | ATTN_FWD_BALANCED))
+    return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
+  const bool accumulate = a->flags & ATTN_FWD_ACCUMULATE;
+  if (accumulate && a->o_dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_FWD_ACCUMULATE needs an fp32 running output");
+  TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim));
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  const bool has_q = a->seqlen_q > 0, has_k = a->seqlen_k > 0;
+  TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
+  TRY(check_view("k", a->k, a->k_stride, 3, a->dtype, has_q && has_k));
+  TRY(check_view("v", a->v, a->v_stride, 3, a->dtype, has_q && has_k));
+  TRY(check_view("o", a->o, a->o_stride, 3, a->o_dtype, has_q));
+  if (has_q && !a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (has_q && !aligned16(a->lse)) return fail(ATTN_ERR_UNSUPPORTED, "lse is not 16-byte aligned");
+  if (a->o_final) TRY(check_view("o_final", a->o_final, a->o_final_stride, 3, ATTN_DTYPE_BF16, has_q));
+  const int64_t units = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64);
+  if (units > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (!has_q) return ok();
+
+  attn::FwdParams p{};
+  p.q = view(a->q, a->q_stride);
+  p.k = view(a->k, a->k_stride);
+  p.v = view(a->v, a->v_stride);
+  p.o = mview(a->o, a->o_stride);
+  p.o_final = mview(a->o_final, a->o_final_stride);
+  p.lse = a->lse;
+  p.B = a->batch;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.Sq = a->seqlen_q;
+  p.Sk = a->seqlen_k;
+  p.group = a->heads_q / a->heads_kv;
+  p.delta = a->q_pos0 - a->k_pos0;
+  p.causal = a->causal != 0;
+  p.o_f32 = a->o_dtype == ATTN_DTYPE_F32;
+  p.accumulate = accumulate;
+  p.balanced = (a->flags & ATTN_FWD_BALANCED) != 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  // A chunk that no query sees leaves a running result unchanged.
+  const bool invisible = a->seqlen_k == 0 || (p.causal && p.delta + (a->seqlen_q - 1) < 0);
+  if (invisible && accumulate && !a->o_final) return ok();
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = a->dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(p, a->head_dim, s)
+                                             : attn::launch_fwd_f32(p, a->head_dim, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd_partial launch");
+  return ok();
+}
+
+int attn_merge_lse(const attn_merge_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_merge_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_merge_args));
+  if (a->n_parts < 1 || a->n_parts > 1024) return fail(ATTN_ERR_INVALID_ARG, "n_parts must be in [1, 1024]");
+  if (a->mode != ATTN_MERGE_SEQUENTIAL && a->mode != ATTN_MERGE_TREE)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown merge mode %u", a->mode);
+  if (a->o_out_dtype != ATTN_DTYPE_BF16 && a->o_out_dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "o_out_dtype %u is not supported", a->o_out_dtype);
+  if (a->batch < 1 || a->heads < 1 || a->seqlen < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "batch and heads must be >= 1, seqlen >= 0");
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", a->head_dim);
+  const bool any = a->seqlen > 0;
+  TRY(check_view("o_parts", a->o_parts, a->o_stride, 3, ATTN_DTYPE_F32, any));
+  TRY(check_view("o_out", a->o_out, a->o_out_stride, 3, a->o_out_dtype, any));
+  if (any && (!a->lse_parts || !a->lse_out)) return fail(ATTN_ERR_INVALID_ARG, "lse_parts or lse_out is NULL");
+  if (any && (!aligned16(a->lse_parts) || !aligned16(a->lse_out)))
+    return fail(ATTN_ERR_UNSUPPORTED, "lse_parts or lse_out is not 16-byte aligned");
+  if (a->n_parts > 1 && (a->o_part_stride <= 0 || a->lse_part_stride <= 0))
+    return fail(ATTN_ERR_INVALID_ARG, "part strides must be positive");
+  if ((a->o_part_stride * 4) % 16) return fail(ATTN_ERR_UNSUPPORTED, "o_part_stride breaks 16-byte alignment");
+  if (!any) return ok();
+  attn::MergeParams p{};
+  p.o_parts = a->o_parts;
+  p.o_part_stride = a->o_part_stride;
+  p.o_sb = a->o_stride[0];
+  p.o_ss = a->o_stride[1];
+  p.o_sh = a->o_stride[2];
+  p.lse_parts = a->lse_parts;
+  p.lse_part_stride = a->lse_part_stride;
+  p.out = mview(a->o_out, a->o_out_stride);
+  p.out_f32 = a->o_out_dtype == ATTN_DTYPE_F32;
+  p.lse_out = a->lse_out;
+  p.n_parts = a->n_parts;
+  p.B = a->batch;
+  p.S = a->seqlen;
+  p.H = a->heads;
+  p.tree = a->mode == ATTN_MERGE_TREE;
+  hipError_t e = attn::launch_merge(p, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_merge_lse launch");
+  return ok();
+}
+
+int attn_bwd(const attn_bwd_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_bwd_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_bwd_args));
+  if (a->dtype != ATTN_DTYPE_BF16 && a->dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported", a->dtype);
+  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED;
+  if (a->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
+  TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim));
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  const bool has_q = a->seqlen_q > 0, has_k = a->seqlen_k > 0;
+  const bool finalize = a->flags & ATTN_BWD_FINALIZE_DQ;
+  TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
+  TRY(check_view("k", a->k, a->k_stride, 3, a->dtype, has_k));
+  TRY(check_view("v", a->v, a->v_stride, 3, a->dtype, has_k));
+  TRY(check_view("o", a->o, a->o_stride, 3, a->dtype, has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)));
+  TRY(check_view("dout", a->dout, a->do_stride, 3, a->dtype, has_q));
+  TRY(check_view("dk", a->dk, a->dk_stride, 3, a->dtype, has_k));
+  TRY(check_view("dv", a->dv, a->dv_stride, 3, a->dtype, has_k));
+  TRY(check_view("dq", a->dq, a->dq_stride, 3, a->dtype, has_q && finalize));
+  if (has_q && (!a->lse || !a->delta || !a->dq_acc))
+    return fail(ATTN_ERR_INVALID_ARG, "lse, delta and dq_acc must not be NULL");
+  if (has_q && (!aligned16(a->lse) || !aligned16(a->delta) || !aligned16(a->dq_acc)))
+    return fail(ATTN_ERR_UNSUPPORTED, "lse, delta and dq_acc must be 16-byte aligned");
+  const int64_t units = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64) +
+                        (int64_t)a->batch * a->heads_kv * ((a->seqlen_k + 63) / 64);
+  if (units > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  attn::BwdParams p{};
+  p.q = view(a->q, a->q_stride);
+  p.k = view(a->k, a->k_stride);
+  p.v = view(a->v, a->v_stride);
+  p.o = view(a->o, a->o_stride);
+  p.dout = view(a->dout, a->do_stride);
+  p.dq = mview(a->dq, a->dq_stride);
+  p.dk = mview(a->dk, a->dk_stride);
+  p.dv = mview(a->dv, a->dv_stride);
+  p.lse = a->lse;
+  p.delta = a->delta;
+  p.dq_acc = a->dq_acc;
+  p.B = a->batch;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.Sq = a->seqlen_q;
+  p.Sk = a->seqlen_k;
+  p.group = a->heads_q / a->heads_kv;
+  p.delta_pos = a->q_pos0 - a->k_pos0;
+  p.causal = a->causal != 0;
+  p.dq_overwrite = (a->flags & ATTN_BWD_DQ_OVERWRITE) != 0;
+  p.finalize_dq = finalize;
+  p.balanced = (a->flags & ATTN_BWD_BALANCED) != 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int D = a->head_dim;
+  const int bf16 = a->dtype == ATTN_DTYPE_BF16;
+  hipError_t e;
+  if (has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)) {
+    e = attn::launch_bwd_delta(p, D, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd delta launch");
+  }
+  // dQ needs a pass unless this chunk is invisible and dq_acc is left as it is.
+  const bool invisible = !has_k || (p.causal && p.delta_pos + (a->seqlen_q - 1) < 0);
+  const int run_dq = has_q && (!invisible || p.dq_overwrite || finalize);
+  e = bf16 ? attn::launch_bwd_bf16(p, D, run_dq, s) : attn::launch_bwd_f32(p, D, run_dq, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  return ok();
+}
+
+size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits) {
+  if (batch < 1 || heads_q < 1 || n_splits < 1 || n_splits > 1024 || (head_dim != 64 && head_dim != 128)) return 0;
+  const size_t rows = (size_t)batch * heads_q * n_splits;
+  const size_t o_bytes = (rows * head_dim * 4 + 255) & ~(size_t)255;
+  return o_bytes + ((rows * 4 + 255) & ~(size_t)255);
+}
+
+int attn_decode_splitkv(const attn_decode_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_decode_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_decode_args));
+  TRY(check_dims(a->batch, a->heads_q, a->heads_kv, 1, 0, a->head_dim));
+  if (a->cache_len < 0) return fail(ATTN_ERR_INVALID_ARG, "cache_len must be >= 0");
+  if (a->n_splits < 1 || a->n_splits > 1024) return fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [1, 1024]");
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  TRY(check_view("q", a->q, a->q_stride, 2, ATTN_DTYPE_BF16, true));
+  TRY(check_view("k_cache", a->k_cache, a->k_stride, 3, ATTN_DTYPE_BF16, a->cache_len > 0));
+  TRY(check_view("v_cache", a->v_cache, a->v_stride, 3, ATTN_DTYPE_BF16, a->cache_len > 0));
+  TRY(check_view("o", a->o, a->o_stride, 2, ATTN_DTYPE_BF16, true));
+  if (!a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (a->seqlens && ((uintptr_t)a->seqlens & 3u)) return fail(ATTN_ERR_UNSUPPORTED, "seqlens is misaligned");
+  const size_t need = attn_decode_workspace_size(a->batch, a->heads_q, a->head_dim, a->n_splits);
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  if ((uintptr_t)a->workspace & 255u) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int group = a->heads_q / a->heads_kv;
+  const int64_t grid = (int64_t)a->batch * a->heads_kv * ((group + 3) / 4) * a->n_splits;
+  if (grid > 0x7fffffffLL || (int64_t)a->batch * a->heads_q > 0x7fffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  attn::DecodeParams p{};
+  p.q = (const uint16_t*)a->q;
+  p.q_sb = a->q_stride[0];
+  p.q_sh = a->q_stride[1];
+  p.k = (const uint16_t*)a->k_cache;
+  p.k_sb = a->k_stride[0];
+  p.k_sl = a->k_stride[1];
+  p.k_sh = a->k_stride[2];
+  p.v = (const uint16_t*)a->v_cache;
+  p.v_sb = a->v_stride[0];
+  p.v_sl = a->v_stride[1];
+  p.v_sh = a->v_stride[2];
+  p.seqlens = a->seqlens;
+  p.L = a->cache_len;
+  p.B = a->batch;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.group = group;
+  p.n_splits = a->n_splits;
+  p.split_len = (a->cache_len + a->n_splits - 1) / a->n_splits;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const size_t rows = (size_t)a->batch * a->heads_q * a->n_splits;
+  p.part_o = (float*)a->workspace;
+  p.part_lse = (float*)((char*)a->workspace + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
+  p.o = (uint16_t*)a->o;
+  p.o_sb = a->o_stride[0];
+  p.o_sh = a->o_stride[1];
+  p.lse = a->lse;
+  hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode_splitkv launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal parameter blocks passed by value to the kernels, and the host-side
+// launchers each kernel file exports to the ABI layer.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// One [batch, seq, head, dim] tensor view: base pointer plus element strides.
+struct View {
+  const void* ptr;
+  int64_t sb, ss, sh;
+};
+
+struct MView {
+  void* ptr;
+  int64_t sb, ss, sh;
+};
+
+struct FwdParams {
+  View q, k, v;
+  MView o;
+  MView o_final;  // ptr == nullptr to skip
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk;
+  int group;        // Hq / Hkv
+  int64_t delta;    // q_pos0 - k_pos0: key j is visible to query i iff j <= delta + i (causal)
+  int causal;
+  int o_f32;        // o is fp32 (else bf16)
+  int accumulate;   // merge into the running (o, lse)
+  int balanced;     // each workgroup takes query tiles t and n-1-t
+  float scale;      // softmax scale (natural units)
+  float scale_log2; // scale * log2(e)
+  int n_qtiles;     // query tiles per (b, h)
+  int n_units;      // work units per (b, h) (n_qtiles, or ceil(n_qtiles / 2) when balanced)
+};
+
+struct MergeParams {
+  const float* o_parts;
+  int64_t o_part_stride, o_sb, o_ss, o_sh;
+  const float* lse_parts;
+  int64_t lse_part_stride;
+  MView out;
+  int out_f32;
+  float* lse_out;
+  int n_parts, B, S, H;
+  int tree;
+};
+
+struct BwdParams {
+  View q, k, v, o, dout;
+  MView dq, dk, dv;
+  const float* lse;
+  float* delta;
+  float* dq_acc;  // contiguous [B, Sq, Hq, D]
+  int B, Hq, Hkv, Sq, Sk;
+  int group;
+  int64_t delta_pos;  // q_pos0 - k_pos0
+  int causal;
+  int dq_overwrite;
+  int finalize_dq;
+  int balanced;
+  float scale, scale_log2;
+  int n_qtiles, n_ktiles, n_units_k;  // filled in by the launchers
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  int64_t q_sb, q_sh;
+  const uint16_t* k;
+  int64_t k_sb, k_sl, k_sh;
+  const uint16_t* v;
+  int64_t v_sb, v_sl, v_sh;
+  const int32_t* seqlens;
+  int64_t L;
+  int B, Hq, Hkv, group;
+  int n_splits;
+  int64_t split_len;
+  float scale, scale_log2;
+  float* part_o;    // [B, Hq, n_splits, D]
+  float* part_lse;  // [B, Hq, n_splits]
+  uint16_t* o;
+  int64_t o_sb, o_sh;
+  float* lse;
+};
+
+// Launchers (return the launch status).  D is the head dimension.
+hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int D, hipStream_t s);
+// Backward: delta = rowsum(dO * O); then dK/dV (key-outer) and, when run_dq,
+// dQ (query-outer, accumulated into dq_acc).  Both kernels write every row
+// they own even when no pair is visible.
+hipError_t launch_bwd_delta(const BwdParams& p, int D, int is_bf16, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, int run_dq, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdParams& p, int D, int run_dq, hipStream_t s);
+// Decode: split partials into the workspace, then the per-(b, h) tree merge.
+hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,240 @@
+// Backward helpers shared by both dtypes (delta = rowsum(dO * O)) and the fp32
+// backward kernels (vector ALUs, fp32 end to end).
+//
+// fp32 dQ kernel: one thread per query row; key/value tiles staged in LDS.
+// fp32 dK/dV kernel: one thread per key row; query tiles (q, dO, LSE, delta)
+// staged in LDS, looping over every query head that reads the key/value head.
+// Both recompute P = exp(s - LSE) from the saved LSE; neither re-runs the forward.
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+// ------------------------------------------------------------------ delta --
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;  // threads per row, 8 features each
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int c = (int)(gid % TPR);
+  const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+  const bool ok = row < rows;
+  int h = 0, i = 0, b = 0;
+  float acc = 0.f;
+  if (ok) {
+    h = (int)(row % p.Hq);
+    i = (int)((row / p.Hq) % p.Sq);
+    b = (int)(row / ((int64_t)p.Hq * p.Sq));
+    const int64_t oo = (int64_t)b * p.o.sb + (int64_t)i * p.o.ss + (int64_t)h * p.o.sh + c * 8;
+    const int64_t od = (int64_t)b * p.dout.sb + (int64_t)i * p.dout.ss + (int64_t)h * p.dout.sh + c * 8;
+    if (BF16) {
+      const u32x4 a = *(const u32x4*)((const u16*)p.o.ptr + oo);
+      const u32x4 g = *(const u32x4*)((const u16*)p.dout.ptr + od);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(bf16_lo(a[w]), bf16_lo(g[w]), acc);
+        acc = fmaf(bf16_hi(a[w]), bf16_hi(g[w]), acc);
+      }
+    } else {
+      const float* a = (const float*)p.o.ptr + oo;
+      const float* g = (const float*)p.dout.ptr + od;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) acc = fmaf(a[w], g[w], acc);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (ok && c == 0) p.delta[((int64_t)b * p.Hq + h) * p.Sq + i] = acc;
+}
+
+// ------------------------------------------------------------- fp32 dQ ----
+
+constexpr int FBM = 64;  // rows per workgroup (one per thread)
+constexpr int FTK = 32;  // rows per staged tile
+
+template <int D>
+__global__ __launch_bounds__(FBM) void dq_f32_kernel(BwdParams p) {
+  __shared__ float ks[FTK][D];
+  __shared__ float vs[FTK][D];
+  const int tid = threadIdx.x;
+  const int qt = blockIdx.x % p.n_qtiles;
+  const int bh = blockIdx.x / p.n_qtiles;
+  const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
+  const int qi = qt * FBM + tid;
+  const bool qok = qi < p.Sq;
+  const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
+  const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
+  const float* kb = (const float*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
+  const float* vb = (const float*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
+  float q[D], dO[D], dq[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = qok ? qb[(int64_t)qi * p.q.ss + d] : 0.f;
+    dO[d] = qok ? dob[(int64_t)qi * p.dout.ss + d] : 0.f;
+    dq[d] = 0.f;
+  }
+  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + qi;
+  const float lse = qok ? p.lse[srow] : neg_inf();
+  const float dlt = qok ? p.delta[srow] : 0.f;
+  const bool live = lse != neg_inf();
+  const int q_last = min(qt * FBM + FBM, p.Sq) - 1;
+  int kv_end = p.Sk;
+  int64_t lim = (int64_t)p.Sk - 1;
+  if (p.causal) {
+    kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q_last + 1, p.Sk));
+    lim = min<int64_t>(p.delta_pos + qi, lim);
+  }
+  for (int key0 = 0; key0 < kv_end; key0 += FTK) {
+    __syncthreads();
+    for (int e = tid; e < FTK * D; e += FBM) {
+      const int r = e / D, c = e % D;
+      const int key = key0 + r;
+      const bool ok = key < p.Sk;
+      ks[r][c] = ok ? kb[(int64_t)key * p.k.ss + c] : 0.f;
+      vs[r][c] = ok ? vb[(int64_t)key * p.v.ss + c] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < FTK; ++j) {
+      if (!live || key0 + j > lim) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(q[d], ks[j][d], s);
+        dp = fmaf(dO[d], vs[j][d], dp);
+      }
+      const float pj = expf(s * p.scale - lse);
+      const float ds = pj * (dp - dlt);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[j][d], dq[d]);
+    }
+  }
+  if (!qok) return;
+  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
+  float* dqp = p.finalize_dq ? (float*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
+                             : nullptr;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    float v = dq[d] * p.scale;
+    if (!p.dq_overwrite) v += accp[d];
+    accp[d] = v;
+    if (dqp) dqp[d] = v;
+  }
+}
+
+// ---------------------------------------------------------- fp32 dK/dV ----
+
+template <int D>
+__global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
+  __shared__ float qs[FTK][D];
+  __shared__ float dos[FTK][D];
+  __shared__ float ls[FTK];
+  __shared__ float ds_[FTK];
+  const int tid = threadIdx.x;
+  const int kt = blockIdx.x % p.n_ktiles;
+  const int bh = blockIdx.x / p.n_ktiles;
+  const int hk = bh % p.Hkv, b = bh / p.Hkv;
+  const int kj = kt * FBM + tid;
+  const bool kok = kj < p.Sk;
+  const float* kb = (const float*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
+  const float* vb = (const float*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
+  float k[D], v[D], dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    k[d] = kok ? kb[(int64_t)kj * p.k.ss + d] : 0.f;
+    v[d] = kok ? vb[(int64_t)kj * p.v.ss + d] : 0.f;
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  const int64_t need = (int64_t)kj - p.delta_pos;  // causal: query index must be >= need
+  int i_start = 0;
+  if (p.causal) i_start = (int)min<int64_t>(p.Sq, max<int64_t>(0, (int64_t)kt * FBM - p.delta_pos));
+  i_start = (i_start / FTK) * FTK;
+  for (int hh = 0; hh < p.group; ++hh) {
+    const int h = hk * p.group + hh;
+    const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
+    const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
+    const float* lseb = p.lse + ((int64_t)b * p.Hq + h) * p.Sq;
+    const float* dltb = p.delta + ((int64_t)b * p.Hq + h) * p.Sq;
+    for (int i0 = i_start; i0 < p.Sq; i0 += FTK) {
+      __syncthreads();
+      for (int e = tid; e < FTK * D; e += FBM) {
+        const int r = e / D, c = e % D;
+        const int i = i0 + r;
+        const bool ok = i < p.Sq;
+        qs[r][c] = ok ? qb[(int64_t)i * p.q.ss + c] : 0.f;
+        dos[r][c] = ok ? dob[(int64_t)i * p.dout.ss + c] : 0.f;
+      }
+      if (tid < FTK) {
+        const int i = i0 + tid;
+        ls[tid] = (i < p.Sq) ? lseb[i] : neg_inf();
+        ds_[tid] = (i < p.Sq) ? dltb[i] : 0.f;
+      }
+      __syncthreads();
+      for (int r = 0; r < FTK; ++r) {
+        const float lse = ls[r];
+        if (lse == neg_inf() || (p.causal && (int64_t)(i0 + r) < need)) continue;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          s = fmaf(k[d], qs[r][d], s);
+          dp = fmaf(v[d], dos[r][d], dp);
+        }
+        const float pj = expf(s * p.scale - lse);
+        const float ds = pj * (dp - ds_[r]);
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          dv[d] = fmaf(pj, dos[r][d], dv[d]);
+          dk[d] = fmaf(ds, qs[r][d], dk[d]);
+        }
+      }
+    }
+  }
+  if (!kok) return;
+  float* dkp = (float*)p.dk.ptr + (int64_t)b * p.dk.sb + (int64_t)kj * p.dk.ss + (int64_t)hk * p.dk.sh;
+  float* dvp = (float*)p.dv.ptr + (int64_t)b * p.dv.sb + (int64_t)kj * p.dv.ss + (int64_t)hk * p.dv.sh;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    dkp[d] = dk[d] * p.scale;
+    dvp[d] = dv[d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_delta(const BwdParams& p, int D, int is_bf16, hipStream_t s) {
+  const int64_t threads = (int64_t)p.B * p.Sq * p.Hq * (D / 8);
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (D == 128) {
+    if (is_bf16) hipLaunchKernelGGL((delta_kernel<128, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((delta_kernel<128, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((delta_kernel<64, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((delta_kernel<64, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const BwdParams& p0, int D, int run_dq, hipStream_t s) {
+  BwdParams p = p0;
+  p.n_ktiles = (p.Sk + FBM - 1) / FBM;
+  p.n_qtiles = (p.Sq + FBM - 1) / FBM;
+  const int64_t gk = (int64_t)p.B * p.Hkv * p.n_ktiles;
+  if (gk > 0) {
+    if (D == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3((unsigned)gk), dim3(FBM), 0, s, p);
+    else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3((unsigned)gk), dim3(FBM), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
+  if (run_dq && gq > 0) {
+    if (D == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)gq), dim3(FBM), 0, s, p);
+    else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)gq), dim3(FBM), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace attn

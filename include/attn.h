@@ -1,0 +1,260 @@
+/*
+ * attn.h - C ABI of libattn: exact blockwise softmax attention on one device's
+ * sequence shard, for AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, each computing exactly (up to floating-point rounding) the
+ * plain softmax attention result that the source pages' blockwise methods reach:
+ *
+ *   attn_fwd_partial     attention of a query shard over one chunk of keys,
+ *                        producing a partial output O and a row log-sum-exp
+ *                        (BurstAttention, "local attention computation"; the
+ *                        per-chunk step of ring-style attention).
+ *   attn_merge_lse       log-sum-exp weighted merge of partial (O, LSE) pairs
+ *                        over disjoint key sets, sequential or as a binary tree
+ *                        (BurstAttention, "global aggregation"; Tree Attention,
+ *                        reduction over the sequence axis).
+ *   attn_bwd             gradients dQ, dK, dV for one key chunk from the saved
+ *                        final O and LSE, with no re-run of the forward
+ *                        (DistFlashAttn digest, rematerialisation-aware
+ *                        gradient checkpointing).
+ *   attn_decode_splitkv  single-token decode over a long KV cache split into
+ *                        chunks whose partials are reduced by a binary tree
+ *                        (Lean Attention and Tree Attention abstracts).
+ *
+ * Definitions (one batch b, query head h):
+ *   query i sits at global position p_i = q_pos0 + i, key j at r_j = k_pos0 + j;
+ *   with causal != 0, key j is visible to query i iff r_j <= p_i.
+ *   s_ij = scale * q_i . k_j, LSE_i = ln sum_{visible j} exp(s_ij) (natural log),
+ *   O_i = sum_{visible j} exp(s_ij - LSE_i) v_j.
+ *   A row with no visible key has O_i = 0 and LSE_i = -inf (the merge identity).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors of shape [batch, seq, heads, head_dim] are given by a base pointer
+ *     and three element strides (batch, seq, head); the head_dim stride is 1.
+ *     LSE and delta vectors are contiguous fp32 [batch, heads, seq].
+ *   - All pointers are device pointers unless stated otherwise, 16-byte
+ *     aligned, and element strides must keep every row start 16-byte aligned.
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     retains a pointer past the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Success means the work is enqueued on `stream`; nothing synchronises.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Every argument is checked on the host before anything is enqueued; on
+ *     error the call returns a nonzero status, enqueues nothing, leaves every
+ *     output untouched and records a message for attn_last_error().
+ *   - Argument structs start with struct_size = sizeof(the struct).
+ *   - head_dim must be 64 or 128.  Scale 0 means 1/sqrt(head_dim); otherwise it
+ *     must be finite and positive.
+ *   - The library keeps no mutable global state; calls are thread-safe.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+/* Status codes. */
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG 1 /* null pointer, bad size, bad stride, bad scale, bad flag */
+#define ATTN_ERR_UNSUPPORTED 2 /* valid request outside what is built (head_dim, dtype, alignment) */
+#define ATTN_ERR_WORKSPACE 3   /* workspace missing or too small */
+#define ATTN_ERR_HIP 4         /* a HIP launch failed; attn_last_error() holds the HIP message */
+
+/* Element types. */
+#define ATTN_DTYPE_F32 0
+#define ATTN_DTYPE_BF16 1
+
+/* attn_fwd_partial flags. */
+#define ATTN_FWD_ACCUMULATE (1u << 0) /* (o, lse) hold a running fp32 result over earlier key
+                                         chunks; replace it by merge(running, this chunk) */
+#define ATTN_FWD_BALANCED (1u << 1)   /* causal work order pairing early and late query tiles */
+
+/*
+ * attn_fwd_partial: exact attention of q over the keys of one chunk.
+ *
+ * q [batch, seqlen_q, heads_q, head_dim], k and v [batch, seqlen_k, heads_kv, head_dim],
+ * all of element type `dtype`; query head h reads key/value head
+ * h / (heads_q / heads_kv) (heads_q must be a multiple of heads_kv).
+ * Writes o [batch, seqlen_q, heads_q, head_dim] of type o_dtype and
+ * lse [batch, heads_q, seqlen_q] fp32.  With ATTN_FWD_ACCUMULATE, o must be fp32
+ * and (o, lse) are read as the running result before being replaced by the
+ * merged one; a chunk that no query can see then changes nothing.  If o_final is
+ * not NULL, the (merged) output is also written there as bf16.
+ * Aliasing: o, lse and o_final must not overlap q, k, v or each other.
+ */
+typedef struct attn_fwd_args {
+  uint32_t struct_size;
+  uint32_t dtype; /* ATTN_DTYPE_BF16 or ATTN_DTYPE_F32: type of q, k, v */
+  int32_t batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
+  const void* q;
+  int64_t q_stride[3];
+  const void* k;
+  int64_t k_stride[3];
+  const void* v;
+  int64_t v_stride[3];
+  void* o;
+  int64_t o_stride[3];
+  uint32_t o_dtype; /* ATTN_DTYPE_F32 or ATTN_DTYPE_BF16 (the latter only without ACCUMULATE) */
+  float* lse;       /* [batch, heads_q, seqlen_q] */
+  void* o_final;    /* optional bf16 copy of the output, NULL to skip */
+  int64_t o_final_stride[3];
+  int64_t q_pos0, k_pos0; /* global positions of query 0 and key 0 */
+  int32_t causal;
+  float scale;
+  uint32_t flags; /* ATTN_FWD_* */
+} attn_fwd_args;
+
+ATTN_API int attn_fwd_partial(const attn_fwd_args* args, void* stream);
+
+/* attn_merge_lse modes. */
+#define ATTN_MERGE_SEQUENTIAL 0 /* fold parts 0, 1, ..., n-1 in order */
+#define ATTN_MERGE_TREE 1       /* binary tree: adjacent pairs per level, odd part carried */
+
+/*
+ * attn_merge_lse: merge n partial results over disjoint key sets.
+ *
+ * Part c is O_c [batch, seqlen, heads, head_dim] fp32 at o_parts + c * o_part_stride
+ * (element strides o_stride) and LSE_c [batch, heads, seqlen] fp32 at
+ * lse_parts + c * lse_part_stride.  With m = max_c LSE_c:
+ * LSE = m + ln sum_c exp(LSE_c - m) and O = sum_c exp(LSE_c - LSE) O_c; parts
+ * with LSE_c = -inf contribute nothing and an all -inf row gives O = 0, LSE = -inf.
+ * o_out may be fp32 or bf16; it may alias part 0 exactly (same pointer and
+ * strides, fp32), and lse_out may alias part 0's LSE.  No other overlap.
+ */
+typedef struct attn_merge_args {
+  uint32_t struct_size;
+  int32_t n_parts; /* >= 1 */
+  int32_t batch, seqlen, heads, head_dim;
+  const float* o_parts;
+  int64_t o_part_stride;
+  int64_t o_stride[3];
+  const float* lse_parts;
+  int64_t lse_part_stride;
+  void* o_out;
+  int64_t o_out_stride[3];
+  uint32_t o_out_dtype;
+  float* lse_out;
+  uint32_t mode; /* ATTN_MERGE_* */
+} attn_merge_args;
+
+ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
+
+/* attn_bwd flags. */
+#define ATTN_BWD_COMPUTE_DELTA (1u << 0) /* write delta = rowsum(dO * O) first; else read it */
+#define ATTN_BWD_DQ_OVERWRITE (1u << 1)  /* dq_acc = this chunk's dQ instead of dq_acc += it */
+#define ATTN_BWD_FINALIZE_DQ (1u << 2)   /* after accumulating, write dq = dq_acc in `dtype` */
+#define ATTN_BWD_BALANCED (1u << 3)      /* causal work order pairing early and late key tiles */
+
+/*
+ * attn_bwd: gradients of sum(dO * O) for one chunk of keys.
+ *
+ * q, o, dout [batch, seqlen_q, heads_q, head_dim]; k, v [batch, seqlen_k, heads_kv,
+ * head_dim]; all of element type `dtype`.  o and lse are the FINAL (merged over
+ * every chunk) forward output and row LSE.  With P_ij = exp(s_ij - LSE_i) on
+ * visible pairs, delta_i = sum dO_i * O_i and dS_ij = P_ij (dO_i . v_j - delta_i):
+ *   dv_j = sum_i P_ij dO_i,   dk_j = scale sum_i dS_ij q_i   (written, this chunk's keys)
+ *   dq_i += scale sum_j dS_ij k_j                           (accumulated in dq_acc)
+ * With grouped heads, dk/dv of a key/value head sum over the query heads that
+ * share it.  dq_acc is fp32 [batch, seqlen_q, heads_q, head_dim] contiguous;
+ * delta is fp32 [batch, heads_q, seqlen_q].  Rows with LSE = -inf contribute
+ * nothing; a chunk no query sees writes dk = dv = 0 and adds nothing to dq.
+ * Results do not depend on scheduling: no floating-point atomics are used.
+ * dq, dk, dv are written in `dtype`.
+ */
+typedef struct attn_bwd_args {
+  uint32_t struct_size;
+  uint32_t dtype;
+  int32_t batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
+  const void* q;
+  int64_t q_stride[3];
+  const void* k;
+  int64_t k_stride[3];
+  const void* v;
+  int64_t v_stride[3];
+  const void* o;
+  int64_t o_stride[3];
+  const void* dout;
+  int64_t do_stride[3];
+  const float* lse;
+  float* delta;
+  float* dq_acc;
+  void* dq; /* used with ATTN_BWD_FINALIZE_DQ, else may be NULL */
+  int64_t dq_stride[3];
+  void* dk;
+  int64_t dk_stride[3];
+  void* dv;
+  int64_t dv_stride[3];
+  int64_t q_pos0, k_pos0;
+  int32_t causal;
+  float scale;
+  uint32_t flags; /* ATTN_BWD_* */
+} attn_bwd_args;
+
+ATTN_API int attn_bwd(const attn_bwd_args* args, void* stream);
+
+/*
+ * attn_decode_splitkv: one query token per sequence over a KV cache.
+ *
+ * q [batch, heads_q, head_dim] bf16 (element strides q_stride = {batch, head});
+ * k_cache, v_cache [batch, cache_len, heads_kv, head_dim] bf16; query head h reads
+ * key/value head h / (heads_q / heads_kv).  The query attends every cached key
+ * 0 .. len_b - 1 with len_b = seqlens[b] (device int32 [batch], each in
+ * [0, cache_len]) or cache_len when seqlens is NULL; no causal mask applies.
+ * The keys are cut into n_splits contiguous splits of ceil(cache_len / n_splits)
+ * keys; each split yields a partial (O, LSE) in the workspace and the partials of
+ * each (b, h) are reduced by a binary tree of adjacent pairs.
+ * Writes o [batch, heads_q, head_dim] bf16 (strides o_stride = {batch, head}) and
+ * lse [batch, heads_q] fp32.  The workspace (device memory of at least
+ * attn_decode_workspace_size(...) bytes, 256-byte aligned) is overwritten.
+ */
+typedef struct attn_decode_args {
+  uint32_t struct_size;
+  int32_t batch, heads_q, heads_kv, head_dim;
+  int64_t cache_len;
+  const void* q;
+  int64_t q_stride[2];
+  const void* k_cache;
+  int64_t k_stride[3];
+  const void* v_cache;
+  int64_t v_stride[3];
+  const int32_t* seqlens; /* optional */
+  int32_t n_splits;       /* 1 .. 1024, power of two not required */
+  float scale;
+  void* o;
+  int64_t o_stride[2];
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} attn_decode_args;
+
+ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
+
+/* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes). */
+ATTN_API size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits);
+
+/* Static description of a status code. */
+ATTN_API const char* attn_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+ATTN_API const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the built library. */
+ATTN_API int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,254 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every symbol
+include/attn.h declares, agrees with the ctypes binding on struct layouts, and
+rejects every invalid argument before enqueueing anything.
+
+Every call here fails validation or has nothing to do (no compute call is made):
+pointers are fake, 16-byte aligned addresses that validation never dereferences.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from exact_blockwise_attention_attn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+FAKE = 0x7F0000000000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) == 8, names
+    assert sorted(B.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    # Internal kernels and launchers stay hidden.
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert not any("launch_" in s for s in exported), "internal launchers are exported"
+
+
+def test_struct_layouts_match_c():
+    prog = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "attn.h"
+#define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F))
+int main(void) {
+  printf("fwd %zu\nmerge %zu\nbwd %zu\ndecode %zu\n", sizeof(attn_fwd_args), sizeof(attn_merge_args),
+         sizeof(attn_bwd_args), sizeof(attn_decode_args));
+  P(attn_fwd_args, flags); P(attn_fwd_args, o_final_stride); P(attn_fwd_args, q_pos0);
+  P(attn_merge_args, mode); P(attn_merge_args, lse_out);
+  P(attn_bwd_args, flags); P(attn_bwd_args, dv_stride); P(attn_bwd_args, dq_acc);
+  P(attn_decode_args, workspace_bytes); P(attn_decode_args, n_splits); P(attn_decode_args, o_stride);
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "s.c"), os.path.join(d, "s")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(l.rsplit(" ", 1) for l in out.strip().splitlines())
+    assert int(got["fwd"]) == ctypes.sizeof(B.FwdArgs)
+    assert int(got["merge"]) == ctypes.sizeof(B.MergeArgs)
+    assert int(got["bwd"]) == ctypes.sizeof(B.BwdArgs)
+    assert int(got["decode"]) == ctypes.sizeof(B.DecodeArgs)
+    cls = {"attn_fwd_args": B.FwdArgs, "attn_merge_args": B.MergeArgs, "attn_bwd_args": B.BwdArgs,
+           "attn_decode_args": B.DecodeArgs}
+    for key, val in got.items():
+        if "." in key:
+            t, f = key.split(".")
+            assert getattr(cls[t], f).offset == int(val), key
+
+
+def test_helpers(lib):
+    assert lib.attn_abi_version() == 1
+    assert lib.attn_status_string(0) == b"ok"
+    assert lib.attn_status_string(3) == b"workspace missing or too small"
+    assert lib.attn_status_string(99) == b"unknown status"
+    # O partials [16, 32, 64, 128] fp32 + LSE [16, 32, 64] fp32, each rounded up to 256 bytes.
+    assert lib.attn_decode_workspace_size(16, 32, 128, 64) == 16 * 32 * 64 * 128 * 4 + 16 * 32 * 64 * 4
+    assert lib.attn_decode_workspace_size(1, 1, 96, 4) == 0
+    assert lib.attn_decode_workspace_size(1, 1, 128, 0) == 0
+
+
+def fwd_args(**kw):
+    a = B.FwdArgs()
+    a.struct_size = ctypes.sizeof(B.FwdArgs)
+    a.dtype = B.ATTN_DTYPE_BF16
+    a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.head_dim = 1, 4, 2, 64, 64, 128
+    for name in ("q", "k", "v", "o", "lse"):
+        setattr(a, name, FAKE)
+    st = B.I64x3(64 * 4 * 128, 4 * 128, 128)
+    a.q_stride, a.o_stride = st, st
+    a.k_stride = a.v_stride = B.I64x3(64 * 2 * 128, 2 * 128, 128)
+    a.o_dtype = B.ATTN_DTYPE_F32
+    a.o_stride = B.I64x3(64 * 4 * 128, 4 * 128, 128)
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+FWD_BAD = [
+    (dict(struct_size=8), B.ATTN_ERR_INVALID_ARG, "struct_size"),
+    (dict(head_dim=96), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(heads_kv=3), B.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(seqlen_q=-1), B.ATTN_ERR_INVALID_ARG, "sequence"),
+    (dict(batch=0), B.ATTN_ERR_INVALID_ARG, "batch"),
+    (dict(dtype=7), B.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(q=None), B.ATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(k=FAKE + 8), B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(q_stride=B.I64x3(1, 4 * 128, 128)), B.ATTN_ERR_UNSUPPORTED, "alignment"),
+    (dict(v_stride=B.I64x3(-256, 256, 128)), B.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse"),
+    (dict(scale=-1.0), B.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), B.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(flags=1 << 5), B.ATTN_ERR_INVALID_ARG, "flag"),
+    (dict(flags=B.ATTN_FWD_ACCUMULATE, o_dtype=B.ATTN_DTYPE_BF16), B.ATTN_ERR_INVALID_ARG, "ACCUMULATE"),
+    (dict(o_final=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "o_final"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", FWD_BAD, ids=[m for _, _, m in FWD_BAD])
+def test_fwd_rejects(lib, kw, code, msg):
+    a = fwd_args(**kw)
+    assert lib.attn_fwd_partial(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_null_args_and_empty(lib):
+    for fn in (lib.attn_fwd_partial, lib.attn_merge_lse, lib.attn_bwd, lib.attn_decode_splitkv):
+        assert fn(None, None) == B.ATTN_ERR_INVALID_ARG
+        assert lib.attn_last_error() == b"args is NULL"
+    # No queries: nothing to do, no launch, success (and the error message is cleared).
+    a = fwd_args(seqlen_q=0)
+    assert lib.attn_fwd_partial(ctypes.byref(a), None) == B.ATTN_OK
+    assert lib.attn_last_error() == b""
+
+
+def merge_args(**kw):
+    a = B.MergeArgs()
+    a.struct_size = ctypes.sizeof(B.MergeArgs)
+    a.n_parts, a.batch, a.seqlen, a.heads, a.head_dim = 4, 1, 16, 2, 64
+    a.o_parts, a.lse_parts, a.o_out, a.lse_out = FAKE, FAKE, FAKE, FAKE
+    a.o_part_stride, a.lse_part_stride = 16 * 2 * 64, 32
+    a.o_stride = a.o_out_stride = B.I64x3(16 * 2 * 64, 2 * 64, 64)
+    a.o_out_dtype = B.ATTN_DTYPE_F32
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+MERGE_BAD = [
+    (dict(n_parts=0), B.ATTN_ERR_INVALID_ARG, "n_parts"),
+    (dict(n_parts=2000), B.ATTN_ERR_INVALID_ARG, "n_parts"),
+    (dict(mode=5), B.ATTN_ERR_INVALID_ARG, "mode"),
+    (dict(head_dim=32), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(lse_out=None), B.ATTN_ERR_INVALID_ARG, "NULL"),
+    (dict(o_part_stride=0), B.ATTN_ERR_INVALID_ARG, "part strides"),
+    (dict(o_out_dtype=9), B.ATTN_ERR_UNSUPPORTED, "o_out_dtype"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", MERGE_BAD, ids=[m for _, _, m in MERGE_BAD])
+def test_merge_rejects(lib, kw, code, msg):
+    a = merge_args(**kw)
+    assert lib.attn_merge_lse(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def bwd_args(**kw):
+    a = B.BwdArgs()
+    a.struct_size = ctypes.sizeof(B.BwdArgs)
+    a.dtype = B.ATTN_DTYPE_BF16
+    a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.head_dim = 1, 2, 2, 32, 32, 64
+    for name in ("q", "k", "v", "o", "dout", "lse", "delta", "dq_acc", "dq", "dk", "dv"):
+        setattr(a, name, FAKE)
+    st = B.I64x3(32 * 2 * 64, 2 * 64, 64)
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride", "do_stride", "dq_stride", "dk_stride", "dv_stride"):
+        setattr(a, name, st)
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+BWD_BAD = [
+    (dict(flags=1 << 9), B.ATTN_ERR_INVALID_ARG, "flag"),
+    (dict(dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
+    (dict(delta=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(dk=None), B.ATTN_ERR_INVALID_ARG, "dk is NULL"),
+    (dict(dq=None, flags=B.ATTN_BWD_FINALIZE_DQ), B.ATTN_ERR_INVALID_ARG, "dq is NULL"),
+    (dict(o=None, flags=B.ATTN_BWD_COMPUTE_DELTA), B.ATTN_ERR_INVALID_ARG, "o is NULL"),
+    (dict(head_dim=256), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(scale=float("inf")), B.ATTN_ERR_INVALID_ARG, "scale"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BWD_BAD, ids=[m for _, _, m in BWD_BAD])
+def test_bwd_rejects(lib, kw, code, msg):
+    a = bwd_args(**kw)
+    assert lib.attn_bwd(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def decode_args(**kw):
+    a = B.DecodeArgs()
+    a.struct_size = ctypes.sizeof(B.DecodeArgs)
+    a.batch, a.heads_q, a.heads_kv, a.head_dim, a.cache_len = 2, 8, 2, 128, 1000
+    a.q, a.k_cache, a.v_cache, a.o, a.lse, a.workspace = FAKE, FAKE, FAKE, FAKE, FAKE, FAKE
+    a.q_stride = a.o_stride = B.I64x2(8 * 128, 128)
+    a.k_stride = a.v_stride = B.I64x3(1000 * 2 * 128, 2 * 128, 128)
+    a.n_splits = 8
+    a.workspace_bytes = 1 << 20
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+DECODE_BAD = [
+    (dict(workspace_bytes=100), B.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(workspace=None), B.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(workspace=FAKE + 16), B.ATTN_ERR_WORKSPACE, "256-byte"),
+    (dict(n_splits=0), B.ATTN_ERR_INVALID_ARG, "n_splits"),
+    (dict(heads_kv=3), B.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(cache_len=-5), B.ATTN_ERR_INVALID_ARG, "cache_len"),
+    (dict(seqlens=FAKE + 2), B.ATTN_ERR_UNSUPPORTED, "seqlens"),
+    (dict(k_stride=B.I64x3(1000 * 2 * 128, 2 * 128 + 1, 128)), B.ATTN_ERR_UNSUPPORTED, "alignment"),
+    (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", DECODE_BAD, ids=[m for _, _, m in DECODE_BAD])
+def test_decode_rejects(lib, kw, code, msg):
+    a = decode_args(**kw)
+    assert lib.attn_decode_splitkv(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+
+    a = fwd_args(head_dim=96)
+    assert lib.attn_fwd_partial(ctypes.byref(a), None) == B.ATTN_ERR_UNSUPPORTED
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.attn_last_error()))
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert b"head_dim" in lib.attn_last_error()

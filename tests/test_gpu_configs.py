@@ -1,0 +1,188 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+
+The fp64 oracle cannot redo every full-size workload within a test, so each
+one is checked on outputs the oracle computes one by one (sampled rows, heads,
+keys or (batch, head) pairs), plus properties that hold at any size and are
+checked on every head:
+
+* a causal self-attention row 0 sees only key 0: O_0 = v_0 exactly and
+  LSE_0 = c q_0 . k_0;
+* softmax rows sum to one, so sum_j dV_j = sum of dO over rows that see a key,
+  and the shift invariance of softmax gives sum_j dK_j = 0.
+
+Bounds (absolute): O 1e-2, dQ/dK/dV 2e-2, LSE 1e-3.  At long context the
+outputs are small (|O| ~ 1e-2), so the LSE bound is the discriminating one and
+errors are also reported relative to the oracle's RMS.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_blockwise_attention_attn_amd import binding as B
+from exact_blockwise_attention_attn_amd import shard
+from seeded_inputs import WORKLOADS, bf16_bits_to_f32, normal_bf16
+from tests.gpu_util import check, log, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _gen(w, tid, S, H):
+    bits = normal_bf16(w.wid, tid, w.B, (S, H, w.D), threads=16)
+    dev = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    return bits, dev
+
+
+def _f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _runs(n, starts, length):
+    return [(s, min(n, s + length)) for s in starts]
+
+
+@pytest.fixture(scope="module")
+def shard_inputs():
+    w = WORKLOADS["shard_fwd_128k"]
+    log("generating shard_fwd_128k inputs")
+    qb, q = _gen(w, 0, w.S_q, w.H_q)
+    kb, k = _gen(w, 1, w.S_k, w.H_kv)
+    vb, v = _gen(w, 2, w.S_k, w.H_kv)
+    dob, do = _gen(w, 3, w.S_q, w.H_q)
+    return w, (qb, kb, vb, dob), (q, k, v, do)
+
+
+def test_shard_fwd_128k(shard_inputs):
+    w, (qb, kb, vb, _), (q, k, v, _) = shard_inputs
+    log("shard_fwd_128k: 32 chunks of 4096, accumulate epilogue")
+    o, lse, o_run = shard.shard_forward(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
+    log("shard_fwd_128k: per-chunk partials + one sequential merge")
+    o2, lse2, _ = shard.shard_forward_partials(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 4096, 32, 128) and o.dtype == torch.bfloat16
+    # Sampled rows of every head against the oracle.  Keys past the shard's last
+    # position are invisible to every query; the oracle sees them all anyway.
+    runs = _runs(w.S_q, [0, 1000, 2048, 4080], 16)
+    o_np, l_np, o2_np, l2_np = to_np(o), to_np(lse), to_np(o2), to_np(lse2)
+    errs = {"O": 0.0, "LSE": 0.0}
+    rms_o = []
+    for h in range(w.H_q):
+        kh, vh = _f64(kb[0, :, h]), _f64(vb[0, :, h])
+        for a, e in runs:
+            O_ref, L_ref = oracle.attention_head(_f64(qb[0, a:e, h]), kh, vh, w.scale, True, w.q_pos0 + a, 0)
+            for got_o, got_l in ((o_np, l_np), (o2_np, l2_np)):
+                errs["O"] = max(errs["O"], np.abs(got_o[0, a:e, h] - O_ref).max())
+                errs["LSE"] = max(errs["LSE"], np.abs(got_l[0, h, a:e] - L_ref).max())
+            rms_o.append(np.sqrt(np.mean(O_ref ** 2)))
+    rms = float(np.mean(rms_o))
+    log(f"  sampled {len(runs) * 16 * w.H_q} rows: max|err| O {errs['O']:.3e} (rms(O) {rms:.3e}, "
+        f"rel {errs['O'] / rms:.3e}), LSE {errs['LSE']:.3e}")
+    assert errs["O"] <= 1e-2 and errs["LSE"] <= 1e-3
+    assert errs["O"] / rms <= 1e-1, "error not small relative to the output's scale"
+
+
+def test_shard_bwd_128k(shard_inputs):
+    w, (qb, kb, vb, dob), (q, k, v, do) = shard_inputs
+    log("shard_bwd_128k: forward, then per-chunk backward from the saved O/LSE")
+    o, lse, _ = shard.shard_forward(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
+    dq, dk, dv = shard.shard_backward(q, k, v, o, do, lse, w.chunk, q_pos0=w.q_pos0, causal=True)
+    torch.cuda.synchronize()
+    last = w.q_pos0 + w.S_q  # keys at or after this position are invisible to the shard
+    assert torch.all(dk[:, last:] == 0) and torch.all(dv[:, last:] == 0)
+    # Sum rules on every head (fp64 sums of the bf16 outputs).
+    dk_sum = dk[0, :last].double().sum(0)
+    dv_sum = dv[0, :last].double().sum(0)
+    do_sum = do[0].double().sum(0)
+    log(f"  sum rules: max|sum dK| {dk_sum.abs().max().item():.3e}, "
+        f"max|sum dV - sum dO| {(dv_sum - do_sum).abs().max().item():.3e}")
+    assert dk_sum.abs().max().item() < 0.05
+    assert (dv_sum - do_sum).abs().max().item() < 0.05
+    # Two heads in full against the oracle (restricted to the visible keys).
+    for h in (0, 17):
+        log(f"  oracle backward head {h}")
+        qh, doh = _f64(qb[0, :, h]), _f64(dob[0, :, h])
+        kh, vh = _f64(kb[0, :last, h]), _f64(vb[0, :last, h])
+        O_ref, L_ref = oracle.attention_head(qh, kh, vh, w.scale, True, w.q_pos0, 0)
+        dq_r, dk_r, dv_r = oracle.attention_backward_head(qh, kh, vh, O_ref, doh, L_ref, w.scale, True, w.q_pos0, 0)
+        check(f"h{h} LSE", lse[0, h], L_ref, 1e-3)
+        check(f"h{h} O", o[0, :, h], O_ref, 1e-2)
+        _, r = check(f"h{h} dQ", dq[0, :, h], dq_r, 2e-2)
+        _, r = check(f"h{h} dK", dk[0, :last, h], dk_r, 2e-2)
+        _, r = check(f"h{h} dV", dv[0, :last, h], dv_r, 2e-2)
+        # Relative to the scale of each gradient: catches an all-zero output the absolute bound would pass.
+        for name, got, ref in (("dQ", dq[0, :, h], dq_r), ("dK", dk[0, :last, h], dk_r), ("dV", dv[0, :last, h], dv_r)):
+            e = np.abs(to_np(got) - ref).max() / np.sqrt(np.mean(ref ** 2))
+            log(f"    {name} error / rms(oracle) = {e:.3e}")
+            assert e < 0.1
+
+
+def test_decode_gqa_128k():
+    w = WORKLOADS["decode_gqa_128k"]
+    log("decode_gqa_128k: generating the 8 GiB KV cache")
+    qbits = normal_bf16(w.wid, 0, w.B, (w.H_q, w.D))
+    q = torch.from_numpy(qbits.view(np.int16)).view(torch.bfloat16).cuda()
+    kb, kc = _gen(w, 1, w.S_k, w.H_kv)
+    vb, vc = _gen(w, 2, w.S_k, w.H_kv)
+    o = torch.empty((w.B, w.H_q, w.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.attn_decode_workspace_size(w.B, w.H_q, w.D, w.n_chunks), dtype=torch.uint8, device="cuda")
+    log("decode_gqa_128k: 64 splits + tree merge")
+    B.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=w.n_chunks)
+    torch.cuda.synchronize()
+    o_np, l_np = to_np(o), to_np(lse)
+    G = w.H_q // w.H_kv
+    err_o = err_l = 0.0
+    for b in range(w.B):
+        g = (3 * b) % w.H_kv
+        heads = list(range(g * G, g * G + G))
+        O_ref, L_ref = oracle.attention_head(_f64(qbits[b, heads]), _f64(kb[b, :, g]), _f64(vb[b, :, g]), w.scale)
+        err_o = max(err_o, np.abs(o_np[b, heads] - O_ref).max())
+        err_l = max(err_l, np.abs(l_np[b, heads] - L_ref).max())
+    log(f"  16 (b, kv head) pairs: max|err| O {err_o:.3e}, LSE {err_l:.3e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+def test_causal_fwdbwd_32k():
+    w = WORKLOADS["causal_fwdbwd_32k"]
+    log("causal_fwdbwd_32k: generating inputs")
+    qb, q = _gen(w, 0, w.S_q, w.H_q)
+    kb, k = _gen(w, 1, w.S_k, w.H_kv)
+    vb, v = _gen(w, 2, w.S_k, w.H_kv)
+    dob, do = _gen(w, 3, w.S_q, w.H_q)
+    log("causal_fwdbwd_32k: balanced forward + backward")
+    o, lse = shard.causal_attention_forward(q, k, v, balanced=True)
+    dq, dk, dv = shard.causal_attention_backward(q, k, v, o, do, lse, balanced=True)
+    torch.cuda.synchronize()
+    # Row 0 of every (b, h) sees only key 0.
+    assert torch.equal(o[:, 0], v[:, 0]), "row 0 must equal v_0 exactly"
+    lse0 = np.einsum("bhd,bhd->bh", _f64(qb[:, 0]), _f64(kb[:, 0])) * w.scale
+    check("LSE row 0, all (b, h)", lse[:, :, 0], lse0, 1e-3)
+    # Sum rules on every (b, h).
+    dk_sum = dk.double().sum(1)
+    dv_sum = dv.double().sum(1)
+    do_sum = do.double().sum(1)
+    log(f"  sum rules: max|sum dK| {dk_sum.abs().max().item():.3e}, "
+        f"max|sum dV - sum dO| {(dv_sum - do_sum).abs().max().item():.3e}")
+    assert dk_sum.abs().max().item() < 0.1
+    assert (dv_sum - do_sum).abs().max().item() < 0.1
+    # One (b, h) in full against the oracle, sampled rows of another.
+    b, h = 1, 31
+    log(f"  oracle forward + backward for (b={b}, h={h})")
+    qh, kh, vh, doh = (_f64(x[b, :, h]) for x in (qb, kb, vb, dob))
+    O_ref, L_ref = oracle.attention_head(qh, kh, vh, w.scale, True)
+    check("LSE", lse[b, h], L_ref, 1e-3)
+    check("O", o[b, :, h], O_ref, 1e-2)
+    dq_r, dk_r, dv_r = oracle.attention_backward_head(qh, kh, vh, O_ref, doh, L_ref, w.scale, True)
+    for name, got, ref in (("dQ", dq[b, :, h], dq_r), ("dK", dk[b, :, h], dk_r), ("dV", dv[b, :, h], dv_r)):
+        check(name, got, ref, 2e-2)
+        e = np.abs(to_np(got) - ref).max() / np.sqrt(np.mean(ref ** 2))
+        log(f"    {name} error / rms(oracle) = {e:.3e}")
+        assert e < 0.1
+    for a, e in _runs(w.S_q, [0, 5000, 20000, 32752], 16):
+        O_ref, L_ref = oracle.attention_head(_f64(qb[0, a:e, 0]), _f64(kb[0, :e, 0]), _f64(vb[0, :e, 0]),
+                                             w.scale, True, a, 0)
+        check(f"(0,0) rows {a}..{e} O", o[0, a:e, 0], O_ref, 1e-2)
+        check(f"(0,0) rows {a}..{e} LSE", lse[0, 0, a:e], L_ref, 1e-3)

@@ -1,0 +1,273 @@
+"""GPU parity at small sizes: every entry point against the fp64 oracle, element by element.
+
+Shapes span several tiles and ragged tails, causal offsets that make rows fully
+visible, diagonal or fully masked, grouped heads, empty inputs, chunked
+accumulation, both merge orders and decode splits.  Bounds: O 1e-2 and
+dQ/dK/dV 2e-2, each times max(1, max|oracle|) because bf16 output rounding
+alone is relative; LSE 1e-3 absolute.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_blockwise_attention_attn_amd import binding as B
+from exact_blockwise_attention_attn_amd import shard
+from seeded_inputs import normal_f32
+from tests.gpu_util import check, log, seq_tensor, to_np
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, G_TOL, L_TOL = 1e-2, 2e-2, 1e-3
+
+# (Sq, Sk, D, causal, q_pos0, k_pos0, B, Hq, Hkv, dtype, balanced)
+FWD_CASES = [
+    (1, 1, 128, False, 0, 0, 1, 1, 1, "bf16", False),
+    (2, 17, 64, False, 0, 0, 1, 2, 2, "bf16", False),
+    (17, 63, 128, True, 0, 0, 1, 1, 1, "bf16", False),
+    (63, 64, 128, True, 10, 0, 2, 2, 1, "bf16", False),
+    (64, 65, 64, False, 0, 0, 1, 3, 3, "bf16", False),
+    (65, 129, 128, True, 64, 0, 2, 4, 2, "bf16", False),
+    (129, 255, 128, True, 0, 100, 1, 2, 2, "bf16", False),  # rows 0..99 see nothing
+    (255, 300, 128, False, 0, 0, 1, 8, 1, "bf16", False),
+    (200, 200, 128, True, 0, 0, 2, 2, 2, "bf16", True),
+    (300, 257, 64, True, 500, 0, 1, 2, 2, "bf16", False),  # every row sees every key
+    (1024, 2048, 128, True, 1024, 0, 1, 2, 2, "bf16", False),
+    (513, 513, 128, True, 0, 0, 1, 1, 1, "bf16", True),
+    (5, 0, 128, False, 0, 0, 1, 1, 1, "bf16", False),  # no keys: identity
+    (100, 77, 64, True, 5, 0, 1, 2, 2, "f32", False),
+    (64, 256, 128, False, 0, 0, 1, 1, 1, "f32", False),
+    (70, 90, 64, True, 0, 30, 2, 2, 1, "f32", False),
+]
+
+
+def _ids(cases):
+    return ["-".join(str(x) for x in c) for c in cases]
+
+
+def _inputs(wid, Bn, Sq, Sk, Hq, Hkv, D, dtype):
+    q, qh = seq_tensor(wid, 0, Bn, Sq, Hq, D, dtype)
+    k, kh = seq_tensor(wid, 1, Bn, Sk, Hkv, D, dtype)
+    v, vh = seq_tensor(wid, 2, Bn, Sk, Hkv, D, dtype)
+    return (q, k, v), (qh, kh, vh)
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=_ids(FWD_CASES))
+def test_fwd_partial(case):
+    Sq, Sk, D, causal, qp, kp, Bn, Hq, Hkv, dtype, bal = case
+    log(f"fwd {case}")
+    (q, k, v), (qh, kh, vh) = _inputs(101, Bn, Sq, Sk, Hq, Hkv, D, dtype)
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention(qh, kh, vh, scale, causal, qp, kp)
+    for odt in (torch.float32, torch.bfloat16) if dtype == "bf16" else (torch.float32,):
+        o = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=odt, device="cuda")
+        lse = torch.full((Bn, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
+        B.attn_fwd_partial(q, k, v, o, lse, q_pos0=qp, k_pos0=kp, causal=causal, balanced=bal)
+        torch.cuda.synchronize()
+        check(f"O ({odt})", o, O_ref, O_TOL, scale_by_max=True)
+        check("LSE", lse, L_ref, L_TOL)
+
+
+def test_fwd_strided_views_and_scale():
+    """Non-contiguous [B, S, H, D] views (a head slice of a wider tensor) and an explicit scale."""
+    log("fwd strided")
+    (q, k, v), (qh, kh, vh) = _inputs(102, 2, 96, 150, 6, 6, 128, "bf16")
+    qs, ks, vs = q[:, :, 1:4], k[:, :, 2:5], v[:, :, 3:6]
+    o = torch.empty((2, 96, 3, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2, 3, 96), dtype=torch.float32, device="cuda")
+    B.attn_fwd_partial(qs, ks, vs, o, lse, causal=True, q_pos0=60, scale=0.05)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention(qh[:, :, 1:4], kh[:, :, 2:5], vh[:, :, 3:6], 0.05, True, 60, 0)
+    check("O", o, O_ref, O_TOL, scale_by_max=True)
+    check("LSE", lse, L_ref, L_TOL)
+
+
+# (Sq, Sk, chunk, causal, q_pos0, Hq, Hkv, D, dtype)
+CHUNK_CASES = [
+    (256, 256, 64, False, 0, 1, 1, 64, "f32"),
+    (128, 1000, 128, True, 600, 2, 2, 128, "bf16"),
+    (300, 700, 100, True, 350, 4, 1, 128, "bf16"),
+    (64, 512, 64, True, 0, 2, 2, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=_ids(CHUNK_CASES))
+def test_chunked_forward_and_merge(case):
+    """Chunk by chunk with the fused accumulate epilogue, and per-chunk partials merged
+    sequentially and as a tree, all against the unchunked oracle."""
+    Sq, Sk, chunk, causal, qp, Hq, Hkv, D, dtype = case
+    log(f"chunked {case}")
+    (q, k, v), (qh, kh, vh) = _inputs(103, 1, Sq, Sk, Hq, Hkv, D, dtype)
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention(qh, kh, vh, scale, causal, qp, 0)
+    o, lse, o_run = shard.shard_forward(q, k, v, chunk, q_pos0=qp, causal=causal)
+    torch.cuda.synchronize()
+    check("O accumulate", o, O_ref, O_TOL, scale_by_max=True)
+    check("O running fp32", o_run, O_ref, O_TOL, scale_by_max=True)
+    check("LSE accumulate", lse, L_ref, L_TOL)
+    for tree in (False, True):
+        o2, l2, _ = shard.shard_forward_partials(q, k, v, chunk, q_pos0=qp, causal=causal, tree=tree)
+        torch.cuda.synchronize()
+        check(f"O merged tree={tree}", o2, O_ref, O_TOL, scale_by_max=True)
+        check(f"LSE merged tree={tree}", l2, L_ref, L_TOL)
+
+
+@pytest.mark.parametrize("n,tree,D", [(1, False, 128), (2, True, 64), (5, True, 128), (17, False, 128),
+                                      (64, True, 128), (100, True, 64)])
+def test_merge_kernel(n, tree, D):
+    log(f"merge n={n} tree={tree} D={D}")
+    Bn, S, H = 2, 37, 3
+    rng = np.random.default_rng([104, n, D])
+    O = rng.standard_normal((n, Bn, S, H, D)).astype(np.float32)
+    L = (3 * rng.standard_normal((n, Bn, H, S))).astype(np.float32)
+    L[:, 0, 0, :5] = -np.inf  # rows with no key in any part
+    if n > 1:
+        L[1] = -np.inf  # an empty part
+        O[1] = 0.0
+    O[np.isinf(L).transpose(0, 1, 3, 2)] = 0.0
+    O_ref, L_ref = (oracle.merge_tree if tree else oracle.merge)(
+        [(O[c], L[c].transpose(0, 2, 1)) for c in range(n)])
+    L_ref = L_ref.transpose(0, 2, 1)
+    o_parts = torch.from_numpy(O).cuda()
+    l_parts = torch.from_numpy(L).cuda()
+    for odt in (torch.float32, torch.bfloat16):
+        o = torch.empty((Bn, S, H, D), dtype=odt, device="cuda")
+        lse = torch.empty((Bn, H, S), dtype=torch.float32, device="cuda")
+        B.attn_merge_lse(o_parts, l_parts, o, lse, tree=tree)
+        torch.cuda.synchronize()
+        check(f"merge O {odt}", o, O_ref, 1e-5 if odt == torch.float32 else O_TOL, scale_by_max=True)
+        check("merge LSE", lse, L_ref, 1e-5)
+    # Output aliasing part 0 (documented as allowed).
+    B.attn_merge_lse(o_parts, l_parts, o_parts[0], l_parts[0], tree=tree)
+    torch.cuda.synchronize()
+    check("merge O aliased", o_parts[0], O_ref, 1e-5, scale_by_max=True)
+    check("merge LSE aliased", l_parts[0], L_ref, 1e-5)
+
+
+# (Sq, Sk, D, causal, q_pos0, k_pos0, B, Hq, Hkv, dtype, balanced)
+BWD_CASES = [
+    (1, 1, 128, False, 0, 0, 1, 1, 1, "bf16", False),
+    (17, 63, 64, True, 0, 0, 1, 2, 2, "bf16", False),
+    (65, 129, 128, True, 64, 0, 2, 4, 2, "bf16", False),
+    (129, 255, 128, True, 0, 100, 1, 2, 2, "bf16", False),
+    (200, 200, 128, True, 0, 0, 2, 2, 2, "bf16", True),
+    (255, 64, 128, False, 0, 0, 1, 4, 1, "bf16", False),
+    (300, 257, 64, True, 500, 0, 1, 2, 2, "bf16", False),
+    (257, 257, 128, True, 0, 0, 1, 1, 1, "bf16", True),
+    (100, 77, 64, True, 5, 0, 1, 2, 2, "f32", False),
+    (64, 130, 128, False, 0, 0, 1, 2, 1, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=_ids(BWD_CASES))
+def test_bwd(case):
+    Sq, Sk, D, causal, qp, kp, Bn, Hq, Hkv, dtype, bal = case
+    log(f"bwd {case}")
+    (q, k, v), (qh, kh, vh) = _inputs(105, Bn, Sq, Sk, Hq, Hkv, D, dtype)
+    do, doh = seq_tensor(105, 3, Bn, Sq, Hq, D, dtype)
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention(qh, kh, vh, scale, causal, qp, kp)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, scale, causal, qp, kp)
+    o = torch.empty_like(q)
+    lse = torch.empty((Bn, Hq, Sq), dtype=torch.float32, device="cuda")
+    B.attn_fwd_partial(q, k, v, o, lse, q_pos0=qp, k_pos0=kp, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    delta = torch.empty((Bn, Hq, Sq), dtype=torch.float32, device="cuda")
+    B.attn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, dq=dq, q_pos0=qp, k_pos0=kp, causal=causal,
+               compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=bal)
+    torch.cuda.synchronize()
+    check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
+    check("dK", dk, dk_ref, G_TOL, scale_by_max=True)
+    check("dV", dv, dv_ref, G_TOL, scale_by_max=True)
+    check("delta", delta, np.einsum("bshd,bshd->bhs", doh, O_ref), G_TOL, scale_by_max=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_chunked(dtype):
+    """Per-chunk backward with the final LSE: dQ accumulated over chunks, dK/dV per chunk."""
+    Sq, Sk, chunk, qp, H, D = 160, 600, 128, 400, 2, 64 if dtype == "f32" else 128
+    log(f"bwd chunked {dtype}")
+    (q, k, v), (qh, kh, vh) = _inputs(106, 1, Sq, Sk, H, H, D, dtype)
+    do, doh = seq_tensor(106, 3, 1, Sq, H, D, dtype)
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.attention(qh, kh, vh, scale, True, qp, 0)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, scale, True, qp, 0)
+    o, lse, _ = shard.shard_forward(q, k, v, chunk, q_pos0=qp, causal=True)
+    dq, dk, dv = shard.shard_backward(q, k, v, o, do, lse, chunk, q_pos0=qp, causal=True)
+    torch.cuda.synchronize()
+    check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
+    check("dK", dk, dk_ref, G_TOL, scale_by_max=True)
+    check("dV", dv, dv_ref, G_TOL, scale_by_max=True)
+    assert torch.all(dk[:, Sq + qp:] == 0) and torch.all(dv[:, Sq + qp:] == 0), "invisible keys got gradient"
+
+
+def test_bwd_deterministic():
+    log("bwd determinism")
+    (q, k, v), _ = _inputs(107, 1, 300, 300, 2, 2, 128, "bf16")
+    do, _ = seq_tensor(107, 3, 1, 300, 2, 128, "bf16")
+    o, lse = shard.causal_attention_forward(q, k, v)
+    r1 = shard.causal_attention_backward(q, k, v, o, do, lse)
+    r2 = shard.causal_attention_backward(q, k, v, o, do, lse)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+# (B, Hq, Hkv, L, D, n_splits, seqlens)
+DECODE_CASES = [
+    (2, 8, 2, 1000, 128, 8, None),
+    (3, 4, 4, 37, 128, 4, [1, 20, 37]),
+    (2, 16, 2, 2048 + 17, 128, 16, None),
+    (1, 2, 1, 5000, 64, 7, None),
+    (2, 4, 1, 64, 128, 64, [0, 64]),
+    (1, 32, 8, 16384, 128, 64, None),
+    (2, 6, 2, 300, 128, 1, [300, 150]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=_ids(DECODE_CASES))
+def test_decode(case):
+    Bn, Hq, Hkv, L, D, ns, lens = case
+    log(f"decode {case}")
+    q, qh = seq_tensor(108, 0, Bn, 1, Hq, D, "bf16")
+    kc, kh = seq_tensor(108, 1, Bn, L, Hkv, D, "bf16")
+    vc, vh = seq_tensor(108, 2, Bn, L, Hkv, D, "bf16")
+    q, qh = q[:, 0], qh[:, 0]
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.decode(qh, kh, vh, scale, seqlens=lens)
+    o = torch.empty((Bn, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Bn, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.attn_decode_workspace_size(Bn, Hq, D, ns), dtype=torch.uint8, device="cuda")
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    B.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=ns, seqlens=sl)
+    torch.cuda.synchronize()
+    check("decode O", o, O_ref, O_TOL, scale_by_max=True)
+    check("decode LSE", lse, L_ref, L_TOL)
+
+
+def test_fp32_s256_four_chunks():
+    """The fp32 workload: S=256, d=64, keys in 4 chunks of 64 merged by LSE weighting, and its backward."""
+    log("fp32 S=256 4 chunks")
+    q, qh = seq_tensor(1, 0, 1, 256, 1, 64, "f32")
+    k, kh = seq_tensor(1, 1, 1, 256, 1, 64, "f32")
+    v, vh = seq_tensor(1, 2, 1, 256, 1, 64, "f32")
+    do, doh = seq_tensor(1, 3, 1, 256, 1, 64, "f32")
+    O_ref, L_ref = oracle.attention(qh, kh, vh, 1 / 8)
+    dq_ref, dk_ref, dv_ref = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, 1 / 8)
+    for mode in ("accumulate", "partials", "tree"):
+        if mode == "accumulate":
+            o, lse, _ = shard.shard_forward(q, k, v, 64)
+        else:
+            o, lse, _ = shard.shard_forward_partials(q, k, v, 64, tree=mode == "tree")
+        torch.cuda.synchronize()
+        check(f"O {mode}", o, O_ref, 1e-5)
+        check(f"LSE {mode}", lse, L_ref, 1e-5)
+    dq, dk, dv = shard.shard_backward(q, k, v, o, do, lse, 64)
+    torch.cuda.synchronize()
+    check("dQ", dq, dq_ref, 1e-5)
+    check("dK", dk, dk_ref, 1e-5)
+    check("dV", dv, dv_ref, 1e-5)
