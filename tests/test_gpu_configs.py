@@ -11,8 +11,9 @@ checked on every head:
   and the shift invariance of softmax gives sum_j dK_j = 0.
 
 Bounds (absolute): O 1e-2, dQ/dK/dV 2e-2, LSE 1e-3.  At long context the
-outputs are small (|O| ~ 1e-2), so the LSE bound is the discriminating one and
-errors are also reported relative to the oracle's RMS.
+outputs are small (|O| ~ 1e-2), so an all-zero output would pass the absolute
+bounds: the LSE bound, the relative Frobenius error (< 1e-2 for O, < 2e-2 for
+gradients) and the sum rules are the discriminating checks.
 """
 
 import math
@@ -38,6 +39,21 @@ def _gen(w, tid, S, H):
 
 def _f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _rel_fro(got, ref):
+    """||got - ref||_F / ||ref||_F: about 2^-9 for correct bf16 results, 1 for an all-zero output."""
+    got = to_np(got) if isinstance(got, torch.Tensor) else got
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def _sum_rule(name, grads, target):
+    """max over (b, h, d) of |sum_j g_j - target| / sum_j |g_j| (sums over the sequence axis 1)."""
+    s = grads.double().sum(1)
+    a = grads.double().abs().sum(1)
+    r = ((s - target).abs() / a.clamp_min(1e-30)).max().item()
+    log(f"  sum rule {name}: max |sum - target| / sum|.| = {r:.3e}")
+    return r
 
 
 def _runs(n, starts, length):
@@ -79,9 +95,9 @@ def test_shard_fwd_128k(shard_inputs):
             rms_o.append(np.sqrt(np.mean(O_ref ** 2)))
     rms = float(np.mean(rms_o))
     log(f"  sampled {len(runs) * 16 * w.H_q} rows: max|err| O {errs['O']:.3e} (rms(O) {rms:.3e}, "
-        f"rel {errs['O'] / rms:.3e}), LSE {errs['LSE']:.3e}")
+        f"max|err| / rms {errs['O'] / rms:.3e}), LSE {errs['LSE']:.3e}")
     assert errs["O"] <= 1e-2 and errs["LSE"] <= 1e-3
-    assert errs["O"] / rms <= 1e-1, "error not small relative to the output's scale"
+    assert errs["O"] / rms <= 5e-2, "error not small relative to the output's scale"
 
 
 def test_shard_bwd_128k(shard_inputs):
@@ -93,13 +109,8 @@ def test_shard_bwd_128k(shard_inputs):
     last = w.q_pos0 + w.S_q  # keys at or after this position are invisible to the shard
     assert torch.all(dk[:, last:] == 0) and torch.all(dv[:, last:] == 0)
     # Sum rules on every head (fp64 sums of the bf16 outputs).
-    dk_sum = dk[0, :last].double().sum(0)
-    dv_sum = dv[0, :last].double().sum(0)
-    do_sum = do[0].double().sum(0)
-    log(f"  sum rules: max|sum dK| {dk_sum.abs().max().item():.3e}, "
-        f"max|sum dV - sum dO| {(dv_sum - do_sum).abs().max().item():.3e}")
-    assert dk_sum.abs().max().item() < 0.05
-    assert (dv_sum - do_sum).abs().max().item() < 0.05
+    assert _sum_rule("dK", dk[:, :last], 0.0) < 1e-2
+    assert _sum_rule("dV", dv[:, :last], do.double().sum(1)) < 1e-2
     # Two heads in full against the oracle (restricted to the visible keys).
     for h in (0, 17):
         log(f"  oracle backward head {h}")
@@ -109,14 +120,13 @@ def test_shard_bwd_128k(shard_inputs):
         dq_r, dk_r, dv_r = oracle.attention_backward_head(qh, kh, vh, O_ref, doh, L_ref, w.scale, True, w.q_pos0, 0)
         check(f"h{h} LSE", lse[0, h], L_ref, 1e-3)
         check(f"h{h} O", o[0, :, h], O_ref, 1e-2)
-        _, r = check(f"h{h} dQ", dq[0, :, h], dq_r, 2e-2)
-        _, r = check(f"h{h} dK", dk[0, :last, h], dk_r, 2e-2)
-        _, r = check(f"h{h} dV", dv[0, :last, h], dv_r, 2e-2)
-        # Relative to the scale of each gradient: catches an all-zero output the absolute bound would pass.
+        # Absolute bounds, and the relative Frobenius error, which catches an
+        # all-zero output that the absolute bound alone would pass at this scale.
         for name, got, ref in (("dQ", dq[0, :, h], dq_r), ("dK", dk[0, :last, h], dk_r), ("dV", dv[0, :last, h], dv_r)):
-            e = np.abs(to_np(got) - ref).max() / np.sqrt(np.mean(ref ** 2))
-            log(f"    {name} error / rms(oracle) = {e:.3e}")
-            assert e < 0.1
+            check(f"h{h} {name}", got, ref, 2e-2)
+            e = _rel_fro(got, ref)
+            log(f"    {name} relative Frobenius error {e:.3e}")
+            assert e < 2e-2
 
 
 def test_decode_gqa_128k():
@@ -161,13 +171,8 @@ def test_causal_fwdbwd_32k():
     lse0 = np.einsum("bhd,bhd->bh", _f64(qb[:, 0]), _f64(kb[:, 0])) * w.scale
     check("LSE row 0, all (b, h)", lse[:, :, 0], lse0, 1e-3)
     # Sum rules on every (b, h).
-    dk_sum = dk.double().sum(1)
-    dv_sum = dv.double().sum(1)
-    do_sum = do.double().sum(1)
-    log(f"  sum rules: max|sum dK| {dk_sum.abs().max().item():.3e}, "
-        f"max|sum dV - sum dO| {(dv_sum - do_sum).abs().max().item():.3e}")
-    assert dk_sum.abs().max().item() < 0.1
-    assert (dv_sum - do_sum).abs().max().item() < 0.1
+    assert _sum_rule("dK", dk, 0.0) < 1e-2
+    assert _sum_rule("dV", dv, do.double().sum(1)) < 1e-2
     # One (b, h) in full against the oracle, sampled rows of another.
     b, h = 1, 31
     log(f"  oracle forward + backward for (b={b}, h={h})")
@@ -175,12 +180,13 @@ def test_causal_fwdbwd_32k():
     O_ref, L_ref = oracle.attention_head(qh, kh, vh, w.scale, True)
     check("LSE", lse[b, h], L_ref, 1e-3)
     check("O", o[b, :, h], O_ref, 1e-2)
+    assert _rel_fro(o[b, :, h], O_ref) < 1e-2
     dq_r, dk_r, dv_r = oracle.attention_backward_head(qh, kh, vh, O_ref, doh, L_ref, w.scale, True)
     for name, got, ref in (("dQ", dq[b, :, h], dq_r), ("dK", dk[b, :, h], dk_r), ("dV", dv[b, :, h], dv_r)):
         check(name, got, ref, 2e-2)
-        e = np.abs(to_np(got) - ref).max() / np.sqrt(np.mean(ref ** 2))
-        log(f"    {name} error / rms(oracle) = {e:.3e}")
-        assert e < 0.1
+        e = _rel_fro(got, ref)
+        log(f"    {name} relative Frobenius error {e:.3e}")
+        assert e < 2e-2
     for a, e in _runs(w.S_q, [0, 5000, 20000, 32752], 16):
         O_ref, L_ref = oracle.attention_head(_f64(qb[0, a:e, 0]), _f64(kb[0, :e, 0]), _f64(vb[0, :e, 0]),
                                              w.scale, True, a, 0)
