@@ -7,15 +7,21 @@
 //
 // Layout of the work:
 //   * one workgroup = 4 wavefronts = 128 queries of one (batch, head); each
-//     wavefront owns 32 queries;
-//   * keys stream through LDS in tiles of 64 (double buffered, the next tile is
-//     fetched into registers while the current one is used);
+//     wavefront owns 32 queries; two workgroups share a CU;
+//   * key and value tiles of 64 rows go straight from HBM to LDS
+//     (global_load_lds, no register staging), double buffered: the next tile
+//     streams in while the current one is used.  Rows are padded so the MFMA
+//     operand reads hit distinct banks;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //     the accumulator puts one query per lane (column) and 16 of its keys in
 //     the lane's registers, so row max and row sum are in-lane reductions plus
-//     one exchange with the other half of the wavefront;
-//   * O^T += V^T P^T uses P^T straight from the registers (no LDS round trip);
-//     V is stored transposed in LDS with keys in the matching slot order;
+//     one exchange between the two half-waves (v_permlane32_swap);
+//   * O^T += V^T P^T takes P^T straight from the registers; the V^T operand is
+//     read from the row-major value tile with the transposing LDS read
+//     (ds_read_b64_tr_b16), keys landing in the same slot order as P^T;
+//   * the output accumulator is rescaled only when a row's running maximum
+//     grows by more than 2^8 in exp2 units (the stale maximum is an equally
+//     valid stabiliser, so the result is unchanged);
 //   * causal tiles are classified per workgroup: tiles no query sees are never
 //     visited, tiles every query sees skip the mask, the rest are masked per
 //     element.
@@ -28,85 +34,161 @@ namespace {
 constexpr int BM = 128;  // queries per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
+constexpr float kRescaleSlack = 8.0f;  // exp2 units a row max may grow before O is rescaled
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
+typedef void __attribute__((address_space(3))) lds_void;
+
+// LDS row strides (elements).  K rows are padded by 16 bytes, so the 8 rows an
+// MFMA operand read touches per LDS cycle start on 8 distinct 16-byte bank
+// groups; V rows by 32 bytes, so the 4 rows a transposing read touches per
+// 16-lane group start on 4 distinct 32-byte bank groups.  With padding (not a
+// swizzle) every fragment address is one per-lane base plus an immediate.
 template <int D>
-struct alignas(16) FwdTile {
-  u16 k[BN][D + 8];   // keys row-major; the pad puts 8 consecutive rows on distinct banks
-  u16 vt[D][BN + 8];  // values transposed: one row per feature, keys in slot order
+struct Lds {
+  static constexpr int KLD = D + 8;
+  static constexpr int VLD = D + 16;
+  static constexpr int KRUNS = (BN * KLD * 2 + 1023) / 1024;  // 1 KB global_load_lds runs per tile
+  static constexpr int VRUNS = (BN * VLD * 2 + 1023) / 1024;
+  static constexpr int KSIZE = KRUNS * 512;  // elements, whole runs
+  static constexpr int VSIZE = VRUNS * 512;
 };
 
-template <int D>
-struct KVRegs {
-  static constexpr int KCH = D / 8;            // 16-byte chunks per key row
-  static constexpr int KPASS = BN * KCH / NT;  // chunks of the key tile per thread
-  u32x4 k[KPASS];
-  u32x4 v[4];  // 4 consecutive keys x 8 features, for the transposed store
-};
-
-__device__ __forceinline__ u32x4 load16(const u16* ptr, bool ok) {
-  if (ok) return *(const u32x4*)ptr;
-  return u32x4{0u, 0u, 0u, 0u};
+// Copy one run of 64 chunks (1 KB of LDS, lane l -> chunk l) of a padded tile.
+// Pad slots receive a copy of the row's first chunk and are never read; rows
+// past the end load a valid row (always masked out), so LDS never holds garbage.
+template <int D, int LD>
+__device__ __forceinline__ void issue_run(u16* lds, const u16* g, int64_t ss, int key0, int Sk, int run, int lane) {
+  const int e = run * 512 + lane * 8;  // element offset of this lane's chunk
+  const int r = e / LD;
+  int col = e - r * LD;
+  if (col >= D) col = 0;
+  const int key = min(key0 + r, Sk - 1);
+  __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)key * ss + col), (lds_void*)(lds + run * 512), 16, 0, 0);
 }
 
+// Issue the global->LDS copy of one 64-row tile (K and V): wave w issues runs w, w+4, ...
 template <int D>
-__device__ __forceinline__ void load_kv(KVRegs<D>& r, const u16* kb, const u16* vb, int64_t k_ss, int64_t v_ss,
-                                        int key0, int Sk, int tid) {
-  constexpr int KCH = KVRegs<D>::KCH;
-  constexpr int RPP = NT / KCH;
+__device__ __forceinline__ void issue_tile(u16* ks, u16* vs, const u16* kb, const u16* vb, int64_t k_ss,
+                                           int64_t v_ss, int key0, int Sk, int wave, int lane) {
+  using L = Lds<D>;
 #pragma unroll
-  for (int p = 0; p < KVRegs<D>::KPASS; ++p) {
-    const int row = tid / KCH + p * RPP;
-    const int key = key0 + row;
-    r.k[p] = load16(kb + (int64_t)key * k_ss + (tid % KCH) * 8, key < Sk);
+  for (int run = wave; run < L::KRUNS; run += 4) issue_run<D, L::KLD>(ks, kb, k_ss, key0, Sk, run, lane);
+#pragma unroll
+  for (int run = wave; run < L::VRUNS; run += 4) issue_run<D, L::VLD>(vs, vb, v_ss, key0, Sk, run, lane);
+}
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct RowState {
+  float m;  // running maximum of the raw scores used as the stabiliser
+  float l;  // this lane's partial row sum
+};
+
+// One 64-key tile: scores, online softmax, O^T update.
+template <int D>
+__device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf16x8* qf, f32x16* oacc,
+                                          RowState& st, int key0, bool need_mask, int64_t lim64, float sl2,
+                                          int lane) {
+  constexpr int NS = D / 16, NDB = D / 32;
+  const int lr = lane & 31, lg = lane >> 5;
+
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const bf16x8 a = as_bf16x8(*(const u32x4*)(ks + (kb2 * 32 + lr) * Lds<D>::KLD + s * 16 + lg * 8));
+      sacc[kb2] = mfma32(a, qf[s], sacc[kb2]);
+    }
   }
-  const int kg = tid & 15, dg = tid >> 4;
-  if (dg < KCH) {
+  if (need_mask) {
+    const int lim = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, BN));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = key0 + kg * 4 + j;
-      r.v[j] = load16(vb + (int64_t)key * v_ss + dg * 8, key < Sk);
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kl = kb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
+        if (kl > lim) sacc[kb2][i] = neg_inf();
+      }
+  }
+  float mt = sacc[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[0][i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
+  mt = half_max(mt);
+  // Rescale only when some row of the wavefront outgrows its stabiliser.
+  const bool grow = (mt - st.m) * sl2 > kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float m_new = grow ? mt : st.m;
+    const float alpha = grow ? exp2_fast((st.m - m_new) * sl2) : 1.f;  // 0 when st.m = -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = (st.m == neg_inf()) ? 0.f : st.m;
+  const float nbias = -m_use * sl2;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = exp2_fast(fmaf(sacc[kb2][i], sl2, nbias));
+      sacc[kb2][i] = e;
+      rs += e;
+    }
+  st.l += rs;
+
+  // O^T += V^T P^T over four 16-key slabs.  Lane (16q + s) of a transposing read
+  // fetches 4 features of key (slab + 8h + 4*(q/2) + s/4); the read hands lane
+  // d = 16*(q%2) + s the 4 keys of its k-slots 4h .. 4h+3.
+  const int q16 = lane >> 4, s16 = lane & 15;
+  const int krow0 = (q16 >> 1) * 4 + (s16 >> 2);
+  const int fcol = (q16 & 1) * 16 + 4 * (s16 & 3);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kb2 = ks >> 1, o = (ks & 1) * 8;
+    const bf16x8 pb = cvt_bf16x8(sacc[kb2][o + 0], sacc[kb2][o + 1], sacc[kb2][o + 2], sacc[kb2][o + 3],
+                                 sacc[kb2][o + 4], sacc[kb2][o + 5], sacc[kb2][o + 6], sacc[kb2][o + 7]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i16x4 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + (ks * 16 + h * 8 + krow0) * Lds<D>::VLD + db * 32 + fcol));
+      }
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = mfma32(a, pb, oacc[db]);
     }
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_kv(FwdTile<D>& t, const KVRegs<D>& r, int tid) {
-  constexpr int KCH = KVRegs<D>::KCH;
-  constexpr int RPP = NT / KCH;
-#pragma unroll
-  for (int p = 0; p < KVRegs<D>::KPASS; ++p) {
-    const int row = tid / KCH + p * RPP;
-    *(u32x4*)&t.k[row][(tid % KCH) * 8] = r.k[p];
-  }
-  const int kg = tid & 15, dg = tid >> 4;
-  if (dg < KCH) {
-    const int pos = slot_pos(kg * 4);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t w0 = r.v[0][w], w1 = r.v[1][w], w2 = r.v[2][w], w3 = r.v[3][w];
-      const u32x2 even = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-      const u32x2 odd = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-      *(u32x2*)&t.vt[dg * 8 + 2 * w][pos] = even;
-      *(u32x2*)&t.vt[dg * 8 + 2 * w + 1][pos] = odd;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void fwd_tile(const FwdParams& p, FwdTile<D>* sm, int qt, int b, int h, const u16* qb,
-                                         const u16* kb, const u16* vb) {
-  constexpr int NS = D / 16;   // 16-feature slabs of the score contraction
-  constexpr int NDB = D / 32;  // 32-feature blocks of the output
+__device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s, u16* k1s, u16* v1s, int qt, int b,
+                                         int h, const u16* qb, const u16* kb, const u16* vb) {
+  constexpr int NS = D / 16;
+  constexpr int NDB = D / 32;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
 
   const int q0 = qt * BM;
   const int qi = q0 + wave * 32 + lr;
   const bool qok = qi < p.Sq;
-
-  bf16x8 qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) qf[s] = as_bf16x8(load16(qb + (int64_t)qi * p.q.ss + s * 16 + lg * 8, qok));
 
   // Keys [0, kv_end) are visible to some query of this tile; keys [0, full_end)
   // to all of them.  Causal visibility: key j is visible to query i iff j <= delta + i.
@@ -119,93 +201,38 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, FwdTile<D>* sm, int
     lim64 = min<int64_t>(p.delta + qi, lim64);
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
+  if (n_tiles > 0) issue_tile<D>(k0s, v0s, kb, vb, p.k.ss, p.v.ss, 0, p.Sk, wave, lane);
 
+  bf16x8 qf[NS];
+  {
+    const u16* qrow = qb + (int64_t)qi * p.q.ss + lg * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = qok ? as_bf16x8(*(const u32x4*)(qrow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m_run = neg_inf(), l_run = 0.f;
+  RowState st{neg_inf(), 0.f};
+  const float sl2 = p.scale_log2;
 
-  KVRegs<D> regs;
-  if (n_tiles > 0) {
-    load_kv<D>(regs, kb, vb, p.k.ss, p.v.ss, 0, p.Sk, tid);
-    store_kv<D>(sm[0], regs, tid);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    const int key0 = t * BN;
-    if (t + 1 < n_tiles) load_kv<D>(regs, kb, vb, p.k.ss, p.v.ss, key0 + BN, p.Sk, tid);
-
-    // S^T = K Q^T for 64 keys (two 32-key blocks) x this wave's 32 queries.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)&sm[cur].k[kb2 * 32 + lr][s * 16 + lg * 8]);
-        sacc[kb2] = mfma32(a, qf[s], sacc[kb2]);
-      }
-    }
-    if (key0 + BN > full_end) {
-      const int lim = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, BN));
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          if (kl > lim) sacc[kb2][i] = neg_inf();
-        }
-    }
-
-    // Online softmax on raw scores; the scale is folded into the exponent.
-    float mt = neg_inf();
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb2][i]);
-    mt = fmaxf(mt, other_half(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = exp2_fast((m_run - m_use) * p.scale_log2);
-    const float nbias = -m_use * p.scale_log2;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = exp2_fast(fmaf(sacc[kb2][i], p.scale_log2, nbias));
-        sacc[kb2][i] = e;
-        rs += e;
-      }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
-    // O^T += V^T P^T over four 16-key slabs.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb2 = ks >> 1, o = (ks & 1) * 8;
-      const bf16x8 pb = cvt_bf16x8(sacc[kb2][o + 0], sacc[kb2][o + 1], sacc[kb2][o + 2], sacc[kb2][o + 3],
-                                   sacc[kb2][o + 4], sacc[kb2][o + 5], sacc[kb2][o + 6], sacc[kb2][o + 7]);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)&sm[cur].vt[db * 32 + lr][ks * 16 + lg * 8]);
-        oacc[db] = mfma32(a, pb, oacc[db]);
-      }
-    }
-
-    if (t + 1 < n_tiles) store_kv<D>(sm[cur ^ 1], regs, tid);
+  for (int t = 0; t < n_tiles; t += 2) {
+    wait_loads();
     __syncthreads();
+    if (t + 1 < n_tiles) issue_tile<D>(k1s, v1s, kb, vb, p.k.ss, p.v.ss, (t + 1) * BN, p.Sk, wave, lane);
+    tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, lane);
+    if (t + 1 >= n_tiles) break;
+    wait_loads();
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_tile<D>(k0s, v0s, kb, vb, p.k.ss, p.v.ss, (t + 2) * BN, p.Sk, wave, lane);
+    tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, lane);
   }
+  __syncthreads();  // the next call of this function reuses the buffers
 
   // Epilogue: normalise, optionally merge into the running result, store.
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = half_sum(st.l);
   if (!qok) return;
-  const float lse_this = (m_run == neg_inf()) ? neg_inf() : fmaf(m_run, p.scale, logf(l_tot));
+  const float lse_this = (l_tot > 0.f) ? fmaf(st.m, p.scale, logf(l_tot)) : neg_inf();
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Sq + qi;
   float w_old = 0.f, w_new = 1.f, L = lse_this;
@@ -235,8 +262,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, FwdTile<D>* sm, int
 }
 
 template <int D>
-__global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
-  __shared__ FwdTile<D> sm[2];
+__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
+  // Two separate LDS objects per buffer so the compiler can tell the tile being
+  // read from the tile being filled.
+  __shared__ __attribute__((aligned(16))) u16 k0s[Lds<D>::KSIZE];
+  __shared__ __attribute__((aligned(16))) u16 v0s[Lds<D>::VSIZE];
+  __shared__ __attribute__((aligned(16))) u16 k1s[Lds<D>::KSIZE];
+  __shared__ __attribute__((aligned(16))) u16 v1s[Lds<D>::VSIZE];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_units;
   const int bh = lin / p.n_units;
@@ -248,15 +280,12 @@ __global__ __launch_bounds__(NT) void fwd_bf16_kernel(FwdParams p) {
   if (p.balanced) {
     // Pair an early and a late query tile so every workgroup carries the same causal work.
     const int t0 = unit, t1 = p.n_qtiles - 1 - unit;
-    fwd_tile<D>(p, sm, t1, b, h, qb, kb, vb);
-    if (t0 != t1) {
-      __syncthreads();
-      fwd_tile<D>(p, sm, t0, b, h, qb, kb, vb);
-    }
+    fwd_tile<D>(p, k0s, v0s, k1s, v1s, t1, b, h, qb, kb, vb);
+    if (t0 != t1) fwd_tile<D>(p, k0s, v0s, k1s, v1s, t0, b, h, qb, kb, vb);
   } else {
     // Causal: heaviest tiles first, so the light ones fill the tail.
     const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
-    fwd_tile<D>(p, sm, qt, b, h, qb, kb, vb);
+    fwd_tile<D>(p, k0s, v0s, k1s, v1s, qt, b, h, qb, kb, vb);
   }
 }
 
