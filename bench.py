@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode"], default=None,
-                    help="run a single workload (for profiling)")
+    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "copy"], default=None,
+                    help="run a single workload (for profiling); 'copy' runs a plain 1 GiB device copy that "
+                         "calibrates the HBM traffic counters")
     return ap.parse_args()
 
 
@@ -94,14 +95,14 @@ def bench_main(args, stream):
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dq_acc = torch.empty((B, S, H, D), dtype=torch.float32, device="cuda")
-    delta = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    ws = shard.bwd_workspace(B, H, S, "cuda")
 
     def fwd():
         shard.causal_attention_forward(q, k, v, balanced=True, o=o, lse=lse, stream=stream)
 
     def bwd():
         shard.causal_attention_backward(q, k, v, o, do, lse, balanced=True, stream=stream, dq=dq, dk=dk, dv=dv,
-                                        dq_acc=dq_acc, delta=delta)
+                                        dq_acc=dq_acc, workspace=ws)
 
     (t_f, t_b), wall = time_calls([fwd, bwd], args.steps, args.warmup, stream)
     f_fwd = causal_flops(B, H, S, D)
@@ -141,11 +142,11 @@ def bench_shard(args, stream, do_bwd):
     dq = torch.empty_like(q)
     dk, dv = torch.empty_like(k), torch.empty_like(v)
     dq_acc = torch.empty((1, SQ, H, D), dtype=torch.float32, device="cuda")
-    delta = torch.empty((1, H, SQ), dtype=torch.float32, device="cuda")
+    ws = shard.bwd_workspace(1, H, SQ, "cuda")
 
     def bwd():
         shard.shard_backward(q, k, v, o, do, lse, CH, q_pos0=QP, causal=True, stream=stream, dq=dq, dk=dk, dv=dv,
-                             dq_acc=dq_acc, delta=delta)
+                             dq_acc=dq_acc, workspace=ws)
 
     (t,), _ = time_calls([bwd], max(3, args.steps), 1, stream)
     f_bwd = 2.5 * f_fwd
@@ -225,6 +226,14 @@ def main():
     if args.only == "decode":
         print(json.dumps(bench_decode(args, stream)), flush=True)
         return
+    if args.only == "copy":
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "copies": 3}), flush=True)
+        return
 
     m = bench_main(args, stream)
     print(f"# main: fwd {m['fwd_ms']:.2f} ms ({m['fwd_tflops']:.0f} TF/s), bwd {m['bwd_ms']:.2f} ms "
@@ -256,7 +265,7 @@ def main():
         "config": {"workload": "causal_fwdbwd_32k", "batch": m["B"], "heads": m["H"], "seq_len": m["S"],
                    "head_dim": m["D"], "causal": True, "schedule": "balanced", "parallelism": "single GPU"},
         "frac_of_mfma_peak": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_bwd call (delta + dK/dV + dQ kernels)",
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd call (statistics + dK/dV + dQ kernels)",
                      "achieved": round(bwd_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
         "kernels": {"fwd_call_ms": round(m["fwd_ms"], 3), "bwd_call_ms": round(m["bwd_ms"], 3),

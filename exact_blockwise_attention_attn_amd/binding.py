@@ -79,7 +79,7 @@ class BwdArgs(ctypes.Structure):
         ("v", c_vp), ("v_stride", I64x3),
         ("o", c_vp), ("o_stride", I64x3),
         ("dout", c_vp), ("do_stride", I64x3),
-        ("lse", c_vp), ("delta", c_vp), ("dq_acc", c_vp),
+        ("lse", c_vp), ("workspace", c_vp), ("workspace_bytes", ctypes.c_size_t), ("dq_acc", c_vp),
         ("dq", c_vp), ("dq_stride", I64x3),
         ("dk", c_vp), ("dk_stride", I64x3),
         ("dv", c_vp), ("dv_stride", I64x3),
@@ -108,6 +108,7 @@ EXPORTED = [
     "attn_merge_lse",
     "attn_bwd",
     "attn_decode_splitkv",
+    "attn_bwd_workspace_size",
     "attn_decode_workspace_size",
     "attn_status_string",
     "attn_last_error",
@@ -147,6 +148,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
+        lib.attn_bwd_workspace_size.argtypes = [c_i32, c_i32, c_i32]
+        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
         lib.attn_decode_workspace_size.restype = ctypes.c_size_t
         lib.attn_status_string.argtypes = [ctypes.c_int]
@@ -205,6 +208,10 @@ def attn_last_error() -> str:
     return load().attn_last_error().decode()
 
 
+def attn_bwd_workspace_size(batch: int, heads_q: int, seqlen_q: int) -> int:
+    return load().attn_bwd_workspace_size(batch, heads_q, seqlen_q)
+
+
 def attn_decode_workspace_size(batch: int, heads_q: int, head_dim: int, n_splits: int) -> int:
     return load().attn_decode_workspace_size(batch, heads_q, head_dim, n_splits)
 
@@ -246,7 +253,7 @@ def attn_merge_lse(o_parts, lse_parts, o_out, lse_out, *, tree=False, stream=Non
     _check(load().attn_merge_lse(ctypes.byref(a), _stream(stream)))
 
 
-def attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq=None, q_pos0=0, k_pos0=0, causal=False,
+def attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, *, dq=None, q_pos0=0, k_pos0=0, causal=False,
              scale=0.0, compute_delta=False, dq_overwrite=False, finalize_dq=False, balanced=False,
              stream=None) -> None:
     """Backward for one key chunk; see include/attn.h for the contract."""
@@ -260,7 +267,9 @@ def attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq=None, q_pos0=0,
     a.v, a.v_stride = _ptr(v), _strides3(v)
     a.o, a.o_stride = _ptr(o), _strides3(o)
     a.dout, a.do_stride = _ptr(dout), _strides3(dout)
-    a.lse, a.delta, a.dq_acc = _ptr(lse), _ptr(delta), _ptr(dq_acc)
+    a.lse, a.dq_acc = _ptr(lse), _ptr(dq_acc)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.dq, a.dq_stride = _ptr(dq), _strides3(dq)
     a.dk, a.dk_stride = _ptr(dk), _strides3(dk)
     a.dv, a.dv_stride = _ptr(dv), _strides3(dv)

@@ -224,10 +224,16 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   TRY(check_view("dk", a->dk, a->dk_stride, 3, a->dtype, has_k));
   TRY(check_view("dv", a->dv, a->dv_stride, 3, a->dtype, has_k));
   TRY(check_view("dq", a->dq, a->dq_stride, 3, a->dtype, has_q && finalize));
-  if (has_q && (!a->lse || !a->delta || !a->dq_acc))
-    return fail(ATTN_ERR_INVALID_ARG, "lse, delta and dq_acc must not be NULL");
-  if (has_q && (!aligned16(a->lse) || !aligned16(a->delta) || !aligned16(a->dq_acc)))
-    return fail(ATTN_ERR_UNSUPPORTED, "lse, delta and dq_acc must be 16-byte aligned");
+  if (has_q && (!a->lse || !a->dq_acc)) return fail(ATTN_ERR_INVALID_ARG, "lse and dq_acc must not be NULL");
+  if (has_q && (!aligned16(a->lse) || !aligned16(a->dq_acc)))
+    return fail(ATTN_ERR_UNSUPPORTED, "lse and dq_acc must be 16-byte aligned");
+  if (has_q) {
+    const size_t need = attn_bwd_workspace_size(a->batch, a->heads_q, a->seqlen_q);
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if ((uintptr_t)a->workspace & 255u) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   const int64_t units = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64) +
                         (int64_t)a->batch * a->heads_kv * ((a->seqlen_k + 63) / 64);
   if (units > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -242,7 +248,8 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   p.dk = mview(a->dk, a->dk_stride);
   p.dv = mview(a->dv, a->dv_stride);
   p.lse = a->lse;
-  p.delta = a->delta;
+  p.stats = (float*)a->workspace;
+  p.Sq_pad = (a->seqlen_q + 63) / 64 * 64;
   p.dq_acc = a->dq_acc;
   p.B = a->batch;
   p.Hq = a->heads_q;
@@ -263,8 +270,8 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   const int bf16 = a->dtype == ATTN_DTYPE_BF16;
   hipError_t e;
   if (has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)) {
-    e = attn::launch_bwd_delta(p, D, bf16, s);
-    if (e != hipSuccess) return hip_fail(e, "attn_bwd delta launch");
+    e = attn::launch_bwd_prepare(p, D, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd prepare launch");
   }
   // dQ needs a pass unless this chunk is invisible and dq_acc is left as it is.
   const bool invisible = !has_k || (p.causal && p.delta_pos + (a->seqlen_q - 1) < 0);
@@ -272,6 +279,12 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   e = bf16 ? attn::launch_bwd_bf16(p, D, run_dq, s) : attn::launch_bwd_f32(p, D, run_dq, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
   return ok();
+}
+
+size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
+  if (batch < 1 || heads_q < 1 || seqlen_q < 0) return 0;
+  const size_t sq_pad = ((size_t)seqlen_q + 63) / 64 * 64;
+  return ((size_t)batch * heads_q * 2 * sq_pad * sizeof(float) + 255) & ~(size_t)255;
 }
 
 size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits) {

@@ -52,7 +52,11 @@ struct BwdParams {
   View q, k, v, o, dout;
   MView dq, dk, dv;
   const float* lse;
-  float* delta;
+  // Per-row statistics workspace: for each (b, h), Sq_pad floats of LSE*log2(e)
+  // (+inf on rows that see no key and on padding rows) followed by Sq_pad
+  // floats of delta (0 on padding rows).  Sq_pad = Sq rounded up to 64.
+  float* stats;
+  int Sq_pad;
   float* dq_acc;  // contiguous [B, Sq, Hq, D]
   int B, Hq, Hkv, Sq, Sk;
   int group;
@@ -89,10 +93,11 @@ struct DecodeParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int D, hipStream_t s);
-// Backward: delta = rowsum(dO * O); then dK/dV (key-outer) and, when run_dq,
-// dQ (query-outer, accumulated into dq_acc).  Both kernels write every row
-// they own even when no pair is visible.
-hipError_t launch_bwd_delta(const BwdParams& p, int D, int is_bf16, hipStream_t s);
+// Backward: fill the statistics workspace (delta = rowsum(dO * O), rescaled
+// LSE); then dK/dV (key-outer) and, when run_dq, dQ (query-outer, accumulated
+// into dq_acc).  Both kernels write every row they own even when no pair is
+// visible.
+hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, int run_dq, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int D, int run_dq, hipStream_t s);
 // Decode: split partials into the workspace, then the per-(b, h) tree merge.

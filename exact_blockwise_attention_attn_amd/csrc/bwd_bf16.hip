@@ -7,13 +7,14 @@
 // and results do not depend on scheduling:
 //
 //   dK/dV kernel (key-outer).  A workgroup owns 128 keys of one key/value head
-//   (32 per wavefront, K and V held in registers as MFMA operands) and walks
-//   the query tiles of every query head that reads that key/value head.  Scores
-//   are formed as S = Q K^T, which puts one key per lane with the tile's
-//   queries in the lane's registers; P and dS then feed dV^T += dO^T P and
-//   dK^T += Q^T dS straight from registers.  Query and dO tiles stream from HBM
-//   into LDS (global_load_lds, double buffered); the transposed operands Q^T,
-//   dO^T are read from the same row-major tiles with ds_read_b64_tr_b16.
+//   and walks the query tiles of every query head that reads that key/value
+//   head.  Scores are formed as S = Q K^T, which puts one key per lane with the
+//   tile's queries in the lane's registers; P and dS then feed dV^T += dO^T P
+//   and dK^T += Q^T dS straight from registers.  Each group of 32 keys is
+//   served by a pair of wavefronts, one producing P and dV, the other dS and dK
+//   (see below).  Query and dO tiles stream from HBM into LDS (global_load_lds,
+//   double buffered); the transposed operands Q^T, dO^T are read from the same
+//   row-major tiles with ds_read_b64_tr_b16.
 //
 //   dQ kernel (query-outer).  A workgroup owns 128 queries (32 per wavefront,
 //   Q and dO in registers) and walks the key tiles.  Scores are formed
@@ -27,6 +28,7 @@
 // is the price of determinism without atomics.
 #include "attn_device.h"
 #include "attn_internal.h"
+#include "tile_lds.h"
 
 namespace attn {
 namespace {
@@ -36,151 +38,204 @@ constexpr int KBN = 128;  // keys per dK/dV workgroup
 constexpr int KBM = 64;   // queries per tile in the dK/dV kernel
 constexpr int QBM = 128;  // queries per dQ workgroup
 constexpr int QBN = 64;   // keys per tile in the dQ kernel
-constexpr int TR = 64;    // rows of a streamed tile
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
-typedef void __attribute__((address_space(3))) lds_void;
-
-// A streamed 64-row tile in LDS: rows padded by 16 bytes so the 8 rows an MFMA
-// operand read touches per LDS cycle start on distinct 16-byte bank groups.
-template <int D>
-struct Tile {
-  static constexpr int LD = D + 8;
-  static constexpr int RUNS = (TR * LD * 2 + 1023) / 1024;  // 1 KB global_load_lds runs
-  static constexpr int SIZE = RUNS * 512;                   // elements
-};
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Issue the copy of rows [row0, row0 + 64) of a [rows, D] view into a padded
-// LDS tile.  Wave w issues runs w, w+4, ...; lane l fills the l-th 16-byte slot
-// of a run.  Pad slots get a copy of the row's first chunk and are never read;
-// rows past the end load a valid row (their results are masked or dropped).
-template <int D>
-__device__ __forceinline__ void issue_tile(u16* lds, const u16* g, int64_t ss, int row0, int nrows, int wave,
-                                           int lane) {
-  using T = Tile<D>;
-#pragma unroll
-  for (int run = wave; run < T::RUNS; run += 4) {
-    const int e = run * 512 + lane * 8;
-    const int r = e / T::LD;
-    int col = e - r * T::LD;
-    if (col >= D) col = 0;
-    const int row = min(row0 + r, nrows - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)row * ss + col), (lds_void*)(lds + run * 512), 16, 0,
-                                     0);
-  }
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (LDS and export counters left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// Workgroup barrier for data exchanged through LDS by ordinary LDS stores.  A
+// fenced barrier (__syncthreads, or any release fence, since global_load_lds
+// writes LDS) makes every wavefront wait for all of its loads in flight, which
+// would drain the prefetches of later tiles at every barrier.  Here each
+// wavefront waits only for its own LDS stores; global_load_lds tiles are
+// waited for explicitly (wait_vm) before the barrier that publishes them.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 slab8(const f32x16& a, int o) {
   return cvt_bf16x8(a[o], a[o + 1], a[o + 2], a[o + 3], a[o + 4], a[o + 5], a[o + 6], a[o + 7]);
 }
 
-// Transposed operand for a 32x32x16 MFMA from a row-major padded tile: lane
-// (16q + s) gets feature (dcol + 16*(q%2) + s) of rows slab + 4*(q/2) + {0..3}
-// and slab + 8 + 4*(q/2) + {0..3}, which is the k-slot order of an operand that
-// comes straight out of an MFMA accumulator.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const u16* t, int slab_row, int dcol, int lane) {
-  const int q16 = lane >> 4, s16 = lane & 15;
-  const int r = slab_row + (q16 >> 1) * 4 + (s16 >> 2);
-  const int c = dcol + (q16 & 1) * 16 + 4 * (s16 & 3);
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + r * Tile<D>::LD + c));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + (r + 8) * Tile<D>::LD + c));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// LSE in log2 units; a row that sees no key gets +inf so that its P is 0.
-__device__ __forceinline__ float lse_log2(float lse) { return (lse == neg_inf()) ? pos_inf() : lse * kLog2e; }
-
 // ---------------------------------------------------------------- dK / dV --
+//
+// Eight wavefronts in four pairs; pair w%4 owns keys j0 + 32*(w%4) .. +31.
+// The "P" wavefront (w < 4) holds K as its register operand and accumulates
+// dV: it forms S = Q K^T, P = exp(S - LSE) (masked), hands P to its partner
+// through LDS and then runs dV^T += dO^T P.  The "dS" wavefront (w >= 4) holds
+// V and accumulates dK: it forms dP = dO V^T, reads P, dS = P (dP - delta) and
+// runs dK^T += Q^T dS.  Both halves carry 32 MFMAs per query tile, and each
+// wavefront keeps one operand and one accumulator instead of two of each, so
+// two wavefronts fit per SIMD.
 
-template <int D>
-__device__ __forceinline__ void dkdv_step(const u16* qs, const u16* dos, const float* l2s, const float* dls,
-                                          const bf16x8* kf, const bf16x8* vf, f32x16* dk, f32x16* dv, int i0,
-                                          bool need_mask, int64_t key_lim, float sl2, int lane) {
-  constexpr int NS = D / 16, NDB = D / 32, LD = Tile<D>::LD;
-  const int lr = lane & 31, lg = lane >> 5;
-  // S = Q K^T and dP = dO V^T: lane = key, registers = 32-query blocks.
-  f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const bf16x8 aq = as_bf16x8(*(const u32x4*)(qs + (qb * 32 + lr) * LD + s * 16 + lg * 8));
-      sacc[qb] = mfma32(aq, kf[s], sacc[qb]);
-      const bf16x8 ad = as_bf16x8(*(const u32x4*)(dos + (qb * 32 + lr) * LD + s * 16 + lg * 8));
-      pacc[qb] = mfma32(ad, vf[s], pacc[qb]);
-    }
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int qo = qb * 32 + g4 * 8 + lg * 4;
-      const f32x4 l4 = *(const f32x4*)(l2s + qo);
-      const f32x4 d4 = *(const f32x4*)(dls + qo);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = g4 * 4 + e;
-        float pv = exp2_fast(fmaf(sacc[qb][i], sl2, -l4[e]));
-        if (need_mask && (int64_t)(i0 + qo + e) < key_lim) pv = 0.f;
-        sacc[qb][i] = pv;
-        pacc[qb][i] = pv * (pacc[qb][i] - d4[e]);
-      }
-    }
-  }
-  // dV^T += dO^T P, dK^T += Q^T dS over four 16-query slabs.
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 pb = slab8(sacc[ks >> 1], (ks & 1) * 8);
-    const bf16x8 sb = slab8(pacc[ks >> 1], (ks & 1) * 8);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      dv[db] = mfma32(tr_operand<D>(dos, ks * 16, db * 32, lane), pb, dv[db]);
-      dk[db] = mfma32(tr_operand<D>(qs, ks * 16, db * 32, lane), sb, dk[db]);
-    }
-  }
-}
+constexpr int DKV_NT = 512;
+constexpr int DKV_STAGES = 3;  // query tiles in flight: the one in use and two being fetched
 
+// One pipeline stage: a query tile, a dO tile and their 64 rows of statistics.
+// Each stage is its own LDS object and every access names its stage at compile
+// time, so the compiler can see that reading one stage never overlaps the
+// global_load_lds writes still filling another.
 template <int D>
-struct DkvSmem {
-  u16 q[2][Tile<D>::SIZE];
-  u16 dO[2][Tile<D>::SIZE];
-  float lse2[2][KBM];
-  float dlt[2][KBM];
+struct DkvStage {
+  u16* q;
+  u16* dO;
+  float* st;  // [0, 64): LSE in log2 units, [64, 128): delta, [128, 256): unused
 };
 
 template <int D>
-__device__ __forceinline__ void dkdv_tile(const BwdParams& p, DkvSmem<D>& sm, int kt, int b, int hk) {
-  constexpr int NS = D / 16, NDB = D / 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int j0 = kt * KBN;
-  const int kj = j0 + wave * 32 + lr;  // this lane's key
-  const bool kok = kj < p.Sk;
+struct DkvCtx {
+  const BwdParams& p;
+  DkvStage<D> s0, s1, s2;
+  u32x4 (*pex)[4][64];  // [4 pairs] P in bf16, in accumulator (lane) order
+  RowFrag<D> rf;
+  TrFrag<D> tf;
+  int wave, lane, lr, lg, pair;
+};
 
-  const u16* kb = (const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
-  const u16* vb = (const u16*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
-  bf16x8 kf[NS], vf[NS];
-  {
-    const u16* kr = kb + (int64_t)kj * p.k.ss + lg * 8;
-    const u16* vr = vb + (int64_t)kj * p.v.ss + lg * 8;
+template <int D, int ST>
+__device__ __forceinline__ const DkvStage<D>& stage(const DkvCtx<D>& c) {
+  if constexpr (ST == 0) return c.s0;
+  else if constexpr (ST == 1) return c.s1;
+  else return c.s2;
+}
+
+// Fetch query tile tq of one head into stage ST: Q and dO rows, and (wave 0)
+// the 64 statistics of each kind in one 1 KB run.  The loads are untracked by
+// the compiler; dkdv_step waits for them before the barrier that publishes
+// the stage, and the last step of every head waits for all of them.
+template <int D, int ST>
+__device__ __forceinline__ void dkdv_issue(const DkvCtx<D>& c, const u16* qb, const u16* dob, const float* stb,
+                                           int tq) {
+  const DkvStage<D>& s = stage<D, ST>(c);
+  if (c.wave == 0) {
+    const int part = (c.lane >> 4) & 1;  // lanes 0-15 LSE, 16-31 delta; 32-63 repeat them
+    const float* src = stb + part * c.p.Sq_pad + tq * KBM + 4 * (c.lane & 15);
+    dma16_untracked(src, (lds_void*)s.st);
+  }
+  issue_swtile<D, 8, true>(s.q, qb, c.p.q.ss, tq * KBM, c.p.Sq, c.wave, c.lane);
+  issue_swtile<D, 8, true>(s.dO, dob, c.p.dout.ss, tq * KBM, c.p.Sq, c.wave, c.lane);
+}
+
+// One query tile of the dK/dV kernel from stage ST, for the P wavefront (PW)
+// or the dS wavefront.  The role is a compile-time constant so that every LDS
+// read names its tile directly: the compiler can then tell these reads apart
+// from the global_load_lds writes still filling the other stages and does not
+// wait for those.
+template <int D, int ST, bool PW>
+__device__ __forceinline__ void dkdv_compute(const DkvCtx<D>& c, const bf16x8* kv, f32x16* acc, int i0, bool need_mask,
+                                             int64_t key_lim, float sl2) {
+  constexpr int NS = D / 16, NDB = D / 32;
+  const DkvStage<D>& s = stage<D, ST>(c);
+  const int lg = c.lg, lane = c.lane;
+  // S = Q K^T (P wavefront) or dP = dO V^T (dS wavefront): lane = key,
+  // registers = two 32-query blocks.
+  const u16* rows = PW ? s.q : s.dO;
+  f32x16 sc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kf[s] = kok ? as_bf16x8(*(const u32x4*)(kr + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      vf[s] = kok ? as_bf16x8(*(const u32x4*)(vr + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  for (int si = 0; si < NS; ++si) {
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(c.rf.get(rows, qb2, si), kv[si], sc[qb2]);
+  }
+  bf16x8 opnd[4];  // B operands of the second contraction, one per 16-query slab
+  if constexpr (PW) {
+    // Causal mask: query i0 + q is hidden from this lane's key when
+    // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a bit
+    // mask, which keeps the 32 decisions in vector registers.
+    const int rel = need_mask ? (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM)) : 0;
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qo = qb2 * 32 + g4 * 8 + lg * 4;
+        const f32x4 l4 = *(const f32x4*)(s.st + qo);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = g4 * 4 + e;
+          const float pv = exp2_fast(fmaf(sc[qb2][i], sl2, -l4[e]));
+          const unsigned keep = ~(unsigned)((qo + e - rel) >> 31);
+          sc[qb2][i] = __uint_as_float(__float_as_uint(pv) & keep);
+        }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      opnd[ks] = slab8(sc[ks >> 1], (ks & 1) * 8);
+      c.pex[c.pair][ks][lane] = __builtin_bit_cast(u32x4, opnd[ks]);
     }
   }
-  f32x16 dk[NDB], dv[NDB];
+  lds_barrier();
+  if constexpr (!PW) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, c.pex[c.pair][ks][lane]);
+      const int qb2 = ks >> 1, o = (ks & 1) * 8;
+      // Slab ks holds queries 16*ks + 8*(e/4) + 4*lg + e%4: two groups of 4 consecutive deltas.
+      const f32x4 d0 = *(const f32x4*)(s.st + KBM + ks * 16 + lg * 4);
+      const f32x4 d1 = *(const f32x4*)(s.st + KBM + ks * 16 + 8 + lg * 4);
+      float ds[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (sc[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
+      opnd[ks] = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+    }
   }
+  // dV^T += dO^T P (P wavefront) or dK^T += Q^T dS (dS wavefront).
+  const u16* tsrc = PW ? s.dO : s.q;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = mfma32(c.tf.get(tsrc, ks, db), opnd[ks], acc[db]);
+  }
+}
+
+// Vector-memory operations one query tile adds per wavefront (wave 0 issues one more).
+template <int D>
+constexpr int dkdv_loads_per_tile() {
+  return 2 * ((SwTile<D>::RUNS + 7) / 8);
+}
+
+// Pipeline step for tile t in stage ST: wait for it, release the stage that
+// tile t + 2 will use, fetch tile t + 2, compute tile t.  Every wavefront of
+// either role passes the same two barriers per step.
+template <int D, int ST, bool PW>
+__device__ __forceinline__ void dkdv_step(const DkvCtx<D>& c, const bf16x8* kv, f32x16* acc, const u16* qb,
+                                          const u16* dob, const float* stb, int t, int n_qt, int i_full,
+                                          int64_t key_lim, float sl2) {
+  if (t + 1 < n_qt) wait_vm<dkdv_loads_per_tile<D>()>();  // only tile t + 1 may remain in flight
+  else wait_vm<0>();
+  lds_barrier();
+  if (t + 2 < n_qt) dkdv_issue<D, (ST + 2) % 3>(c, qb, dob, stb, t + 2);
+  dkdv_compute<D, ST, PW>(c, kv, acc, t * KBM, c.p.causal && t * KBM < i_full, key_lim, sl2);
+}
+
+template <int D, bool PW>
+__device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int hk) {
+  constexpr int NS = D / 16, NDB = D / 32;
+  const BwdParams& p = c.p;
+  const int j0 = kt * KBN;
+  const int kj = j0 + c.pair * 32 + c.lr;  // this lane's key
+  const bool kok = kj < p.Sk;
+
+  // Register operand: K rows for the P wavefront, V rows for the dS wavefront.
+  bf16x8 kv[NS];
+  {
+    const View& src = PW ? p.k : p.v;
+    const u16* base = (const u16*)src.ptr + (int64_t)b * src.sb + (int64_t)hk * src.sh + (int64_t)kj * src.ss;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kv[s] = kok ? as_bf16x8(*(const u32x4*)(base + c.lg * 8 + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x16 acc[NDB];  // dV^T (P wavefront) or dK^T (dS wavefront)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   // Query i sees key j iff j <= delta + i (causal).  Queries before i_start see
   // no key of this tile; from i_full on every query sees every key of it.
+  // Query rows past the end carry LSE = +inf in the statistics, so their P is 0.
   const int j_last = min(j0 + KBN, p.Sk) - 1;
   int i_start = 0, i_full = 0;
   if (p.causal) {
@@ -196,79 +251,69 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, DkvSmem<D>& sm, in
     const int h = hk * p.group + hh;
     const u16* qb = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const u16* dob = (const u16*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
-    const float* lseb = p.lse + ((int64_t)b * p.Hq + h) * p.Sq;
-    const float* dltb = p.delta + ((int64_t)b * p.Hq + h) * p.Sq;
-    // Row statistics of the next tile go through registers (one value per thread).
-    float nl = 0.f, nd = 0.f;
-    auto fetch_stats = [&](int tq) {
-      const int i = tq * KBM + tid;
-      if (tid < KBM) {
-        nl = (i < p.Sq) ? lse_log2(lseb[i]) : pos_inf();
-        nd = (i < p.Sq) ? dltb[i] : 0.f;
-      }
-    };
-    auto store_stats = [&](int buf) {
-      if (tid < KBM) {
-        sm.lse2[buf][tid] = nl;
-        sm.dlt[buf][tid] = nd;
-      }
-    };
-    if (t_start < n_qt) {
-      issue_tile<D>(sm.q[0], qb, p.q.ss, t_start * KBM, p.Sq, wave, lane);
-      issue_tile<D>(sm.dO[0], dob, p.dout.ss, t_start * KBM, p.Sq, wave, lane);
-      fetch_stats(t_start);
-      store_stats(0);
+    const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
+    if (t_start < n_qt) dkdv_issue<D, 0>(c, qb, dob, stb, t_start);
+    if (t_start + 1 < n_qt) dkdv_issue<D, 1>(c, qb, dob, stb, t_start + 1);
+    for (int t = t_start; t < n_qt; t += 3) {
+      dkdv_step<D, 0, PW>(c, kv, acc, qb, dob, stb, t, n_qt, i_full, key_lim, sl2);
+      if (t + 1 >= n_qt) break;
+      dkdv_step<D, 1, PW>(c, kv, acc, qb, dob, stb, t + 1, n_qt, i_full, key_lim, sl2);
+      if (t + 2 >= n_qt) break;
+      dkdv_step<D, 2, PW>(c, kv, acc, qb, dob, stb, t + 2, n_qt, i_full, key_lim, sl2);
     }
-    int buf = 0;
-    for (int t = t_start; t < n_qt; ++t) {
-      wait_loads();
-      __syncthreads();
-      if (t + 1 < n_qt) {
-        issue_tile<D>(sm.q[buf ^ 1], qb, p.q.ss, (t + 1) * KBM, p.Sq, wave, lane);
-        issue_tile<D>(sm.dO[buf ^ 1], dob, p.dout.ss, (t + 1) * KBM, p.Sq, wave, lane);
-        fetch_stats(t + 1);
-      }
-      const int i0 = t * KBM;
-      dkdv_step<D>(sm.q[buf], sm.dO[buf], sm.lse2[buf], sm.dlt[buf], kf, vf, dk, dv, i0,
-                   p.causal && i0 < i_full, key_lim, sl2, lane);
-      if (t + 1 < n_qt) store_stats(buf ^ 1);
-      buf ^= 1;
-    }
-    __syncthreads();  // buffers are reused by the next head / tile
+    lds_barrier();  // stages are reused by the next head / tile
   }
 
   if (!kok) return;
-  u16* dkp = (u16*)p.dk.ptr + (int64_t)b * p.dk.sb + (int64_t)kj * p.dk.ss + (int64_t)hk * p.dk.sh;
-  u16* dvp = (u16*)p.dv.ptr + (int64_t)b * p.dv.sb + (int64_t)kj * p.dv.ss + (int64_t)hk * p.dv.sh;
+  const float f = PW ? 1.0f : p.scale;
+  const MView& dst = PW ? p.dv : p.dk;
+  u16* out = (u16*)dst.ptr + (int64_t)b * dst.sb + (int64_t)kj * dst.ss + (int64_t)hk * dst.sh;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + j * 8 + lg * 4;
-      const f32x16& K = dk[db];
-      const f32x16& V = dv[db];
-      *(u32x2*)(dkp + d) = u32x2{pack_bf16x2(K[4 * j] * p.scale, K[4 * j + 1] * p.scale),
-                                 pack_bf16x2(K[4 * j + 2] * p.scale, K[4 * j + 3] * p.scale)};
-      *(u32x2*)(dvp + d) = u32x2{pack_bf16x2(V[4 * j], V[4 * j + 1]), pack_bf16x2(V[4 * j + 2], V[4 * j + 3])};
+      const int d = db * 32 + j * 8 + c.lg * 4;
+      const f32x16& A = acc[db];
+      *(u32x2*)(out + d) = u32x2{pack_bf16x2(A[4 * j] * f, A[4 * j + 1] * f), pack_bf16x2(A[4 * j + 2] * f, A[4 * j + 3] * f)};
     }
   }
 }
 
+// A work unit is one key tile, or with the balanced order the pair of key
+// tiles (u, n - 1 - u), whose causal work adds up to about the same for every u.
+// Early keys are seen by the most queries, so they come first.
+template <int D, bool PW>
+__device__ __forceinline__ void dkdv_unit(const DkvCtx<D>& c, int unit, int b, int hk) {
+  const BwdParams& p = c.p;
+  const int last = p.n_ktiles - 1 - unit;
+  const int n = (p.balanced && last != unit) ? 2 : 1;
+  for (int k = 0; k < n; ++k) dkdv_tile<D, PW>(c, k == 0 ? unit : last, b, hk);
+}
+
 template <int D>
-__global__ __launch_bounds__(NT) void dkdv_bf16_kernel(BwdParams p) {
-  __shared__ DkvSmem<D> sm;
+__global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) u16 q0[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 q1[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 q2[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d0[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d1[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d2[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) float st0[256];
+  __shared__ __attribute__((aligned(16))) float st1[256];
+  __shared__ __attribute__((aligned(16))) float st2[256];
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][4][64];
+  // The wavefront index is uniform across the wavefront; say so, so that the
+  // role branch below is a scalar branch.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  DkvCtx<D> c{p, {q0, d0, st0}, {q1, d1, st1}, {q2, d2, st2}, pex_s, {}, {}, wave, lane, lane & 31, lane >> 5, wave & 3};
+  c.rf.init(lane);
+  c.tf.init(lane);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_units_k;
   const int bh = lin / p.n_units_k;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  if (p.balanced) {
-    const int t0 = unit, t1 = p.n_ktiles - 1 - unit;
-    dkdv_tile<D>(p, sm, t0, b, hk);
-    if (t1 != t0) dkdv_tile<D>(p, sm, t1, b, hk);
-  } else {
-    // Causal: early keys are seen by the most queries; start with them.
-    dkdv_tile<D>(p, sm, unit, b, hk);
-  }
+  if (wave < 4) dkdv_unit<D, true>(c, unit, b, hk);
+  else dkdv_unit<D, false>(c, unit, b, hk);
 }
 
 // --------------------------------------------------------------------- dQ --
@@ -276,8 +321,8 @@ __global__ __launch_bounds__(NT) void dkdv_bf16_kernel(BwdParams p) {
 template <int D>
 __device__ __forceinline__ void dq_step(const u16* ks, const u16* vs, const bf16x8* qf, const bf16x8* dof,
                                         f32x16* acc, float lse2, float dlt, int key0, bool need_mask, int64_t lim64,
-                                        float sl2, int lane) {
-  constexpr int NS = D / 16, NDB = D / 32, LD = Tile<D>::LD;
+                                        float sl2, const RowFrag<D>& rf, const TrFrag<D>& tf, int lane) {
+  constexpr int NS = D / 16, NDB = D / 32;
   const int lr = lane & 31, lg = lane >> 5;
   const int lim = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, QBN));
   // Two 32-key halves keep only one score block live at a time.
@@ -287,10 +332,8 @@ __device__ __forceinline__ void dq_step(const u16* ks, const u16* vs, const bf16
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 ak = as_bf16x8(*(const u32x4*)(ks + (kb2 * 32 + lr) * LD + s * 16 + lg * 8));
-      sacc = mfma32(ak, qf[s], sacc);
-      const bf16x8 av = as_bf16x8(*(const u32x4*)(vs + (kb2 * 32 + lr) * LD + s * 16 + lg * 8));
-      pacc = mfma32(av, dof[s], pacc);
+      sacc = mfma32(rf.get(ks, kb2, s), qf[s], sacc);
+      pacc = mfma32(rf.get(vs, kb2, s), dof[s], pacc);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -304,7 +347,7 @@ __device__ __forceinline__ void dq_step(const u16* ks, const u16* vs, const bf16
       const bf16x8 sb = slab8(pacc, hs * 8);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma32(tr_operand<D>(ks, kb2 * 32 + hs * 16, db * 32, lane), sb, acc[db]);
+        acc[db] = mfma32(tf.get(ks, kb2 * 2 + hs, db), sb, acc[db]);
     }
   }
 }
@@ -312,10 +355,10 @@ __device__ __forceinline__ void dq_step(const u16* ks, const u16* vs, const bf16
 template <int D>
 __global__ __launch_bounds__(NT) void dq_bf16_kernel(BwdParams p) {
   constexpr int NS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 k0s[Tile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 v0s[Tile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 k1s[Tile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 v1s[Tile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_qtiles;
@@ -338,8 +381,8 @@ __global__ __launch_bounds__(NT) void dq_bf16_kernel(BwdParams p) {
   }
   const int n_tiles = (kv_end + QBN - 1) / QBN;
   if (n_tiles > 0) {
-    issue_tile<D>(k0s, kb, p.k.ss, 0, p.Sk, wave, lane);
-    issue_tile<D>(v0s, vb, p.v.ss, 0, p.Sk, wave, lane);
+    issue_swtile<D, 4>(k0s, kb, p.k.ss, 0, p.Sk, wave, lane);
+    issue_swtile<D, 4>(v0s, vb, p.v.ss, 0, p.Sk, wave, lane);
   }
 
   bf16x8 qf[NS], dof[NS];
@@ -353,10 +396,15 @@ __global__ __launch_bounds__(NT) void dq_bf16_kernel(BwdParams p) {
       dof[s] = qok ? as_bf16x8(*(const u32x4*)(drow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
   }
-  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + qi;
-  const float lse2 = qok ? lse_log2(p.lse[srow]) : pos_inf();
-  const float dlt = qok ? p.delta[srow] : 0.f;
+  // Statistics rows exist up to Sq_pad >= Sq; rows past Sq hold LSE = +inf, delta = 0.
+  const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
+  const float lse2 = qi < p.Sq_pad ? stb[qi] : pos_inf();
+  const float dlt = qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f;
   const float sl2 = p.scale_log2;
+  RowFrag<D> rf;
+  TrFrag<D> tf;
+  rf.init(lane);
+  tf.init(lane);
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -366,18 +414,18 @@ __global__ __launch_bounds__(NT) void dq_bf16_kernel(BwdParams p) {
     wait_loads();
     __syncthreads();
     if (t + 1 < n_tiles) {
-      issue_tile<D>(k1s, kb, p.k.ss, (t + 1) * QBN, p.Sk, wave, lane);
-      issue_tile<D>(v1s, vb, p.v.ss, (t + 1) * QBN, p.Sk, wave, lane);
+      issue_swtile<D, 4>(k1s, kb, p.k.ss, (t + 1) * QBN, p.Sk, wave, lane);
+      issue_swtile<D, 4>(v1s, vb, p.v.ss, (t + 1) * QBN, p.Sk, wave, lane);
     }
-    dq_step<D>(k0s, v0s, qf, dof, acc, lse2, dlt, t * QBN, t * QBN + QBN > full_end, lim64, sl2, lane);
+    dq_step<D>(k0s, v0s, qf, dof, acc, lse2, dlt, t * QBN, t * QBN + QBN > full_end, lim64, sl2, rf, tf, lane);
     if (t + 1 >= n_tiles) break;
     wait_loads();
     __syncthreads();
     if (t + 2 < n_tiles) {
-      issue_tile<D>(k0s, kb, p.k.ss, (t + 2) * QBN, p.Sk, wave, lane);
-      issue_tile<D>(v0s, vb, p.v.ss, (t + 2) * QBN, p.Sk, wave, lane);
+      issue_swtile<D, 4>(k0s, kb, p.k.ss, (t + 2) * QBN, p.Sk, wave, lane);
+      issue_swtile<D, 4>(v0s, vb, p.v.ss, (t + 2) * QBN, p.Sk, wave, lane);
     }
-    dq_step<D>(k1s, v1s, qf, dof, acc, lse2, dlt, (t + 1) * QBN, (t + 1) * QBN + QBN > full_end, lim64, sl2, lane);
+    dq_step<D>(k1s, v1s, qf, dof, acc, lse2, dlt, (t + 1) * QBN, (t + 1) * QBN + QBN > full_end, lim64, sl2, rf, tf, lane);
   }
 
   if (!qok) return;
@@ -408,9 +456,9 @@ hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s
   const int64_t gk = (int64_t)p.B * p.Hkv * p.n_units_k;
   if (gk > 0) {
     if (D == 128)
-      hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3((unsigned)gk), dim3(NT), 0, s, p);
+      hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p);
     else
-      hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3((unsigned)gk), dim3(NT), 0, s, p);
+      hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

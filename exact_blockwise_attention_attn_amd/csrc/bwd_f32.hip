@@ -1,5 +1,6 @@
-// Backward helpers shared by both dtypes (delta = rowsum(dO * O)) and the fp32
-// backward kernels (vector ALUs, fp32 end to end).
+// Backward helpers shared by both dtypes (the per-row statistics: delta =
+// rowsum(dO * O) and the rescaled LSE) and the fp32 backward kernels (vector
+// ALUs, fp32 end to end).
 //
 // fp32 dQ kernel: one thread per query row; key/value tiles staged in LDS.
 // fp32 dK/dV kernel: one thread per key row; query tiles (q, dO, LSE, delta)
@@ -11,42 +12,58 @@
 namespace attn {
 namespace {
 
-// ------------------------------------------------------------------ delta --
+// ---------------------------------------------------------------- prepare --
+// Fills the statistics workspace: for row i of (b, h), delta_i = sum_t dO_it O_it
+// and LSE_i * log2(e) (+inf when LSE_i = -inf, i.e. the row sees no key), plus
+// padding rows up to a multiple of 64 (LSE +inf, delta 0) so that the kernels
+// can fetch whole 64-row tiles of statistics.
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void delta_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
   constexpr int TPR = D / 8;  // threads per row, 8 features each
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / TPR;
+  const int64_t row = gid / TPR;  // over (b, h, padded i), i fastest
   const int c = (int)(gid % TPR);
-  const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq_pad;
   const bool ok = row < rows;
-  int h = 0, i = 0, b = 0;
+  int i = 0;
+  int64_t bh = 0;
   float acc = 0.f;
   if (ok) {
-    h = (int)(row % p.Hq);
-    i = (int)((row / p.Hq) % p.Sq);
-    b = (int)(row / ((int64_t)p.Hq * p.Sq));
-    const int64_t oo = (int64_t)b * p.o.sb + (int64_t)i * p.o.ss + (int64_t)h * p.o.sh + c * 8;
-    const int64_t od = (int64_t)b * p.dout.sb + (int64_t)i * p.dout.ss + (int64_t)h * p.dout.sh + c * 8;
-    if (BF16) {
-      const u32x4 a = *(const u32x4*)((const u16*)p.o.ptr + oo);
-      const u32x4 g = *(const u32x4*)((const u16*)p.dout.ptr + od);
+    i = (int)(row % p.Sq_pad);
+    bh = row / p.Sq_pad;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    if (i < p.Sq) {
+      const int64_t oo = (int64_t)b * p.o.sb + (int64_t)i * p.o.ss + (int64_t)h * p.o.sh + c * 8;
+      const int64_t od = (int64_t)b * p.dout.sb + (int64_t)i * p.dout.ss + (int64_t)h * p.dout.sh + c * 8;
+      if (BF16) {
+        const u32x4 a = *(const u32x4*)((const u16*)p.o.ptr + oo);
+        const u32x4 g = *(const u32x4*)((const u16*)p.dout.ptr + od);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = fmaf(bf16_lo(a[w]), bf16_lo(g[w]), acc);
-        acc = fmaf(bf16_hi(a[w]), bf16_hi(g[w]), acc);
+        for (int w = 0; w < 4; ++w) {
+          acc = fmaf(bf16_lo(a[w]), bf16_lo(g[w]), acc);
+          acc = fmaf(bf16_hi(a[w]), bf16_hi(g[w]), acc);
+        }
+      } else {
+        const float* a = (const float*)p.o.ptr + oo;
+        const float* g = (const float*)p.dout.ptr + od;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) acc = fmaf(a[w], g[w], acc);
       }
-    } else {
-      const float* a = (const float*)p.o.ptr + oo;
-      const float* g = (const float*)p.dout.ptr + od;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) acc = fmaf(a[w], g[w], acc);
     }
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-  if (ok && c == 0) p.delta[((int64_t)b * p.Hq + h) * p.Sq + i] = acc;
+  if (ok && c == 0) {
+    float* base = p.stats + bh * 2 * p.Sq_pad;
+    float l2 = pos_inf();
+    if (i < p.Sq) {
+      const float lse = p.lse[bh * p.Sq + i];
+      l2 = (lse == neg_inf()) ? pos_inf() : lse * kLog2e;
+    }
+    base[i] = l2;
+    base[p.Sq_pad + i] = (i < p.Sq) ? acc : 0.f;
+  }
 }
 
 // ------------------------------------------------------------- fp32 dQ ----
@@ -77,7 +94,7 @@ __global__ __launch_bounds__(FBM) void dq_f32_kernel(BwdParams p) {
   }
   const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + qi;
   const float lse = qok ? p.lse[srow] : neg_inf();
-  const float dlt = qok ? p.delta[srow] : 0.f;
+  const float dlt = qok ? p.stats[((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad + qi] : 0.f;
   const bool live = lse != neg_inf();
   const int q_last = min(qt * FBM + FBM, p.Sq) - 1;
   int kv_end = p.Sk;
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
     const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
     const float* lseb = p.lse + ((int64_t)b * p.Hq + h) * p.Sq;
-    const float* dltb = p.delta + ((int64_t)b * p.Hq + h) * p.Sq;
+    const float* dltb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad;
     for (int i0 = i_start; i0 < p.Sq; i0 += FTK) {
       __syncthreads();
       for (int e = tid; e < FTK * D; e += FBM) {
@@ -203,16 +220,16 @@ __global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_bwd_delta(const BwdParams& p, int D, int is_bf16, hipStream_t s) {
-  const int64_t threads = (int64_t)p.B * p.Sq * p.Hq * (D / 8);
+hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_t s) {
+  const int64_t threads = (int64_t)p.B * p.Hq * p.Sq_pad * (D / 8);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (D == 128) {
-    if (is_bf16) hipLaunchKernelGGL((delta_kernel<128, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((delta_kernel<128, false>), grid, dim3(256), 0, s, p);
+    if (is_bf16) hipLaunchKernelGGL((prepare_kernel<128, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prepare_kernel<128, false>), grid, dim3(256), 0, s, p);
   } else {
-    if (is_bf16) hipLaunchKernelGGL((delta_kernel<64, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((delta_kernel<64, false>), grid, dim3(256), 0, s, p);
+    if (is_bf16) hipLaunchKernelGGL((prepare_kernel<64, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prepare_kernel<64, false>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -10,8 +10,8 @@
 //     wavefront owns 32 queries; two workgroups share a CU;
 //   * key and value tiles of 64 rows go straight from HBM to LDS
 //     (global_load_lds, no register staging), double buffered: the next tile
-//     streams in while the current one is used.  Rows are padded so the MFMA
-//     operand reads hit distinct banks;
+//     streams in while the current one is used.  Chunks are swizzled so both
+//     the row reads and the transposing reads are free of bank conflicts;
 //   * scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
 //     the accumulator puts one query per lane (column) and 16 of its keys in
 //     the lane's registers, so row max and row sum are in-lane reductions plus
@@ -27,6 +27,7 @@
 //     element.
 #include "attn_device.h"
 #include "attn_internal.h"
+#include "tile_lds.h"
 
 namespace attn {
 namespace {
@@ -36,47 +37,12 @@ constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kRescaleSlack = 8.0f;  // exp2 units a row max may grow before O is rescaled
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
-typedef void __attribute__((address_space(3))) lds_void;
-
-// LDS row strides (elements).  K rows are padded by 16 bytes, so the 8 rows an
-// MFMA operand read touches per LDS cycle start on 8 distinct 16-byte bank
-// groups; V rows by 32 bytes, so the 4 rows a transposing read touches per
-// 16-lane group start on 4 distinct 32-byte bank groups.  With padding (not a
-// swizzle) every fragment address is one per-lane base plus an immediate.
-template <int D>
-struct Lds {
-  static constexpr int KLD = D + 8;
-  static constexpr int VLD = D + 16;
-  static constexpr int KRUNS = (BN * KLD * 2 + 1023) / 1024;  // 1 KB global_load_lds runs per tile
-  static constexpr int VRUNS = (BN * VLD * 2 + 1023) / 1024;
-  static constexpr int KSIZE = KRUNS * 512;  // elements, whole runs
-  static constexpr int VSIZE = VRUNS * 512;
-};
-
-// Copy one run of 64 chunks (1 KB of LDS, lane l -> chunk l) of a padded tile.
-// Pad slots receive a copy of the row's first chunk and are never read; rows
-// past the end load a valid row (always masked out), so LDS never holds garbage.
-template <int D, int LD>
-__device__ __forceinline__ void issue_run(u16* lds, const u16* g, int64_t ss, int key0, int Sk, int run, int lane) {
-  const int e = run * 512 + lane * 8;  // element offset of this lane's chunk
-  const int r = e / LD;
-  int col = e - r * LD;
-  if (col >= D) col = 0;
-  const int key = min(key0 + r, Sk - 1);
-  __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)key * ss + col), (lds_void*)(lds + run * 512), 16, 0, 0);
-}
-
-// Issue the global->LDS copy of one 64-row tile (K and V): wave w issues runs w, w+4, ...
+// Issue the global->LDS copy of one 64-row tile of K and of V.
 template <int D>
 __device__ __forceinline__ void issue_tile(u16* ks, u16* vs, const u16* kb, const u16* vb, int64_t k_ss,
                                            int64_t v_ss, int key0, int Sk, int wave, int lane) {
-  using L = Lds<D>;
-#pragma unroll
-  for (int run = wave; run < L::KRUNS; run += 4) issue_run<D, L::KLD>(ks, kb, k_ss, key0, Sk, run, lane);
-#pragma unroll
-  for (int run = wave; run < L::VRUNS; run += 4) issue_run<D, L::VLD>(vs, vb, v_ss, key0, Sk, run, lane);
+  issue_swtile<D, 4>(ks, kb, k_ss, key0, Sk, wave, lane);
+  issue_swtile<D, 4>(vs, vb, v_ss, key0, Sk, wave, lane);
 }
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
@@ -99,7 +65,7 @@ struct RowState {
 template <int D>
 __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf16x8* qf, f32x16* oacc,
                                           RowState& st, int key0, bool need_mask, int64_t lim64, float sl2,
-                                          int lane) {
+                                          const RowFrag<D>& rf, const TrFrag<D>& tf, int lane) {
   constexpr int NS = D / 16, NDB = D / 32;
   const int lr = lane & 31, lg = lane >> 5;
 
@@ -108,8 +74,7 @@ __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const bf16x8 a = as_bf16x8(*(const u32x4*)(ks + (kb2 * 32 + lr) * Lds<D>::KLD + s * 16 + lg * 8));
-      sacc[kb2] = mfma32(a, qf[s], sacc[kb2]);
+      sacc[kb2] = mfma32(rf.get(ks, kb2, s), qf[s], sacc[kb2]);
     }
   }
   if (need_mask) {
@@ -153,28 +118,14 @@ __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf
     }
   st.l += rs;
 
-  // O^T += V^T P^T over four 16-key slabs.  Lane (16q + s) of a transposing read
-  // fetches 4 features of key (slab + 8h + 4*(q/2) + s/4); the read hands lane
-  // d = 16*(q%2) + s the 4 keys of its k-slots 4h .. 4h+3.
-  const int q16 = lane >> 4, s16 = lane & 15;
-  const int krow0 = (q16 >> 1) * 4 + (s16 >> 2);
-  const int fcol = (q16 & 1) * 16 + 4 * (s16 & 3);
+  // O^T += V^T P^T over four 16-key slabs; V^T comes from the transposing read.
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int kb2 = ks >> 1, o = (ks & 1) * 8;
     const bf16x8 pb = cvt_bf16x8(sacc[kb2][o + 0], sacc[kb2][o + 1], sacc[kb2][o + 2], sacc[kb2][o + 3],
                                  sacc[kb2][o + 4], sacc[kb2][o + 5], sacc[kb2][o + 6], sacc[kb2][o + 7]);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      i16x4 part[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs + (ks * 16 + h * 8 + krow0) * Lds<D>::VLD + db * 32 + fcol));
-      }
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[db] = mfma32(a, pb, oacc[db]);
-    }
+    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(tf.get(vs, ks, db), pb, oacc[db]);
   }
 }
 
@@ -215,17 +166,21 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   RowState st{neg_inf(), 0.f};
   const float sl2 = p.scale_log2;
+  RowFrag<D> rf;
+  TrFrag<D> tf;
+  rf.init(lane);
+  tf.init(lane);
 
   for (int t = 0; t < n_tiles; t += 2) {
     wait_loads();
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile<D>(k1s, v1s, kb, vb, p.k.ss, p.v.ss, (t + 1) * BN, p.Sk, wave, lane);
-    tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, lane);
+    tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf, lane);
     if (t + 1 >= n_tiles) break;
     wait_loads();
     __syncthreads();
     if (t + 2 < n_tiles) issue_tile<D>(k0s, v0s, kb, vb, p.k.ss, p.v.ss, (t + 2) * BN, p.Sk, wave, lane);
-    tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, lane);
+    tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, rf, tf, lane);
   }
   __syncthreads();  // the next call of this function reuses the buffers
 
@@ -265,10 +220,10 @@ template <int D>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   // Two separate LDS objects per buffer so the compiler can tell the tile being
   // read from the tile being filled.
-  __shared__ __attribute__((aligned(16))) u16 k0s[Lds<D>::KSIZE];
-  __shared__ __attribute__((aligned(16))) u16 v0s[Lds<D>::VSIZE];
-  __shared__ __attribute__((aligned(16))) u16 k1s[Lds<D>::KSIZE];
-  __shared__ __attribute__((aligned(16))) u16 v1s[Lds<D>::VSIZE];
+  __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_units;
   const int bh = lin / p.n_units;

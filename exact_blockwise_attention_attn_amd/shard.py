@@ -75,8 +75,14 @@ def shard_forward_partials(q, k, v, chunk, *, q_pos0=0, k_pos0=0, causal=False, 
     return o, lse, (o_parts, lse_parts)
 
 
+def bwd_workspace(batch, heads_q, seqlen_q, device):
+    """A statistics workspace for attn_bwd (uint8, 256-byte aligned by the caching allocator)."""
+    n = B.attn_bwd_workspace_size(batch, heads_q, seqlen_q)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def shard_backward(q, k, v, o, dout, lse, chunk, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0, stream=None,
-                   dq=None, dk=None, dv=None, dq_acc=None, delta=None):
+                   dq=None, dk=None, dv=None, dq_acc=None, workspace=None):
     """Gradients for a query shard whose keys come in chunks.  Returns (dq, dk, dv)."""
     b, sq, hq, d = q.shape
     sk, hkv = k.shape[1], k.shape[2]
@@ -85,13 +91,13 @@ def shard_backward(q, k, v, o, dout, lse, chunk, *, q_pos0=0, k_pos0=0, causal=F
     dk = torch.empty((b, sk, hkv, d), dtype=q.dtype, device=dev) if dk is None else dk
     dv = torch.empty((b, sk, hkv, d), dtype=q.dtype, device=dev) if dv is None else dv
     dq_acc = torch.empty((b, sq, hq, d), dtype=torch.float32, device=dev) if dq_acc is None else dq_acc
-    delta = torch.empty((b, hq, sq), dtype=torch.float32, device=dev) if delta is None else delta
+    workspace = bwd_workspace(b, hq, sq, dev) if workspace is None else workspace
     bounds = chunk_bounds(sk, chunk) or [(0, 0)]
     live = [i for i, (a, _) in enumerate(bounds) if _chunk_visible(q_pos0, sq, k_pos0 + a, causal)]
     first_dq = live[0] if live else 0
     last_dq = live[-1] if live else 0
     for i, (a, e) in enumerate(bounds):
-        B.attn_bwd(q, k[:, a:e], v[:, a:e], o, dout, lse, delta, dq_acc, dk[:, a:e], dv[:, a:e], dq=dq,
+        B.attn_bwd(q, k[:, a:e], v[:, a:e], o, dout, lse, workspace, dq_acc, dk[:, a:e], dv[:, a:e], dq=dq,
                    q_pos0=q_pos0, k_pos0=k_pos0 + a, causal=causal, scale=scale, compute_delta=i == 0,
                    dq_overwrite=i == first_dq, finalize_dq=i == last_dq, stream=stream)
     return dq, dk, dv
@@ -106,14 +112,14 @@ def causal_attention_forward(q, k, v, *, scale=0.0, balanced=True, o=None, lse=N
 
 
 def causal_attention_backward(q, k, v, o, dout, lse, *, scale=0.0, balanced=True, stream=None,
-                              dq=None, dk=None, dv=None, dq_acc=None, delta=None):
+                              dq=None, dk=None, dv=None, dq_acc=None, workspace=None):
     b, s, hq, d = q.shape
     dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     dq_acc = torch.empty((b, s, hq, d), dtype=torch.float32, device=dev) if dq_acc is None else dq_acc
-    delta = torch.empty((b, hq, s), dtype=torch.float32, device=dev) if delta is None else delta
-    B.attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq=dq, causal=True, scale=scale, compute_delta=True,
+    workspace = bwd_workspace(b, hq, s, dev) if workspace is None else workspace
+    B.attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, dq=dq, causal=True, scale=scale, compute_delta=True,
                dq_overwrite=True, finalize_dq=True, balanced=balanced, stream=stream)
     return dq, dk, dv

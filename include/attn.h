@@ -31,7 +31,7 @@
  * Conventions shared by every entry point:
  *   - Tensors of shape [batch, seq, heads, head_dim] are given by a base pointer
  *     and three element strides (batch, seq, head); the head_dim stride is 1.
- *     LSE and delta vectors are contiguous fp32 [batch, heads, seq].
+ *     LSE vectors are contiguous fp32 [batch, heads, seq].
  *   - All pointers are device pointers unless stated otherwise, 16-byte
  *     aligned, and element strides must keep every row start 16-byte aligned.
  *     The caller owns every buffer; the library never allocates, frees or
@@ -46,6 +46,8 @@
  *   - head_dim must be 64 or 128.  Scale 0 means 1/sqrt(head_dim); otherwise it
  *     must be finite and positive.
  *   - The library keeps no mutable global state; calls are thread-safe.
+ *   - Scratch memory is always caller-provided (a workspace argument sized by
+ *     attn_*_workspace_size); the library never allocates.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -63,7 +65,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -152,7 +154,7 @@ typedef struct attn_merge_args {
 ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
 
 /* attn_bwd flags. */
-#define ATTN_BWD_COMPUTE_DELTA (1u << 0) /* write delta = rowsum(dO * O) first; else read it */
+#define ATTN_BWD_COMPUTE_DELTA (1u << 0) /* fill the workspace from o, dout and lse first; else reuse it */
 #define ATTN_BWD_DQ_OVERWRITE (1u << 1)  /* dq_acc = this chunk's dQ instead of dq_acc += it */
 #define ATTN_BWD_FINALIZE_DQ (1u << 2)   /* after accumulating, write dq = dq_acc in `dtype` */
 #define ATTN_BWD_BALANCED (1u << 3)      /* causal work order pairing early and late key tiles */
@@ -167,11 +169,17 @@ ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
  *   dv_j = sum_i P_ij dO_i,   dk_j = scale sum_i dS_ij q_i   (written, this chunk's keys)
  *   dq_i += scale sum_j dS_ij k_j                           (accumulated in dq_acc)
  * With grouped heads, dk/dv of a key/value head sum over the query heads that
- * share it.  dq_acc is fp32 [batch, seqlen_q, heads_q, head_dim] contiguous;
- * delta is fp32 [batch, heads_q, seqlen_q].  Rows with LSE = -inf contribute
- * nothing; a chunk no query sees writes dk = dv = 0 and adds nothing to dq.
- * Results do not depend on scheduling: no floating-point atomics are used.
- * dq, dk, dv are written in `dtype`.
+ * share it.  dq_acc is fp32 [batch, seqlen_q, heads_q, head_dim] contiguous.
+ * The workspace (device memory of at least attn_bwd_workspace_size(...) bytes,
+ * 256-byte aligned) holds the per-row statistics: for each (b, h) in row-major
+ * order, Sq_pad = round_up(seqlen_q, 64) floats of LSE * log2(e) (+inf for rows
+ * with LSE = -inf and for padding rows) followed by Sq_pad floats of delta (0 on
+ * padding rows).  ATTN_BWD_COMPUTE_DELTA fills it; later calls for other key
+ * chunks of the same o, dout and lse may reuse it without the flag.  A row with
+ * LSE = -inf must have no visible key; it contributes nothing.  A chunk no query
+ * sees writes dk = dv = 0 and adds nothing to dq.  Results do not depend on
+ * scheduling: no floating-point atomics are used.  dq, dk, dv are written in
+ * `dtype`.
  */
 typedef struct attn_bwd_args {
   uint32_t struct_size;
@@ -188,7 +196,8 @@ typedef struct attn_bwd_args {
   const void* dout;
   int64_t do_stride[3];
   const float* lse;
-  float* delta;
+  void* workspace;
+  size_t workspace_bytes;
   float* dq_acc;
   void* dq; /* used with ATTN_BWD_FINALIZE_DQ, else may be NULL */
   int64_t dq_stride[3];
@@ -240,6 +249,9 @@ typedef struct attn_decode_args {
 } attn_decode_args;
 
 ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
+
+/* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
+ATTN_API size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q);
 
 /* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes). */
 ATTN_API size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits);

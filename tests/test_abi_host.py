@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -55,6 +55,7 @@ int main(void) {
   P(attn_fwd_args, flags); P(attn_fwd_args, o_final_stride); P(attn_fwd_args, q_pos0);
   P(attn_merge_args, mode); P(attn_merge_args, lse_out);
   P(attn_bwd_args, flags); P(attn_bwd_args, dv_stride); P(attn_bwd_args, dq_acc);
+  P(attn_bwd_args, workspace); P(attn_bwd_args, workspace_bytes);
   P(attn_decode_args, workspace_bytes); P(attn_decode_args, n_splits); P(attn_decode_args, o_stride);
   return 0;
 }
@@ -78,7 +79,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -86,6 +87,13 @@ def test_helpers(lib):
     assert lib.attn_decode_workspace_size(16, 32, 128, 64) == 16 * 32 * 64 * 128 * 4 + 16 * 32 * 64 * 4
     assert lib.attn_decode_workspace_size(1, 1, 96, 4) == 0
     assert lib.attn_decode_workspace_size(1, 1, 128, 0) == 0
+    # Backward statistics: 2 floats per row, rows padded to 64, total rounded to 256 bytes.
+    assert lib.attn_bwd_workspace_size(2, 32, 32768) == 2 * 32 * 2 * 32768 * 4
+    assert lib.attn_bwd_workspace_size(1, 1, 1) == 512
+    assert lib.attn_bwd_workspace_size(1, 3, 65) == 3 * 2 * 128 * 4
+    assert lib.attn_bwd_workspace_size(1, 1, 0) == 0
+    assert lib.attn_bwd_workspace_size(0, 1, 64) == 0
+    assert lib.attn_bwd_workspace_size(1, 1, -1) == 0
 
 
 def fwd_args(**kw):
@@ -178,8 +186,9 @@ def bwd_args(**kw):
     a.struct_size = ctypes.sizeof(B.BwdArgs)
     a.dtype = B.ATTN_DTYPE_BF16
     a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.seqlen_k, a.head_dim = 1, 2, 2, 32, 32, 64
-    for name in ("q", "k", "v", "o", "dout", "lse", "delta", "dq_acc", "dq", "dk", "dv"):
+    for name in ("q", "k", "v", "o", "dout", "lse", "workspace", "dq_acc", "dq", "dk", "dv"):
         setattr(a, name, FAKE)
+    a.workspace_bytes = 2 * 2 * 64 * 4
     st = B.I64x3(32 * 2 * 64, 2 * 64, 64)
     for name in ("q_stride", "k_stride", "v_stride", "o_stride", "do_stride", "dq_stride", "dk_stride", "dv_stride"):
         setattr(a, name, st)
@@ -191,7 +200,10 @@ def bwd_args(**kw):
 BWD_BAD = [
     (dict(flags=1 << 9), B.ATTN_ERR_INVALID_ARG, "flag"),
     (dict(dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
-    (dict(delta=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(lse=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(workspace=None), B.ATTN_ERR_WORKSPACE, "workspace of 1024 bytes"),
+    (dict(workspace_bytes=1023), B.ATTN_ERR_WORKSPACE, "1023 given"),
+    (dict(workspace=FAKE + 16), B.ATTN_ERR_WORKSPACE, "256-byte"),
     (dict(dk=None), B.ATTN_ERR_INVALID_ARG, "dk is NULL"),
     (dict(dq=None, flags=B.ATTN_BWD_FINALIZE_DQ), B.ATTN_ERR_INVALID_ARG, "dq is NULL"),
     (dict(o=None, flags=B.ATTN_BWD_COMPUTE_DELTA), B.ATTN_ERR_INVALID_ARG, "o is NULL"),

@@ -176,14 +176,20 @@ def test_bwd(case):
     B.attn_fwd_partial(q, k, v, o, lse, q_pos0=qp, k_pos0=kp, causal=causal)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dq_acc = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    delta = torch.empty((Bn, Hq, Sq), dtype=torch.float32, device="cuda")
-    B.attn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, dq=dq, q_pos0=qp, k_pos0=kp, causal=causal,
+    ws = torch.full((B.attn_bwd_workspace_size(Bn, Hq, Sq) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_bwd(q, k, v, o, do, lse, ws, dq_acc, dk, dv, dq=dq, q_pos0=qp, k_pos0=kp, causal=causal,
                compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=bal)
     torch.cuda.synchronize()
     check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
     check("dK", dk, dk_ref, G_TOL, scale_by_max=True)
     check("dV", dv, dv_ref, G_TOL, scale_by_max=True)
-    check("delta", delta, np.einsum("bshd,bshd->bhs", doh, O_ref), G_TOL, scale_by_max=True)
+    # Workspace layout: per (b, h), Sq_pad rows of LSE*log2(e) then Sq_pad rows of delta.
+    sq_pad = (Sq + 63) // 64 * 64
+    st = ws[: Bn * Hq * 2 * sq_pad].view(Bn, Hq, 2, sq_pad).cpu().double().numpy()
+    check("delta", st[:, :, 1, :Sq], np.einsum("bshd,bshd->bhs", doh, O_ref), G_TOL, scale_by_max=True)
+    l2_ref = np.where(np.isneginf(L_ref), np.inf, L_ref * math.log2(math.e))
+    check("lse*log2e", st[:, :, 0, :Sq], l2_ref, L_TOL * math.log2(math.e))
+    assert np.all(st[:, :, 0, Sq:] == np.inf) and np.all(st[:, :, 1, Sq:] == 0)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
