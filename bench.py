@@ -34,6 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+# HBM bytes per backward call of the workload above, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
+# of these kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
+# copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md).  None once the kernels change.
+BWD_CALL_HBM_BYTES = 1.8994e10
 HBM_PEAK_GBS = 8000.0
 
 
@@ -267,7 +271,7 @@ def main():
         "frac_of_mfma_peak": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_bwd call (statistics + dK/dV + dQ kernels)",
                      "achieved": round(bwd_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": BWD_CALL_HBM_BYTES},
         "kernels": {"fwd_call_ms": round(m["fwd_ms"], 3), "bwd_call_ms": round(m["bwd_ms"], 3),
                     "fwd_tflops": round(m["fwd_tflops"], 2), "bwd_tflops": round(m["bwd_tflops"], 2),
                     "event_ms_per_step": round(m["event_ms"], 3)},
