@@ -34,10 +34,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-# HBM bytes per backward call of the workload above, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
-# of these kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
-# copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md).  None once the kernels change.
-BWD_CALL_HBM_BYTES = 1.8994e10
+# HBM bytes per backward call of the causal 32K workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# runs of its kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
+# copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md).  None until re-measured after the
+# kernels change.
+BWD_CALL_HBM_BYTES = None
 HBM_PEAK_GBS = 8000.0
 
 

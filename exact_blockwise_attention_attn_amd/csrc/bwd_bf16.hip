@@ -143,22 +143,27 @@ __device__ __forceinline__ void dkdv_compute(const DkvCtx<D>& c, const bf16x8* k
   }
   bf16x8 opnd[4];  // B operands of the second contraction, one per 16-query slab
   if constexpr (PW) {
-    // Causal mask: query i0 + q is hidden from this lane's key when
-    // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a bit
-    // mask, which keeps the 32 decisions in vector registers.
-    const int rel = need_mask ? (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM)) : 0;
 #pragma unroll
     for (int qb2 = 0; qb2 < 2; ++qb2) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int qo = qb2 * 32 + g4 * 8 + lg * 4;
-        const f32x4 l4 = *(const f32x4*)(s.st + qo);
+        const f32x4 l4 = *(const f32x4*)(s.st + qb2 * 32 + g4 * 8 + lg * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = g4 * 4 + e;
-          const float pv = exp2_fast(fmaf(sc[qb2][i], sl2, -l4[e]));
-          const unsigned keep = ~(unsigned)((qo + e - rel) >> 31);
-          sc[qb2][i] = __uint_as_float(__float_as_uint(pv) & keep);
+        for (int e = 0; e < 4; ++e) sc[qb2][g4 * 4 + e] = exp2_fast(fmaf(sc[qb2][g4 * 4 + e], sl2, -l4[e]));
+      }
+    }
+    if (need_mask) {
+      // Causal mask: query i0 + q is hidden from this lane's key when
+      // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a bit
+      // mask, which keeps the 32 decisions in vector registers.
+      const int rel = (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM));
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qo = qb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
+          const unsigned keep = ~(unsigned)((qo - rel) >> 31);
+          sc[qb2][i] = __uint_as_float(__float_as_uint(sc[qb2][i]) & keep);
         }
       }
     }
@@ -229,6 +234,10 @@ __device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int
     for (int s = 0; s < NS; ++s)
       kv[s] = kok ? as_bf16x8(*(const u32x4*)(base + c.lg * 8 + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
+  // Complete these loads here: left to the compiler, the wait for them sits at
+  // their first use inside the loop, where it would also drain every tile
+  // prefetch in flight on each pass.
+  wait_vm<0>();
   f32x16 acc[NDB];  // dV^T (P wavefront) or dK^T (dS wavefront)
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
@@ -317,133 +326,177 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
 }
 
 // --------------------------------------------------------------------- dQ --
+//
+// Eight wavefronts in four pairs; pair w%4 owns queries q0 + 32*(w%4) .. +31.
+// Key/value tiles of 64 rows stream through a 3-stage LDS ring and are
+// consumed in 32-key steps.  At step k:
+//   * the "S" wavefront (w < 4) holds Q in registers, forms S^T = K Q^T for the
+//     keys of step k (one query per lane), P = exp(S - LSE) with the mask, and
+//     hands P to its partner through LDS;
+//   * the "dP" wavefront (w >= 4) holds dO and the whole dQ^T accumulator,
+//     forms dP^T = V dO^T for step k, and for step k - 1 (one step behind, so
+//     that P is already published) reads P, forms dS = P (dP - delta) and runs
+//     dQ^T += K^T dS^T.
+// The S wavefront carries the exponentials, the dP wavefront two thirds of the
+// contractions; a pair shares one SIMD, whose matrix core they keep busy in
+// turn.  One LDS-only barrier per step publishes P and, every other step, the
+// next key/value tile.
+
+constexpr int DQ_NT = 512;
 
 template <int D>
-__device__ __forceinline__ void dq_step(const u16* ks, const u16* vs, const bf16x8* qf, const bf16x8* dof,
-                                        f32x16* acc, float lse2, float dlt, int key0, bool need_mask, int64_t lim64,
-                                        float sl2, const RowFrag<D>& rf, const TrFrag<D>& tf, int lane) {
-  constexpr int NS = D / 16, NDB = D / 32;
-  const int lr = lane & 31, lg = lane >> 5;
-  const int lim = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, QBN));
-  // Two 32-key halves keep only one score block live at a time.
-#pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    // S^T = K Q^T and dP^T = V dO^T: lane = query, registers = 32 keys.
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sacc = mfma32(rf.get(ks, kb2, s), qf[s], sacc);
-      pacc = mfma32(rf.get(vs, kb2, s), dof[s], pacc);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float pv = exp2_fast(fmaf(sacc[i], sl2, -lse2));
-      if (need_mask && kb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3) > lim) pv = 0.f;
-      pacc[i] = pv * (pacc[i] - dlt);
-    }
-    // dQ^T += K^T dS^T over the two 16-key slabs of this half.
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const bf16x8 sb = slab8(pacc, hs * 8);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = mfma32(tf.get(ks, kb2 * 2 + hs, db), sb, acc[db]);
-    }
-  }
+constexpr int dq_loads_per_tile() {
+  return 2 * (SwTile<D>::RUNS / 8);
 }
 
-template <int D>
-__global__ __launch_bounds__(NT) void dq_bf16_kernel(BwdParams p) {
-  constexpr int NS = D / 16, NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = lin % p.n_qtiles;
-  const int bh = lin / p.n_qtiles;
-  const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
-  const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
-  const int q0 = qt * QBM;
-  const int qi = q0 + wave * 32 + lr;
+template <int D, bool SW>
+__device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, u32x4 (*pex)[2][2][64], int wave,
+                                        int lane, int b, int h, int q0) {
+  constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE, L = dq_loads_per_tile<D>();
+  const int lr = lane & 31, lg = lane >> 5, pair = wave & 3;
+  const int hk = h / p.group;
+  const int qi = q0 + pair * 32 + lr;
   const bool qok = qi < p.Sq;
-
   const u16* kb = (const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
   const u16* vb = (const u16*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
   const int q_last = min(q0 + QBM, p.Sq) - 1;
   int kv_end = p.Sk, full_end = p.Sk;
-  int64_t lim64 = (int64_t)p.Sk - 1;
+  int64_t lim64 = (int64_t)p.Sk - 1;  // last key this lane's query sees
   if (p.causal) {
     kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q_last + 1, p.Sk));
     full_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q0 + 1, p.Sk));
     lim64 = min<int64_t>(p.delta_pos + qi, lim64);
   }
-  const int n_tiles = (kv_end + QBN - 1) / QBN;
-  if (n_tiles > 0) {
-    issue_swtile<D, 4>(k0s, kb, p.k.ss, 0, p.Sk, wave, lane);
-    issue_swtile<D, 4>(v0s, vb, p.v.ss, 0, p.Sk, wave, lane);
-  }
+  const int n = (kv_end + QBN - 1) / QBN;
 
-  bf16x8 qf[NS], dof[NS];
+  // Register operand (Q rows or dO rows of this lane's query) and statistic.
+  bf16x8 op[NS];
   {
-    const u16* qrow = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh + (int64_t)qi * p.q.ss + lg * 8;
-    const u16* drow =
-        (const u16*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh + (int64_t)qi * p.dout.ss + lg * 8;
+    const View& src = SW ? p.q : p.dout;
+    const u16* row = (const u16*)src.ptr + (int64_t)b * src.sb + (int64_t)h * src.sh + (int64_t)qi * src.ss + lg * 8;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qf[s] = qok ? as_bf16x8(*(const u32x4*)(qrow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      dof[s] = qok ? as_bf16x8(*(const u32x4*)(drow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int s = 0; s < NS; ++s)
+      op[s] = qok ? as_bf16x8(*(const u32x4*)(row + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   // Statistics rows exist up to Sq_pad >= Sq; rows past Sq hold LSE = +inf, delta = 0.
   const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
-  const float lse2 = qi < p.Sq_pad ? stb[qi] : pos_inf();
-  const float dlt = qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f;
+  const float stat = SW ? (qi < p.Sq_pad ? stb[qi] : pos_inf()) : (qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f);
   const float sl2 = p.scale_log2;
   RowFrag<D> rf;
-  TrFrag<D> tf;
   rf.init(lane);
-  tf.init(lane);
+  TrFrag<D> tf;
+  if constexpr (!SW) tf.init(lane);
+  // Complete these loads here: left to the compiler, the wait for them sits at
+  // their first use inside the loop, where it would also drain every tile
+  // prefetch in flight on each pass.
+  wait_vm<0>();
 
-  f32x16 acc[NDB];
+  f32x16 acc[SW ? 1 : NDB];  // dQ^T (dP wavefront)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  for (int db = 0; db < (SW ? 1 : NDB); ++db) acc[db] = f32x16{};
+  f32x16 dp_prev = f32x16{};
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    wait_loads();
-    __syncthreads();
-    if (t + 1 < n_tiles) {
-      issue_swtile<D, 4>(k1s, kb, p.k.ss, (t + 1) * QBN, p.Sk, wave, lane);
-      issue_swtile<D, 4>(v1s, vb, p.v.ss, (t + 1) * QBN, p.Sk, wave, lane);
+  auto issue = [&](int tile) {
+    const int slot = tile % 3;
+    issue_swtile<D, 8, true>(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, wave, lane);
+    issue_swtile<D, 8, true>(v_s + slot * SZ, vb, p.v.ss, tile * QBN, p.Sk, wave, lane);
+  };
+
+  if (n > 0) {
+    issue(0);
+    if (n > 1) issue(1);
+    if (n > 1) wait_vm<L>();
+    else wait_vm<0>();
+    lds_barrier();
+  }
+  const int steps = n > 0 ? 2 * n + 1 : 0;
+  for (int k = 0; k < steps; ++k) {
+    const int T = k >> 1, hf = k & 1;
+    // Tile T + 2 takes the slot of tile T - 1, whose last reader (the dP
+    // wavefront, one step behind) finished before the previous barrier.
+    if (hf == 1 && T + 2 < n) issue(T + 2);
+    f32x16 sc = f32x16{};
+    if (k < 2 * n) {
+      const u16* rows = (SW ? k_s : v_s) + (T % 3) * SZ;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) sc = mfma32(rf.get(rows, hf, s), op[s], sc);
+      if constexpr (SW) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -stat));
+        if (32 * k + 32 > full_end) {
+          // Key of register i: 32k + 8(i/4) + 4lg + i%4; hidden when it exceeds
+          // lim64.  The sign of the difference gives a bit mask.
+          const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - 32 * k, 32)) - 4 * lg;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const unsigned keep = ~(unsigned)((rel - (8 * (i >> 2) + (i & 3))) >> 31);
+            sc[i] = __uint_as_float(__float_as_uint(sc[i]) & keep);
+          }
+        }
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) pex[pair][k & 1][hs][lane] = __builtin_bit_cast(u32x4, slab8(sc, hs * 8));
+      }
     }
-    dq_step<D>(k0s, v0s, qf, dof, acc, lse2, dlt, t * QBN, t * QBN + QBN > full_end, lim64, sl2, rf, tf, lane);
-    if (t + 1 >= n_tiles) break;
-    wait_loads();
-    __syncthreads();
-    if (t + 2 < n_tiles) {
-      issue_swtile<D, 4>(k0s, kb, p.k.ss, (t + 2) * QBN, p.Sk, wave, lane);
-      issue_swtile<D, 4>(v0s, vb, p.v.ss, (t + 2) * QBN, p.Sk, wave, lane);
+    if constexpr (!SW) {
+      if (k >= 1) {
+        const int kp = k - 1;
+        const u16* kt = k_s + ((kp >> 1) % 3) * SZ;
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][kp & 1][hs][lane]);
+          float ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[hs * 8 + e] - stat);
+          const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, (kp & 1) * 2 + hs, db), sb, acc[db]);
+        }
+      }
+      dp_prev = sc;
     }
-    dq_step<D>(k1s, v1s, qf, dof, acc, lse2, dlt, (t + 1) * QBN, (t + 1) * QBN + QBN > full_end, lim64, sl2, rf, tf, lane);
+    // The next tile must be resident before the barrier that ends its
+    // predecessor's second step.
+    if (hf == 1 && k < 2 * n) {
+      if (T + 2 < n) wait_vm<L>();
+      else wait_vm<0>();
+    }
+    lds_barrier();
   }
 
-  if (!qok) return;
-  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
-  u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
-                           : nullptr;
+  if constexpr (!SW) {
+    if (!qok) return;
+    float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
+    u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
+                             : nullptr;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + j * 8 + lg * 4;
-      f32x4 v = {acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale, acc[db][4 * j + 2] * p.scale,
-                 acc[db][4 * j + 3] * p.scale};
-      if (!p.dq_overwrite) v += *(const f32x4*)(accp + d);
-      *(f32x4*)(accp + d) = v;
-      if (dqp) *(u32x2*)(dqp + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + j * 8 + lg * 4;
+        f32x4 v = {acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale, acc[db][4 * j + 2] * p.scale,
+                   acc[db][4 * j + 3] * p.scale};
+        if (!p.dq_overwrite) v += *(const f32x4*)(accp + d);
+        *(f32x4*)(accp + d) = v;
+        if (dqp) *(u32x2*)(dqp + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
     }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) u16 k_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][2][64];  // [pair][step parity][slab][lane]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = lin % p.n_qtiles;
+  const int bh = lin / p.n_qtiles;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  // Causal: late query tiles see the most keys; start with them.
+  const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
+  if (wave < 4) dq_role<D, true>(p, k_s, v_s, pex_s, wave, lane, b, h, qt * QBM);
+  else dq_role<D, false>(p, k_s, v_s, pex_s, wave, lane, b, h, qt * QBM);
 }
 
 }  // namespace
@@ -465,9 +518,9 @@ hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s
   const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (run_dq && gq > 0) {
     if (D == 128)
-      hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((unsigned)gq), dim3(NT), 0, s, p);
+      hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
     else
-      hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((unsigned)gq), dim3(NT), 0, s, p);
+      hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
