@@ -65,164 +65,29 @@ __device__ __forceinline__ bf16x8 slab8(const f32x16& a, int o) {
 // ---------------------------------------------------------------- dK / dV --
 //
 // Eight wavefronts in four pairs; pair w%4 owns keys j0 + 32*(w%4) .. +31.
-// The "P" wavefront (w < 4) holds K as its register operand and accumulates
-// dV: it forms S = Q K^T, P = exp(S - LSE) (masked), hands P to its partner
-// through LDS and then runs dV^T += dO^T P.  The "dS" wavefront (w >= 4) holds
-// V and accumulates dK: it forms dP = dO V^T, reads P, dS = P (dP - delta) and
-// runs dK^T += Q^T dS.  Both halves carry 32 MFMAs per query tile, and each
-// wavefront keeps one operand and one accumulator instead of two of each, so
-// two wavefronts fit per SIMD.
+// Query tiles of 64 rows (Q, dO and their statistics) stream through a
+// 3-stage LDS ring, one tile per step.  At step t:
+//   * the "P" wavefront (w < 4) holds K in registers and accumulates dV: it
+//     forms S = Q K^T for tile t (one key per lane), P = exp(S - LSE) with the
+//     mask, hands P to its partner through LDS and runs dV^T += dO^T P;
+//   * the "dS" wavefront (w >= 4) holds V and accumulates dK: it forms
+//     dP = dO V^T for tile t, and for tile t - 1 (one step behind, so that P
+//     is already published) reads P, forms dS = P (dP - delta) and runs
+//     dK^T += Q^T dS.
+// Both carry 32 contractions per tile; the exponentials of one overlap the
+// contractions of the other on their shared SIMD.  One LDS-only barrier per
+// step publishes P and the next tile.
 
 constexpr int DKV_NT = 512;
-constexpr int DKV_STAGES = 3;  // query tiles in flight: the one in use and two being fetched
-
-// One pipeline stage: a query tile, a dO tile and their 64 rows of statistics.
-// Each stage is its own LDS object and every access names its stage at compile
-// time, so the compiler can see that reading one stage never overlaps the
-// global_load_lds writes still filling another.
-template <int D>
-struct DkvStage {
-  u16* q;
-  u16* dO;
-  float* st;  // [0, 64): LSE in log2 units, [64, 128): delta, [128, 256): unused
-};
-
-template <int D>
-struct DkvCtx {
-  const BwdParams& p;
-  DkvStage<D> s0, s1, s2;
-  u32x4 (*pex)[4][64];  // [4 pairs] P in bf16, in accumulator (lane) order
-  RowFrag<D> rf;
-  TrFrag<D> tf;
-  int wave, lane, lr, lg, pair;
-};
-
-template <int D, int ST>
-__device__ __forceinline__ const DkvStage<D>& stage(const DkvCtx<D>& c) {
-  if constexpr (ST == 0) return c.s0;
-  else if constexpr (ST == 1) return c.s1;
-  else return c.s2;
-}
-
-// Fetch query tile tq of one head into stage ST: Q and dO rows, and (wave 0)
-// the 64 statistics of each kind in one 1 KB run.  The loads are untracked by
-// the compiler; dkdv_step waits for them before the barrier that publishes
-// the stage, and the last step of every head waits for all of them.
-template <int D, int ST>
-__device__ __forceinline__ void dkdv_issue(const DkvCtx<D>& c, const u16* qb, const u16* dob, const float* stb,
-                                           int tq) {
-  const DkvStage<D>& s = stage<D, ST>(c);
-  if (c.wave == 0) {
-    const int part = (c.lane >> 4) & 1;  // lanes 0-15 LSE, 16-31 delta; 32-63 repeat them
-    const float* src = stb + part * c.p.Sq_pad + tq * KBM + 4 * (c.lane & 15);
-    dma16_untracked(src, (lds_void*)s.st);
-  }
-  issue_swtile<D, 8, true>(s.q, qb, c.p.q.ss, tq * KBM, c.p.Sq, c.wave, c.lane);
-  issue_swtile<D, 8, true>(s.dO, dob, c.p.dout.ss, tq * KBM, c.p.Sq, c.wave, c.lane);
-}
-
-// One query tile of the dK/dV kernel from stage ST, for the P wavefront (PW)
-// or the dS wavefront.  The role is a compile-time constant so that every LDS
-// read names its tile directly: the compiler can then tell these reads apart
-// from the global_load_lds writes still filling the other stages and does not
-// wait for those.
-template <int D, int ST, bool PW>
-__device__ __forceinline__ void dkdv_compute(const DkvCtx<D>& c, const bf16x8* kv, f32x16* acc, int i0, bool need_mask,
-                                             int64_t key_lim, float sl2) {
-  constexpr int NS = D / 16, NDB = D / 32;
-  const DkvStage<D>& s = stage<D, ST>(c);
-  const int lg = c.lg, lane = c.lane;
-  // S = Q K^T (P wavefront) or dP = dO V^T (dS wavefront): lane = key,
-  // registers = two 32-query blocks.
-  const u16* rows = PW ? s.q : s.dO;
-  f32x16 sc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-  for (int si = 0; si < NS; ++si) {
-#pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(c.rf.get(rows, qb2, si), kv[si], sc[qb2]);
-  }
-  bf16x8 opnd[4];  // B operands of the second contraction, one per 16-query slab
-  if constexpr (PW) {
-#pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 l4 = *(const f32x4*)(s.st + qb2 * 32 + g4 * 8 + lg * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[qb2][g4 * 4 + e] = exp2_fast(fmaf(sc[qb2][g4 * 4 + e], sl2, -l4[e]));
-      }
-    }
-    if (need_mask) {
-      // Causal mask: query i0 + q is hidden from this lane's key when
-      // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a bit
-      // mask, which keeps the 32 decisions in vector registers.
-      const int rel = (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM));
-#pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qo = qb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          const unsigned keep = ~(unsigned)((qo - rel) >> 31);
-          sc[qb2][i] = __uint_as_float(__float_as_uint(sc[qb2][i]) & keep);
-        }
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      opnd[ks] = slab8(sc[ks >> 1], (ks & 1) * 8);
-      c.pex[c.pair][ks][lane] = __builtin_bit_cast(u32x4, opnd[ks]);
-    }
-  }
-  lds_barrier();
-  if constexpr (!PW) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, c.pex[c.pair][ks][lane]);
-      const int qb2 = ks >> 1, o = (ks & 1) * 8;
-      // Slab ks holds queries 16*ks + 8*(e/4) + 4*lg + e%4: two groups of 4 consecutive deltas.
-      const f32x4 d0 = *(const f32x4*)(s.st + KBM + ks * 16 + lg * 4);
-      const f32x4 d1 = *(const f32x4*)(s.st + KBM + ks * 16 + 8 + lg * 4);
-      float ds[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (sc[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
-      opnd[ks] = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-    }
-  }
-  // dV^T += dO^T P (P wavefront) or dK^T += Q^T dS (dS wavefront).
-  const u16* tsrc = PW ? s.dO : s.q;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = mfma32(c.tf.get(tsrc, ks, db), opnd[ks], acc[db]);
-  }
-}
-
-// Vector-memory operations one query tile adds per wavefront (wave 0 issues one more).
-template <int D>
-constexpr int dkdv_loads_per_tile() {
-  return 2 * ((SwTile<D>::RUNS + 7) / 8);
-}
-
-// Pipeline step for tile t in stage ST: wait for it, release the stage that
-// tile t + 2 will use, fetch tile t + 2, compute tile t.  Every wavefront of
-// either role passes the same two barriers per step.
-template <int D, int ST, bool PW>
-__device__ __forceinline__ void dkdv_step(const DkvCtx<D>& c, const bf16x8* kv, f32x16* acc, const u16* qb,
-                                          const u16* dob, const float* stb, int t, int n_qt, int i_full,
-                                          int64_t key_lim, float sl2) {
-  if (t + 1 < n_qt) wait_vm<dkdv_loads_per_tile<D>()>();  // only tile t + 1 may remain in flight
-  else wait_vm<0>();
-  lds_barrier();
-  if (t + 2 < n_qt) dkdv_issue<D, (ST + 2) % 3>(c, qb, dob, stb, t + 2);
-  dkdv_compute<D, ST, PW>(c, kv, acc, t * KBM, c.p.causal && t * KBM < i_full, key_lim, sl2);
-}
 
 template <int D, bool PW>
-__device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int hk) {
-  constexpr int NS = D / 16, NDB = D / 32;
-  const BwdParams& p = c.p;
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s, float (*st_s)[256],
+                                          u32x4 (*pex)[2][4][64], const RowFrag<D>& rf, const TrFrag<D>& tf,
+                                          int wave, int lane, int kt, int b, int hk) {
+  constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
+  const int lg = lane >> 5, pair = wave & 3;
   const int j0 = kt * KBN;
-  const int kj = j0 + c.pair * 32 + c.lr;  // this lane's key
+  const int kj = j0 + pair * 32 + (lane & 31);  // this lane's key
   const bool kok = kj < p.Sk;
 
   // Register operand: K rows for the P wavefront, V rows for the dS wavefront.
@@ -232,7 +97,7 @@ __device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int
     const u16* base = (const u16*)src.ptr + (int64_t)b * src.sb + (int64_t)hk * src.sh + (int64_t)kj * src.ss;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      kv[s] = kok ? as_bf16x8(*(const u32x4*)(base + c.lg * 8 + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      kv[s] = kok ? as_bf16x8(*(const u32x4*)(base + lg * 8 + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   // Complete these loads here: left to the compiler, the wait for them sits at
   // their first use inside the loop, where it would also drain every tile
@@ -261,16 +126,105 @@ __device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int
     const u16* qb = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const u16* dob = (const u16*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
     const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
-    if (t_start < n_qt) dkdv_issue<D, 0>(c, qb, dob, stb, t_start);
-    if (t_start + 1 < n_qt) dkdv_issue<D, 1>(c, qb, dob, stb, t_start + 1);
-    for (int t = t_start; t < n_qt; t += 3) {
-      dkdv_step<D, 0, PW>(c, kv, acc, qb, dob, stb, t, n_qt, i_full, key_lim, sl2);
-      if (t + 1 >= n_qt) break;
-      dkdv_step<D, 1, PW>(c, kv, acc, qb, dob, stb, t + 1, n_qt, i_full, key_lim, sl2);
-      if (t + 2 >= n_qt) break;
-      dkdv_step<D, 2, PW>(c, kv, acc, qb, dob, stb, t + 2, n_qt, i_full, key_lim, sl2);
+    // Fetch query tile tq into slot tq % 3: Q and dO rows, and (wave 0) the 64
+    // statistics of each kind in one 1 KB run.  The loads are untracked by the
+    // compiler and waited for before the barrier that publishes the slot.
+    auto issue = [&](int tq) {
+      const int slot = tq % 3;
+      if (wave == 0) {
+        const int part = (lane >> 4) & 1;  // lanes 0-15 LSE, 16-31 delta; 32-63 repeat them
+        dma16_untracked(stb + part * p.Sq_pad + tq * KBM + 4 * (lane & 15), (lds_void*)st_s[slot]);
+      }
+      issue_swtile<D, 8, true>(q_s + slot * SZ, qb, p.q.ss, tq * KBM, p.Sq, wave, lane);
+      issue_swtile<D, 8, true>(d_s + slot * SZ, dob, p.dout.ss, tq * KBM, p.Sq, wave, lane);
+    };
+    if (t_start >= n_qt) continue;
+    issue(t_start);
+    wait_vm<0>();
+    lds_barrier();
+    f32x16 dp_prev[2] = {f32x16{}, f32x16{}};
+    for (int t = t_start; t <= n_qt; ++t) {
+      // Tile t + 1 takes the slot of tile t - 2, last read (by the dS
+      // wavefront) before the previous barrier.
+      if (t + 1 < n_qt) issue(t + 1);
+      const int slot = t % 3;
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
+      if (t < n_qt) {
+        // S = Q K^T (P wavefront) or dP = dO V^T (dS wavefront): lane = key,
+        // registers = two 32-query blocks.
+        const u16* rows = (PW ? q_s : d_s) + slot * SZ;
+#pragma unroll
+        for (int si = 0; si < NS; ++si) {
+#pragma unroll
+          for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(rf.get(rows, qb2, si), kv[si], sc[qb2]);
+        }
+        if constexpr (PW) {
+          const float* st = st_s[slot];
+#pragma unroll
+          for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x4 l4 = *(const f32x4*)(st + qb2 * 32 + g4 * 8 + lg * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sc[qb2][g4 * 4 + e] = exp2_fast(fmaf(sc[qb2][g4 * 4 + e], sl2, -l4[e]));
+            }
+          }
+          const int i0 = t * KBM;
+          if (p.causal && i0 < i_full) {
+            // Causal mask: query i0 + q is hidden from this lane's key when
+            // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a
+            // bit mask, which keeps the 32 decisions in vector registers.
+            const int rel = (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM));
+#pragma unroll
+            for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int qo = qb2 * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
+                const unsigned keep = ~(unsigned)((qo - rel) >> 31);
+                sc[qb2][i] = __uint_as_float(__float_as_uint(sc[qb2][i]) & keep);
+              }
+            }
+          }
+          // P in bf16, one B operand per 16-query slab: published for the
+          // partner and used right away for dV^T += dO^T P.
+          const u16* dsrc = d_s + slot * SZ;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 pb = slab8(sc[ks >> 1], (ks & 1) * 8);
+            pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(dsrc, ks, db), pb, acc[db]);
+          }
+        }
+      }
+      if constexpr (!PW) {
+        if (t > t_start) {
+          // dS for tile t - 1 from the published P and last step's dP, then
+          // dK^T += Q^T dS.
+          const int tp = t - 1, sp = tp % 3;
+          const float* st = st_s[sp];
+          const u16* qsrc = q_s + sp * SZ;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
+            const int qb2 = ks >> 1, o = (ks & 1) * 8;
+            // Slab ks holds queries 16*ks + 8*(e/4) + 4*lg + e%4: two groups of 4 consecutive deltas.
+            const f32x4 d0 = *(const f32x4*)(st + KBM + ks * 16 + lg * 4);
+            const f32x4 d1 = *(const f32x4*)(st + KBM + ks * 16 + 8 + lg * 4);
+            float ds[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
+            const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(qsrc, ks, db), sb, acc[db]);
+          }
+        }
+        dp_prev[0] = sc[0];
+        dp_prev[1] = sc[1];
+      }
+      wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
+      lds_barrier();
     }
-    lds_barrier();  // stages are reused by the next head / tile
   }
 
   if (!kok) return;
@@ -281,7 +235,7 @@ __device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + j * 8 + c.lg * 4;
+      const int d = db * 32 + j * 8 + lg * 4;
       const f32x16& A = acc[db];
       *(u32x2*)(out + d) = u32x2{pack_bf16x2(A[4 * j] * f, A[4 * j + 1] * f), pack_bf16x2(A[4 * j + 2] * f, A[4 * j + 3] * f)};
     }
@@ -292,37 +246,33 @@ __device__ __forceinline__ void dkdv_tile(const DkvCtx<D>& c, int kt, int b, int
 // tiles (u, n - 1 - u), whose causal work adds up to about the same for every u.
 // Early keys are seen by the most queries, so they come first.
 template <int D, bool PW>
-__device__ __forceinline__ void dkdv_unit(const DkvCtx<D>& c, int unit, int b, int hk) {
-  const BwdParams& p = c.p;
+__device__ __forceinline__ void dkdv_unit(const BwdParams& p, u16* q_s, u16* d_s, float (*st_s)[256],
+                                          u32x4 (*pex)[2][4][64], int wave, int lane, int unit, int b, int hk) {
+  RowFrag<D> rf;
+  TrFrag<D> tf;
+  rf.init(lane);
+  tf.init(lane);
   const int last = p.n_ktiles - 1 - unit;
   const int n = (p.balanced && last != unit) ? 2 : 1;
-  for (int k = 0; k < n; ++k) dkdv_tile<D, PW>(c, k == 0 ? unit : last, b, hk);
+  for (int k = 0; k < n; ++k) dkdv_tile<D, PW>(p, q_s, d_s, st_s, pex, rf, tf, wave, lane, k == 0 ? unit : last, b, hk);
 }
 
 template <int D>
 __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) u16 q0[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 q1[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 q2[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 d0[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 d1[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 d2[SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) float st0[256];
-  __shared__ __attribute__((aligned(16))) float st1[256];
-  __shared__ __attribute__((aligned(16))) float st2[256];
-  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][4][64];
+  __shared__ __attribute__((aligned(16))) u16 q_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
+  // [slot] [0, 64): LSE in log2 units, [64, 128): delta, [128, 256): unused
+  __shared__ __attribute__((aligned(16))) float st_s[3][256];
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];  // [pair][step parity][slab][lane]
   // The wavefront index is uniform across the wavefront; say so, so that the
   // role branch below is a scalar branch.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  DkvCtx<D> c{p, {q0, d0, st0}, {q1, d1, st1}, {q2, d2, st2}, pex_s, {}, {}, wave, lane, lane & 31, lane >> 5, wave & 3};
-  c.rf.init(lane);
-  c.tf.init(lane);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_units_k;
   const int bh = lin / p.n_units_k;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  if (wave < 4) dkdv_unit<D, true>(c, unit, b, hk);
-  else dkdv_unit<D, false>(c, unit, b, hk);
+  if (wave < 4) dkdv_unit<D, true>(p, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
+  else dkdv_unit<D, false>(p, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
 }
 
 // --------------------------------------------------------------------- dQ --
