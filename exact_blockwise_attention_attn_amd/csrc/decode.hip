@@ -5,19 +5,25 @@
 //
 // Split kernel: one workgroup per (batch, key/value head, group slice of up to
 // 4 query heads, split).  The cache is read exactly once per key/value head, so
-// the 4 query heads of a GQA group share every byte.  Per 64-key block a
-// wavefront
-//   * loads K with one key per lane (16 keys x 4 lane groups of features) and
-//     forms the scores with the 16x16x32 bf16 MFMA, the 4 queries replicated
-//     over the 16 rows so every lane receives all 4 scores of its key;
-//   * applies the online softmax per 64-key block (max over 16 lanes);
-//   * passes P through a small per-wavefront LDS buffer to the layout in which
-//     V is loaded (16 lanes cover one 256-byte key row, fully coalesced) and
-//     accumulates O on the vector ALUs.
+// the 4 query heads of a GQA group share every byte.  The split's keys come in
+// tiles of 16; wavefront w takes tiles w, w + 4, w + 8, ... and runs on its own
+// (no barrier until the final merge), loading K and V straight into registers
+// with four tiles in flight, so that a CU keeps about 256 KB of loads
+// outstanding, enough to cover HBM latency under full load.  Per tile:
+//   * scores with the 16x16x32 bf16 MFMA, the 4 queries replicated over the 16
+//     rows so every lane receives the 4 scores of its key (lane group g holds
+//     features 8 (4 kk + g) .. +7 of k-step kk, loaded as 64-byte row pieces);
+//   * online softmax per tile (max over the 16 key lanes);
+//   * P goes through a small per-wavefront LDS buffer to the layout in which V
+//     was loaded (16 lanes cover one key row) and O accumulates on the vector
+//     ALUs.
 // The four wavefronts' partials are merged in LDS and written to the workspace.
 //
-// Tree kernel: one workgroup per (batch, query head), one thread per feature;
-// a binary-carry stack realises the adjacent-pair tree over the splits.
+// Tree kernel: one workgroup per (batch, query head); a binary-carry stack
+// realises the adjacent-pair tree over the splits, whose power-of-two chunks
+// are reduced in parallel (see decode_tree_kernel).
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -25,26 +31,28 @@ namespace attn {
 namespace {
 
 constexpr int NT = 256;
-constexpr int NW = 4;    // wavefronts
-constexpr int KB = 64;   // keys per wavefront block
-constexpr int QPW = 4;   // query heads per workgroup
+constexpr int NW = 4;      // wavefronts
+constexpr int KW = 16;     // keys per tile
+constexpr int DEPTH = 4;   // tiles in flight per wavefront
+constexpr int QPW = 4;     // query heads per workgroup
 constexpr int kMaxLevels = 11;
 
 template <int D>
-struct DecodeSmem {
-  f32x4 p[NW][KB];         // P exchange, 4 queries per key
-  float m[NW][QPW], l[NW][QPW];
-  float o[NW][QPW][D];
+struct KvTile {
+  using VT = typename std::conditional<D == 128, u32x4, u32x2>::type;
+  u32x4 k[D / 32];  // K: this lane's key, features 8 (4 kk + g) ..
+  VT v[4];          // V: keys 4 j + g, features (D / 16) l16 ..
 };
 
 template <int D>
-__global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams prm, int n_qblk) {
-  constexpr int FPL = D / 4;   // K features per lane group
-  constexpr int NKK = FPL / 8; // MFMA k-steps over the features
+__global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, int n_qblk) {
+  constexpr int NKK = D / 32;  // MFMA k-steps over the features
   constexpr int FPV = D / 16;  // V features per lane
-  __shared__ DecodeSmem<D> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(16))) f32x4 pex[NW][KW];  // P of 4 queries per key
+  __shared__ float m_s[NW][QPW], l_s[NW][QPW];
+  __shared__ __attribute__((aligned(16))) float o_s[NW][QPW][D];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int lin = blockIdx.x;
   const int sp = lin % prm.n_splits;
@@ -59,23 +67,37 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams prm, int 
   int64_t Lb = prm.L;
   if (prm.seqlens) Lb = min<int64_t>(max<int64_t>(prm.seqlens[b], 0), prm.L);
   const int64_t k_begin = (int64_t)sp * prm.split_len;
-  const int64_t k_end = min<int64_t>(k_begin + prm.split_len, Lb);
-  const int64_t n_keys = max<int64_t>(0, k_end - k_begin);
-  const int n_blocks = (int)((n_keys + KB - 1) / KB);
-  const int n_iter = (n_blocks + NW - 1) / NW;
+  const int n_keys = (int)max<int64_t>(0, min<int64_t>(k_begin + prm.split_len, Lb) - k_begin);
+  const int n_tiles = (n_keys + KW - 1) / KW;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
-  // A operand: row r of the 16x32 tile is query r % 4 (zero when outside the group slice).
+  // A operand: row r of the 16x32 tile is query r % 4 (zero outside the group slice).
   bf16x8 qa[NKK];
   {
     const int qq = l16 & 3;
     const bool ok = qq < nq;
-    const u16* qp = prm.q + (int64_t)b * prm.q_sb + (int64_t)(h0 + qq) * prm.q_sh + g * FPL;
+    const u16* qp = prm.q + (int64_t)b * prm.q_sb + (int64_t)(h0 + qq) * prm.q_sh;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      qa[kk] = ok ? as_bf16x8(*(const u32x4*)(qp + kk * 8)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      qa[kk] = ok ? as_bf16x8(*(const u32x4*)(qp + (4 * kk + g) * 8)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
-  const u16* kbase = prm.k + (int64_t)b * prm.k_sb + (int64_t)hk * prm.k_sh;
-  const u16* vbase = prm.v + (int64_t)b * prm.v_sb + (int64_t)hk * prm.v_sh;
+  const u16* kbase = prm.k + (int64_t)b * prm.k_sb + (int64_t)hk * prm.k_sh + k_begin * prm.k_sl;
+  const u16* vbase = prm.v + (int64_t)b * prm.v_sb + (int64_t)hk * prm.v_sh + k_begin * prm.v_sl;
+
+  // Load this wavefront's i-th tile.  Indices past its last tile load the last
+  // tile again (cache hits, never used), so every pass issues the same loads.
+  auto load = [&](int i, KvTile<D>& t) {
+    const int key0 = (wave + NW * min(i, max(my_tiles - 1, 0))) * KW;
+    const int kkey = min(key0 + l16, n_keys - 1);
+    const u16* kp = kbase + (int64_t)kkey * prm.k_sl;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) t.k[kk] = *(const u32x4*)(kp + (4 * kk + g) * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int vkey = min(key0 + 4 * j + g, n_keys - 1);
+      t.v[j] = *(const typename KvTile<D>::VT*)(vbase + (int64_t)vkey * prm.v_sl + FPV * l16);
+    }
+  };
 
   float m[QPW], lsum[QPW], acc[QPW][FPV];
 #pragma unroll
@@ -86,124 +108,108 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeParams prm, int 
     for (int e = 0; e < FPV; ++e) acc[i][e] = 0.f;
   }
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int64_t kb0 = k_begin + (int64_t)(it * NW + wave) * KB;
-    // Scores for 4 sub-blocks of 16 keys.
-    f32x4 sv[4];
+  auto compute = [&](int i, const KvTile<D>& t) {
+    const int key0 = (wave + NW * i) * KW;
+    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t key = kb0 + nb * 16 + l16;
-      const bool ok = key < k_end;
-      const u16* kp = kbase + key * prm.k_sl + g * FPL;
-      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < NKK; ++kk) c = mfma16(qa[kk], as_bf16x8(t.k[kk]), c);
+    if (key0 + l16 >= n_keys) c = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+    // Online softmax per query over the 16 keys.
+    float pv[QPW];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 kr = ok ? *(const u32x4*)(kp + kk * 8) : u32x4{0u, 0u, 0u, 0u};
-        c = mfma16(qa[kk], as_bf16x8(kr), c);
-      }
-      if (!ok) c = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-      sv[nb] = c;
-    }
-    // V for this lane: keys kb0 + 4*jj + g, features l16*FPV ..
-    u32x4 vr[16];
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int64_t key = kb0 + 4 * jj + g;
-      const bool ok = key < k_end;
-      const u16* vp = vbase + key * prm.v_sl + l16 * FPV;
-      if (FPV == 8) {
-        vr[jj] = ok ? *(const u32x4*)vp : u32x4{0u, 0u, 0u, 0u};
-      } else {
-        const u32x2 t = ok ? *(const u32x2*)vp : u32x2{0u, 0u};
-        vr[jj] = u32x4{t[0], t[1], 0u, 0u};
-      }
-    }
-    // Online softmax per query over the block (max across the 16 key lanes).
-    float pv[4][QPW];
-#pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      float mt = fmaxf(fmaxf(sv[0][i], sv[1][i]), fmaxf(sv[2][i], sv[3][i]));
+    for (int q = 0; q < QPW; ++q) {
+      float mt = c[q];
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
-      const float m_new = fmaxf(m[i], mt);
+      const float m_new = fmaxf(m[q], mt);
       const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = exp2_fast((m[i] - m_use) * prm.scale_log2);
-      const float nbias = -m_use * prm.scale_log2;
-      float rs = 0.f;
+      const float alpha = exp2_fast((m[q] - m_use) * prm.scale_log2);
+      pv[q] = exp2_fast(fmaf(c[q], prm.scale_log2, -m_use * prm.scale_log2));
+      lsum[q] = lsum[q] * alpha + pv[q];
+      m[q] = m_new;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        pv[nb][i] = exp2_fast(fmaf(sv[nb][i], prm.scale_log2, nbias));
-        rs += pv[nb][i];
-      }
-      lsum[i] = lsum[i] * alpha + rs;
-      m[i] = m_new;
-#pragma unroll
-      for (int e = 0; e < FPV; ++e) acc[i][e] *= alpha;
+      for (int e = 0; e < FPV; ++e) acc[q][e] *= alpha;
     }
-    if (g == 0) {
+    // Hand P to the V layout within the wavefront (LDS operations of one
+    // wavefront complete in order; the wait makes the stores visible).
+    if (g == 0) pex[wave][l16] = f32x4{pv[0], pv[1], pv[2], pv[3]};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) sm.p[wave][nb * 16 + l16] = f32x4{pv[nb][0], pv[nb][1], pv[nb][2], pv[nb][3]};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const f32x4 p4 = sm.p[wave][4 * jj + g];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 p4 = pex[wave][4 * j + g];
       float vf[FPV];
 #pragma unroll
-      for (int w = 0; w < FPV / 2; ++w) {
-        vf[2 * w] = bf16_lo(vr[jj][w]);
-        vf[2 * w + 1] = bf16_hi(vr[jj][w]);
+      for (int x = 0; x < FPV / 2; ++x) {
+        vf[2 * x] = bf16_lo(t.v[j][x]);
+        vf[2 * x + 1] = bf16_hi(t.v[j][x]);
       }
 #pragma unroll
-      for (int i = 0; i < QPW; ++i)
+      for (int q = 0; q < QPW; ++q)
 #pragma unroll
-        for (int e = 0; e < FPV; ++e) acc[i][e] = fmaf(p4[i], vf[e], acc[i][e]);
+        for (int e = 0; e < FPV; ++e) acc[q][e] = fmaf(p4[q], vf[e], acc[q][e]);
     }
-    __syncthreads();
+    // The next tile's P store must not overtake these reads (in-order LDS).
+    asm volatile("" ::: "memory");
+  };
+
+  if (my_tiles > 0) {
+    KvTile<D> buf[DEPTH];
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r) load(r, buf[r]);
+    for (int i = 0; i < my_tiles; i += DEPTH) {
+#pragma unroll
+      for (int r = 0; r < DEPTH; ++r) {
+        if (i + r < my_tiles) {
+          compute(i + r, buf[r]);
+          load(i + r + DEPTH, buf[r]);
+        }
+      }
+    }
   }
 
-  // Reduce within the wavefront: lsum over the 16 key lanes, acc over the 4 lane groups.
+  // Reduce within the wavefront: lsum over the 16 key lanes (every lane group
+  // holds the same values), acc over the 4 lane groups (disjoint keys).
 #pragma unroll
-  for (int i = 0; i < QPW; ++i) {
+  for (int q = 0; q < QPW; ++q) {
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) lsum[i] += __shfl_xor(lsum[i], off, 64);
+    for (int off = 1; off < 16; off <<= 1) lsum[q] += __shfl_xor(lsum[q], off, 64);
 #pragma unroll
     for (int e = 0; e < FPV; ++e) {
-      acc[i][e] += __shfl_xor(acc[i][e], 16, 64);
-      acc[i][e] += __shfl_xor(acc[i][e], 32, 64);
+      acc[q][e] += __shfl_xor(acc[q][e], 16, 64);
+      acc[q][e] += __shfl_xor(acc[q][e], 32, 64);
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      sm.m[wave][i] = m[i];
-      sm.l[wave][i] = lsum[i];
+    for (int q = 0; q < QPW; ++q) {
+      m_s[wave][q] = m[q];
+      l_s[wave][q] = lsum[q];
     }
   }
   if (g == 0) {
 #pragma unroll
-    for (int i = 0; i < QPW; ++i)
+    for (int q = 0; q < QPW; ++q)
 #pragma unroll
-      for (int e = 0; e < FPV; ++e) sm.o[wave][i][l16 * FPV + e] = acc[i][e];
+      for (int e = 0; e < FPV; ++e) o_s[wave][q][l16 * FPV + e] = acc[q][e];
   }
   __syncthreads();
 
   // Merge the four wavefronts and write this split's partial.
   for (int x = tid; x < nq * D; x += NT) {
-    const int i = x / D, d = x % D;
+    const int q = x / D, d = x % D;
     float M = neg_inf();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][i]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, m_s[w][q]);
     float tot = 0.f, o = 0.f;
     if (M != neg_inf()) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = exp2_fast((sm.m[w][i] - M) * prm.scale_log2);
-        tot = fmaf(f, sm.l[w][i], tot);
-        o = fmaf(f, sm.o[w][i][d], o);
+        const float f = exp2_fast((m_s[w][q] - M) * prm.scale_log2);
+        tot = fmaf(f, l_s[w][q], tot);
+        o = fmaf(f, o_s[w][q][d], o);
       }
     }
-    const int h = h0 + i;
+    const int h = h0 + q;
     const int64_t prow = ((int64_t)b * prm.Hq + h) * prm.n_splits + sp;
     prm.part_o[prow * D + d] = (tot > 0.f) ? o / tot : 0.f;
     if (d == 0) prm.part_lse[prow] = (M == neg_inf()) ? neg_inf() : fmaf(M, prm.scale, logf(tot));
@@ -220,16 +226,12 @@ __device__ __forceinline__ void merge_scalar(float& La, float& Oa, float Lb, flo
   La = L;
 }
 
-template <int D>
-__global__ __launch_bounds__(D) void decode_tree_kernel(DecodeParams prm) {
-  const int d = threadIdx.x;
-  const int h = blockIdx.x % prm.Hq, b = blockIdx.x / prm.Hq;
-  const int64_t base = ((int64_t)b * prm.Hq + h) * prm.n_splits;
+// Binary-carry stack for the adjacent-pair tree: push partials in order; a
+// push merges equal-size subtrees as soon as both exist.
+struct TreeStack {
   float sl[kMaxLevels], so[kMaxLevels];
   unsigned pending = 0;
-  for (int i = 0; i < prm.n_splits; ++i) {
-    float xl = prm.part_lse[base + i];
-    float xo = prm.part_o[(base + i) * D + d];
+  __device__ __forceinline__ void push(float xl, float xo) {
 #pragma unroll
     for (int k = 0; k < kMaxLevels; ++k) {
       if (pending & (1u << k)) {
@@ -241,27 +243,76 @@ __global__ __launch_bounds__(D) void decode_tree_kernel(DecodeParams prm) {
         sl[k] = xl;
         so[k] = xo;
         pending |= 1u << k;
-        break;
+        return;
       }
     }
   }
-  float L = neg_inf(), O = 0.f;
-  bool have = false;
+  // Combine what is left, smaller subtrees first: the tree's root.
+  __device__ __forceinline__ void root(float& L, float& O) const {
+    L = neg_inf();
+    O = 0.f;
+    bool have = false;
 #pragma unroll
-  for (int k = 0; k < kMaxLevels; ++k) {
-    if (pending & (1u << k)) {
-      if (!have) {
-        L = sl[k];
-        O = so[k];
-        have = true;
-      } else {
-        float l2 = sl[k], o2 = so[k];
-        merge_scalar(l2, o2, L, O);
-        L = l2;
-        O = o2;
+    for (int k = 0; k < kMaxLevels; ++k) {
+      if (pending & (1u << k)) {
+        if (!have) {
+          L = sl[k];
+          O = so[k];
+          have = true;
+        } else {
+          float l2 = sl[k], o2 = so[k];
+          merge_scalar(l2, o2, L, O);
+          L = l2;
+          O = o2;
+        }
       }
     }
   }
+};
+
+// One workgroup per (batch, query head) with TREE_NT threads: NC = TREE_NT / D
+// groups of D threads (one per feature).  Group c reduces splits
+// [c * cs, (c + 1) * cs) with cs a power of two, giving the root of that
+// subtree; group 0 then pushes the NC roots in order.  Because every chunk but
+// the last is a complete subtree, this is the same adjacent-pair tree as
+// pushing all splits one by one, with a much shorter dependency chain.
+constexpr int TREE_NT = 1024;
+
+template <int D>
+__global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) {
+  constexpr int NC = TREE_NT / D;
+  __shared__ float rl[NC], ro[NC][D];
+  const int d = threadIdx.x % D, c = threadIdx.x / D;
+  const int h = blockIdx.x % prm.Hq, b = blockIdx.x / prm.Hq;
+  const int64_t base = ((int64_t)b * prm.Hq + h) * prm.n_splits;
+  int cs = 1;
+  while (cs * NC < prm.n_splits) cs *= 2;
+  const int i_beg = min(c * cs, prm.n_splits), i_end = min(i_beg + cs, prm.n_splits);
+  TreeStack st;
+  // Fetch 16 partials at a time (independent loads whose latencies overlap).
+  constexpr int CH = 16;
+  for (int i0 = i_beg; i0 < i_end; i0 += CH) {
+    float cl[CH], co[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = min(i0 + j, i_end - 1);
+      cl[j] = prm.part_lse[base + i];
+      co[j] = prm.part_o[(base + i) * D + d];
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (i0 + j < i_end) st.push(cl[j], co[j]);
+  }
+  float L, O;
+  st.root(L, O);
+  if (d == 0) rl[c] = L;
+  ro[c][d] = O;
+  __syncthreads();
+  if (c != 0) return;
+  TreeStack top;
+  for (int k = 0; k < NC; ++k)
+    if (k * cs < prm.n_splits) top.push(rl[k], ro[k][d]);
+  top.root(L, O);
   prm.o[(int64_t)b * prm.o_sb + (int64_t)h * prm.o_sh + d] = f32_to_bf16(O);
   if (d == 0) prm.lse[(int64_t)b * prm.Hq + h] = L;
 }
@@ -280,9 +331,9 @@ hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s) {
   if (e != hipSuccess) return e;
   const dim3 tg((unsigned)((int64_t)p.B * p.Hq));
   if (D == 128)
-    hipLaunchKernelGGL(decode_tree_kernel<128>, tg, dim3(128), 0, s, p);
+    hipLaunchKernelGGL(decode_tree_kernel<128>, tg, dim3(TREE_NT), 0, s, p);
   else
-    hipLaunchKernelGGL(decode_tree_kernel<64>, tg, dim3(64), 0, s, p);
+    hipLaunchKernelGGL(decode_tree_kernel<64>, tg, dim3(TREE_NT), 0, s, p);
   return hipGetLastError();
 }
 
