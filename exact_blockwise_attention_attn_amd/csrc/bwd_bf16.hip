@@ -278,31 +278,25 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
 // --------------------------------------------------------------------- dQ --
 //
 // Eight wavefronts in four pairs; pair w%4 owns queries q0 + 32*(w%4) .. +31.
-// Key/value tiles of 64 rows stream through a 3-stage LDS ring and are
-// consumed in 32-key steps.  At step k:
-//   * the "S" wavefront (w < 4) holds Q in registers, forms S^T = K Q^T for the
-//     keys of step k (one query per lane), P = exp(S - LSE) with the mask, and
-//     hands P to its partner through LDS;
-//   * the "dP" wavefront (w >= 4) holds dO and the whole dQ^T accumulator,
-//     forms dP^T = V dO^T for step k, and for step k - 1 (one step behind, so
-//     that P is already published) reads P, forms dS = P (dP - delta) and runs
-//     dQ^T += K^T dS^T.
+// Key/value tiles of 64 rows stream through a 3-stage LDS ring, one tile per
+// step.  At step t:
+//   * the "S" wavefront (w < 4) holds Q in registers, forms S^T = K Q^T for
+//     tile t (one query per lane, two 32-key blocks), P = exp(S - LSE) with
+//     the mask, and hands P to its partner through LDS;
+//   * the "dP" wavefront (w >= 4) holds dO and the whole dQ^T accumulator. It
+//     first finishes tile t - 1 (one step behind, so that P is published):
+//     reads P, forms dS = P (dP - delta) and runs dQ^T += K^T dS^T; then it
+//     forms dP^T = V dO^T for tile t.
 // The S wavefront carries the exponentials, the dP wavefront two thirds of the
 // contractions; a pair shares one SIMD, whose matrix core they keep busy in
-// turn.  One LDS-only barrier per step publishes P and, every other step, the
-// next key/value tile.
+// turn.  One LDS-only barrier per step publishes P and the next tile.
 
 constexpr int DQ_NT = 512;
 
-template <int D>
-constexpr int dq_loads_per_tile() {
-  return 2 * (SwTile<D>::RUNS / 8);
-}
-
 template <int D, bool SW>
-__device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, u32x4 (*pex)[2][2][64], int wave,
+__device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, u32x4 (*pex)[2][4][64], int wave,
                                         int lane, int b, int h, int q0) {
-  constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE, L = dq_loads_per_tile<D>();
+  constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
   const int lr = lane & 31, lg = lane >> 5, pair = wave & 3;
   const int hk = h / p.group;
   const int qi = q0 + pair * 32 + lr;
@@ -344,8 +338,9 @@ __device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, 
   f32x16 acc[SW ? 1 : NDB];  // dQ^T (dP wavefront)
 #pragma unroll
   for (int db = 0; db < (SW ? 1 : NDB); ++db) acc[db] = f32x16{};
-  f32x16 dp_prev = f32x16{};
+  f32x16 dp_prev[2] = {f32x16{}, f32x16{}};
 
+  // Tile u into slot u % 3, K and V rows; untracked loads, waited for below.
   auto issue = [&](int tile) {
     const int slot = tile % 3;
     issue_swtile<D, 8, true>(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, wave, lane);
@@ -354,62 +349,68 @@ __device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, 
 
   if (n > 0) {
     issue(0);
-    if (n > 1) issue(1);
-    if (n > 1) wait_vm<L>();
-    else wait_vm<0>();
+    wait_vm<0>();
     lds_barrier();
   }
-  const int steps = n > 0 ? 2 * n + 1 : 0;
-  for (int k = 0; k < steps; ++k) {
-    const int T = k >> 1, hf = k & 1;
-    // Tile T + 2 takes the slot of tile T - 1, whose last reader (the dP
-    // wavefront, one step behind) finished before the previous barrier.
-    if (hf == 1 && T + 2 < n) issue(T + 2);
-    f32x16 sc = f32x16{};
-    if (k < 2 * n) {
-      const u16* rows = (SW ? k_s : v_s) + (T % 3) * SZ;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) sc = mfma32(rf.get(rows, hf, s), op[s], sc);
-      if constexpr (SW) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -stat));
-        if (32 * k + 32 > full_end) {
-          // Key of register i: 32k + 8(i/4) + 4lg + i%4; hidden when it exceeds
-          // lim64.  The sign of the difference gives a bit mask.
-          const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - 32 * k, 32)) - 4 * lg;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const unsigned keep = ~(unsigned)((rel - (8 * (i >> 2) + (i & 3))) >> 31);
-            sc[i] = __uint_as_float(__float_as_uint(sc[i]) & keep);
-          }
-        }
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) pex[pair][k & 1][hs][lane] = __builtin_bit_cast(u32x4, slab8(sc, hs * 8));
-      }
-    }
+  for (int t = 0; n > 0 && t <= n; ++t) {
+    // Tile t + 1 takes the slot of tile t - 2, last read (by the dP
+    // wavefront, one step behind) before the previous barrier.
+    if (t + 1 < n) issue(t + 1);
     if constexpr (!SW) {
-      if (k >= 1) {
-        const int kp = k - 1;
-        const u16* kt = k_s + ((kp >> 1) % 3) * SZ;
+      if (t > 0) {
+        // dS for tile t - 1 from the published P and last step's dP, then
+        // dQ^T += K^T dS^T over its four 16-key slabs.
+        const int tp = t - 1;
+        const u16* kt = k_s + (tp % 3) * SZ;
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][kp & 1][hs][lane]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
           float ds[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[hs * 8 + e] - stat);
+          for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[ks >> 1][(ks & 1) * 8 + e] - stat);
           const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, (kp & 1) * 2 + hs, db), sb, acc[db]);
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, ks, db), sb, acc[db]);
         }
       }
-      dp_prev = sc;
     }
-    // The next tile must be resident before the barrier that ends its
-    // predecessor's second step.
-    if (hf == 1 && k < 2 * n) {
-      if (T + 2 < n) wait_vm<L>();
-      else wait_vm<0>();
+    if (t < n) {
+      // S^T = K Q^T (S wavefront) or dP^T = V dO^T (dP wavefront): lane =
+      // query, registers = two 32-key blocks.
+      const u16* rows = (SW ? k_s : v_s) + (t % 3) * SZ;
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) sc[kb2] = mfma32(rf.get(rows, kb2, s), op[s], sc[kb2]);
+      }
+      if constexpr (SW) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[kb2][i] = exp2_fast(fmaf(sc[kb2][i], sl2, -stat));
+        if (QBN * t + QBN > full_end) {
+          // Key of register i of block kb2: 64t + 32kb2 + 8(i/4) + 4lg + i%4;
+          // hidden when it exceeds lim64.  The sign of the difference gives a
+          // bit mask.
+          const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - QBN * t, QBN)) - 4 * lg;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const unsigned keep = ~(unsigned)((rel - (32 * kb2 + 8 * (i >> 2) + (i & 3))) >> 31);
+              sc[kb2][i] = __uint_as_float(__float_as_uint(sc[kb2][i]) & keep);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, slab8(sc[ks >> 1], (ks & 1) * 8));
+      } else {
+        dp_prev[0] = sc[0];
+        dp_prev[1] = sc[1];
+      }
     }
+    wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
     lds_barrier();
   }
 
@@ -437,7 +438,7 @@ template <int D>
 __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) u16 k_s[3 * SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 v_s[3 * SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][2][64];  // [pair][step parity][slab][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];  // [pair][step parity][slab][lane]
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_qtiles;

@@ -232,9 +232,8 @@ DECODE_CASES = [
     (2, 4, 1, 64, 128, 64, [0, 64]),
     (1, 32, 8, 16384, 128, 64, None),
     (2, 6, 2, 300, 128, 1, [300, 150]),
-    # Enough work items that a workgroup streams several consecutive splits:
-    # ragged lengths (empty, one key, mid-split cut) and a split length of 65
-    # keys, so tiles straddle split ends.
+    # Ragged lengths (empty, one key, mid-split cut), a split length of 65 keys
+    # (a last tile of one key), and 64 splits over many (batch, head) items.
     (4, 8, 8, 4133, 128, 64, [0, 1, 2000, 4133]),
     (2, 16, 4, 8192, 64, 128, [8192, 777]),
 ]
