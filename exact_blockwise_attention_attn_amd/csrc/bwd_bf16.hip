@@ -142,8 +142,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
     issue(t_start);
     wait_vm<0>();
     lds_barrier();
-    f32x16 dp_prev[2] = {f32x16{}, f32x16{}};
-    for (int t = t_start; t <= n_qt; ++t) {
+    f32x16 dpa[2] = {f32x16{}, f32x16{}}, dpb[2] = {f32x16{}, f32x16{}};
+    auto step = [&](int t, f32x16* dp_in, f32x16* dp_out) {
       // Tile t + 1 takes the slot of tile t - 2, last read (by the dS
       // wavefront) before the previous barrier.
       if (t + 1 < n_qt) issue(t + 1);
@@ -157,6 +157,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
         for (int si = 0; si < NS; ++si) {
 #pragma unroll
           for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(rf.get(rows, qb2, si), kv[si], sc[qb2]);
+        }
+        if constexpr (!PW) {
+          dp_out[0] = sc[0];
+          dp_out[1] = sc[1];
         }
         if constexpr (PW) {
           const float* st = st_s[slot];
@@ -213,17 +217,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
             const f32x4 d1 = *(const f32x4*)(st + KBM + ks * 16 + 8 + lg * 4);
             float ds[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
+            for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_in[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
             const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(qsrc, ks, db), sb, acc[db]);
           }
         }
-        dp_prev[0] = sc[0];
-        dp_prev[1] = sc[1];
       }
       wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
       lds_barrier();
+    };
+    for (int t = t_start; t <= n_qt; t += 2) {
+      step(t, dpa, dpb);
+      if (t + 1 > n_qt) break;
+      step(t + 1, dpb, dpa);
     }
   }
 
