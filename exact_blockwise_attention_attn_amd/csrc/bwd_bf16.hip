@@ -26,6 +26,10 @@
 //
 // The dQ pass recomputes S and dP (7 contractions in all instead of 5); that
 // is the price of determinism without atomics.
+//
+// Around each block of matrix products a wavefront raises its issue priority
+// (s_setprio), so that while one wavefront of a SIMD has products ready the
+// matrix core is fed first and its partner's vector work fills the gaps.
 #include "attn_device.h"
 #include "attn_internal.h"
 #include "tile_lds.h"
@@ -153,11 +157,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
         // S = Q K^T (P wavefront) or dP = dO V^T (dS wavefront): lane = key,
         // registers = two 32-query blocks.
         const u16* rows = (PW ? q_s : d_s) + slot * SZ;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int si = 0; si < NS; ++si) {
 #pragma unroll
           for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(rf.get(rows, qb2, si), kv[si], sc[qb2]);
         }
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (!PW) {
           dp_out[0] = sc[0];
           dp_out[1] = sc[1];
@@ -192,6 +198,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
           // P in bf16, one B operand per 16-query slab: published for the
           // partner and used right away for dV^T += dO^T P.
           const u16* dsrc = d_s + slot * SZ;
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 pb = slab8(sc[ks >> 1], (ks & 1) * 8);
@@ -199,6 +206,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(dsrc, ks, db), pb, acc[db]);
           }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       if constexpr (!PW) {
@@ -219,8 +227,10 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
 #pragma unroll
             for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_in[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
             const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(qsrc, ks, db), sb, acc[db]);
+            __builtin_amdgcn_s_setprio(0);
           }
         }
       }
@@ -376,8 +386,10 @@ __device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, 
 #pragma unroll
           for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[ks >> 1][(ks & 1) * 8 + e] - stat);
           const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, ks, db), sb, acc[db]);
+          __builtin_amdgcn_s_setprio(0);
         }
       }
     }
@@ -386,11 +398,13 @@ __device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, 
       // query, registers = two 32-key blocks.
       const u16* rows = (SW ? k_s : v_s) + (t % 3) * SZ;
       f32x16 sc[2] = {f32x16{}, f32x16{}};
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) sc[kb2] = mfma32(rf.get(rows, kb2, s), op[s], sc[kb2]);
       }
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (SW) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
