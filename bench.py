@@ -137,11 +137,16 @@ def bench_shard(args, stream, do_bwd):
     def fwd():
         shard.shard_forward(q, k, v, CH, q_pos0=QP, causal=True, stream=stream, o_run=o_run, lse=lse, o_out=o)
 
+    def fwd_fused():
+        shard.shard_forward_fused(q, k, v, CH, q_pos0=QP, causal=True, stream=stream, lse=lse, o_out=o)
+
     f_fwd = 4.0 * SQ * SK * D * H / 2.0  # the stated convention: halved for causal
     if not do_bwd:
-        (t,), _ = time_calls([fwd], max(3, args.steps), 1, stream)
+        (t, tf), _ = time_calls([fwd, fwd_fused], max(3, args.steps), 1, stream)
         return {"workload": "shard_fwd_128k", "ms": t, "tflops": f_fwd / t / 1e9,
-                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": 17}
+                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": 17,
+                "fused_chunk_table": {"ms": tf, "tflops": f_fwd / tf / 1e9,
+                                      "frac_mfma": f_fwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
     fwd()
     do = randn_bf16((1, SQ, H, D), g)
     dq = torch.empty_like(q)

@@ -58,6 +58,24 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class FwdChunksArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("dtype", c_u32),
+        ("batch", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32), ("seqlen_q", c_i32), ("head_dim", c_i32),
+        ("n_chunks", c_i32),
+        ("q", c_vp), ("q_stride", I64x3),
+        ("k_chunks", ctypes.POINTER(c_vp)), ("v_chunks", ctypes.POINTER(c_vp)),
+        ("chunk_len", ctypes.POINTER(c_i32)), ("chunk_pos0", ctypes.POINTER(c_i64)),
+        ("k_stride", I64x3), ("v_stride", I64x3),
+        ("chunk_k_bstride", ctypes.POINTER(c_i64)), ("chunk_v_bstride", ctypes.POINTER(c_i64)),
+        ("o", c_vp), ("o_stride", I64x3), ("o_dtype", c_u32),
+        ("lse", c_vp),
+        ("o_final", c_vp), ("o_final_stride", I64x3),
+        ("q_pos0", c_i64),
+        ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+    ]
+
+
 class MergeArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_u32), ("n_parts", c_i32),
@@ -105,6 +123,7 @@ class DecodeArgs(ctypes.Structure):
 
 EXPORTED = [
     "attn_fwd_partial",
+    "attn_fwd_chunks",
     "attn_merge_lse",
     "attn_bwd",
     "attn_decode_splitkv",
@@ -142,6 +161,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
             _build.build()
         lib = ctypes.CDLL(path)
         for name, argt in (("attn_fwd_partial", [ctypes.POINTER(FwdArgs), c_vp]),
+                           ("attn_fwd_chunks", [ctypes.POINTER(FwdChunksArgs), c_vp]),
                            ("attn_merge_lse", [ctypes.POINTER(MergeArgs), c_vp]),
                            ("attn_bwd", [ctypes.POINTER(BwdArgs), c_vp]),
                            ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp])):
@@ -235,6 +255,44 @@ def attn_fwd_partial(q, k, v, o, lse, *, q_pos0=0, k_pos0=0, causal=False, scale
     a.scale = float(scale)
     a.flags = (ATTN_FWD_ACCUMULATE if accumulate else 0) | (ATTN_FWD_BALANCED if balanced else 0)
     _check(load().attn_fwd_partial(ctypes.byref(a), _stream(stream)))
+
+
+def attn_fwd_chunks(q, k_chunks, v_chunks, o, lse, *, chunk_pos0, q_pos0=0, causal=False, scale=0.0,
+                    accumulate=False, balanced=False, o_final=None, stream=None) -> None:
+    """Forward of q over a list of key/value chunks ([B, len_c, Hkv, D] bf16 each, common strides), one launch."""
+    n = len(k_chunks)
+    assert len(v_chunks) == n and len(chunk_pos0) == n
+    a = FwdChunksArgs()
+    a.struct_size = ctypes.sizeof(FwdChunksArgs)
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k_chunks[0].shape[2] if n else q.shape[2]
+    a.n_chunks = n
+    a.q, a.q_stride = _ptr(q), _strides3(q)
+    kp = (c_vp * max(n, 1))(*[_ptr(k) for k in k_chunks])
+    vp = (c_vp * max(n, 1))(*[_ptr(v) for v in v_chunks])
+    ln = (c_i32 * max(n, 1))(*[k.shape[1] for k in k_chunks])
+    ps = (c_i64 * max(n, 1))(*[int(x) for x in chunk_pos0])
+    a.k_chunks, a.v_chunks, a.chunk_len, a.chunk_pos0 = kp, vp, ln, ps
+    live = [k for k in k_chunks if k.shape[1] > 0]
+    a.k_stride = _strides3(live[0]) if live else I64x3(0, 0, 0)
+    live_v = [v for v in v_chunks if v.shape[1] > 0]
+    a.v_stride = _strides3(live_v[0]) if live_v else I64x3(0, 0, 0)
+    for k in live:
+        assert tuple(k.stride()[1:3]) == tuple(a.k_stride)[1:], "key chunks must share sequence and head strides"
+    for v in live_v:
+        assert tuple(v.stride()[1:3]) == tuple(a.v_stride)[1:], "value chunks must share sequence and head strides"
+    kbs = (c_i64 * max(n, 1))(*[k.stride(0) if k.numel() else 0 for k in k_chunks])
+    vbs = (c_i64 * max(n, 1))(*[v.stride(0) if v.numel() else 0 for v in v_chunks])
+    a.chunk_k_bstride, a.chunk_v_bstride = kbs, vbs
+    a.o, a.o_stride, a.o_dtype = _ptr(o), _strides3(o), _dtype_code(o)
+    a.lse = _ptr(lse)
+    a.o_final, a.o_final_stride = _ptr(o_final), _strides3(o_final)
+    a.q_pos0 = int(q_pos0)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = (ATTN_FWD_ACCUMULATE if accumulate else 0) | (ATTN_FWD_BALANCED if balanced else 0)
+    _check(load().attn_fwd_chunks(ctypes.byref(a), _stream(stream)))
 
 
 def attn_merge_lse(o_parts, lse_parts, o_out, lse_out, *, tree=False, stream=None) -> None:

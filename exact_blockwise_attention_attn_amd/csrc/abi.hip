@@ -159,6 +159,82 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   return ok();
 }
 
+int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_fwd_chunks_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_fwd_chunks_args));
+  if (a->dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported (bf16 only)", a->dtype);
+  if (a->o_dtype != ATTN_DTYPE_BF16 && a->o_dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "o_dtype %u is not supported", a->o_dtype);
+  if (a->flags & ~(ATTN_FWD_ACCUMULATE | ATTN_FWD_BALANCED))
+    return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
+  const bool accumulate = a->flags & ATTN_FWD_ACCUMULATE;
+  if (accumulate && a->o_dtype != ATTN_DTYPE_F32)
+    return fail(ATTN_ERR_INVALID_ARG, "ATTN_FWD_ACCUMULATE needs an fp32 running output");
+  if (a->n_chunks < 0 || a->n_chunks > ATTN_MAX_CHUNKS)
+    return fail(ATTN_ERR_INVALID_ARG, "n_chunks must be in [0, %d]", ATTN_MAX_CHUNKS);
+  TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, 0, a->head_dim));
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  const bool has_q = a->seqlen_q > 0;
+  TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
+  TRY(check_view("o", a->o, a->o_stride, 3, a->o_dtype, has_q));
+  if (has_q && !a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (has_q && !aligned16(a->lse)) return fail(ATTN_ERR_UNSUPPORTED, "lse is not 16-byte aligned");
+  if (a->o_final) TRY(check_view("o_final", a->o_final, a->o_final_stride, 3, ATTN_DTYPE_BF16, has_q));
+  if (a->n_chunks > 0 && (!a->k_chunks || !a->v_chunks || !a->chunk_len || !a->chunk_pos0))
+    return fail(ATTN_ERR_INVALID_ARG, "chunk arrays must not be NULL");
+  attn::ChunkTable ct{};
+  ct.q_pos0 = a->q_pos0;
+  for (int c = 0; c < a->n_chunks; ++c) {
+    if (a->chunk_len[c] < 0) return fail(ATTN_ERR_INVALID_ARG, "chunk_len[%d] is negative", c);
+    if (a->chunk_len[c] == 0) continue;
+    const int64_t ks[3] = {a->chunk_k_bstride ? a->chunk_k_bstride[c] : a->k_stride[0], a->k_stride[1],
+                           a->k_stride[2]};
+    const int64_t vs[3] = {a->chunk_v_bstride ? a->chunk_v_bstride[c] : a->v_stride[0], a->v_stride[1],
+                           a->v_stride[2]};
+    char name[32];
+    snprintf(name, sizeof name, "k_chunks[%d]", c);
+    TRY(check_view(name, a->k_chunks[c], ks, 3, a->dtype, has_q));
+    snprintf(name, sizeof name, "v_chunks[%d]", c);
+    TRY(check_view(name, a->v_chunks[c], vs, 3, a->dtype, has_q));
+    ct.k[ct.n] = a->k_chunks[c];
+    ct.v[ct.n] = a->v_chunks[c];
+    ct.kb[ct.n] = ks[0];
+    ct.vb[ct.n] = vs[0];
+    ct.len[ct.n] = a->chunk_len[c];
+    ct.pos0[ct.n] = a->chunk_pos0[c];
+    ++ct.n;
+  }
+  const int64_t units = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64);
+  if (units > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (!has_q) return ok();
+  // No chunk with keys: a running result is left as it is.
+  if (ct.n == 0 && accumulate && !a->o_final) return ok();
+
+  attn::FwdParams p{};
+  p.q = view(a->q, a->q_stride);
+  p.k = view(nullptr, a->k_stride);
+  p.v = view(nullptr, a->v_stride);
+  p.o = mview(a->o, a->o_stride);
+  p.o_final = mview(a->o_final, a->o_final_stride);
+  p.lse = a->lse;
+  p.B = a->batch;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.Sq = a->seqlen_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.causal = a->causal != 0;
+  p.o_f32 = a->o_dtype == ATTN_DTYPE_F32;
+  p.accumulate = accumulate;
+  p.balanced = (a->flags & ATTN_FWD_BALANCED) != 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_fwd_chunks_bf16(p, ct, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunks launch");
+  return ok();
+}
+
 int attn_merge_lse(const attn_merge_args* a, void* stream) {
   if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
   if (a->struct_size < sizeof(attn_merge_args))

@@ -36,6 +36,21 @@ struct FwdParams {
   int n_units;      // work units per (b, h) (n_qtiles, or ceil(n_qtiles / 2) when balanced)
 };
 
+// Key/value chunks of a fused multi-chunk forward: chunk c has len[c] keys at
+// global positions pos0[c] .. pos0[c] + len[c] - 1, in tensors at k[c] and v[c]
+// with batch strides kb[c], vb[c] and the sequence and head strides of
+// FwdParams::k and FwdParams::v.
+constexpr int kMaxChunks = 64;
+struct ChunkTable {
+  const void* k[kMaxChunks];
+  const void* v[kMaxChunks];
+  int64_t kb[kMaxChunks], vb[kMaxChunks];
+  int64_t pos0[kMaxChunks];
+  int len[kMaxChunks];
+  int n;
+  int64_t q_pos0;
+};
+
 struct MergeParams {
   const float* o_parts;
   int64_t o_part_stride, o_sb, o_ss, o_sh;
@@ -92,6 +107,9 @@ struct DecodeParams {
 // Launchers (return the launch status).  D is the head dimension.
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
+// Fused forward over a chunk table (bf16): one launch, the running (O, LSE) of
+// each query stays in registers across chunks.
+hipError_t launch_fwd_chunks_bf16(const FwdParams& p, const ChunkTable& c, int D, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int D, hipStream_t s);
 // Backward: fill the statistics workspace (delta = rowsum(dO * O), rescaled
 // LSE); then dK/dV (key-outer) and, when run_dq, dQ (query-outer, accumulated

@@ -129,6 +129,42 @@ __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf
   }
 }
 
+// Epilogue: normalise, optionally merge into the running result, store.
+template <int D>
+__device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x16* oacc, const RowState& st, int qi,
+                                          bool qok, int b, int h, int lg) {
+  constexpr int NDB = D / 32;
+  const float l_tot = half_sum(st.l);
+  if (!qok) return;
+  const float lse_this = (l_tot > 0.f) ? fmaf(st.m, p.scale, logf(l_tot)) : neg_inf();
+  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Sq + qi;
+  float w_old = 0.f, w_new = 1.f, L = lse_this;
+  if (p.accumulate) merge_weights(*lse_ptr, lse_this, w_old, w_new, L);
+  w_new *= inv;
+  const int64_t orow = (int64_t)b * p.o.sb + (int64_t)qi * p.o.ss + (int64_t)h * p.o.sh;
+  const int64_t frow = (int64_t)b * p.o_final.sb + (int64_t)qi * p.o_final.ss + (int64_t)h * p.o_final.sh;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = db * 32 + j * 8 + lg * 4;
+      f32x4 v = {oacc[db][4 * j] * w_new, oacc[db][4 * j + 1] * w_new, oacc[db][4 * j + 2] * w_new,
+                 oacc[db][4 * j + 3] * w_new};
+      if (p.o_f32) {
+        f32x4* dst = (f32x4*)((float*)p.o.ptr + orow + d);
+        if (p.accumulate && w_old != 0.f) v += w_old * (*dst);
+        *dst = v;
+      } else {
+        *(u32x2*)((u16*)p.o.ptr + orow + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+      if (p.o_final.ptr)
+        *(u32x2*)((u16*)p.o_final.ptr + frow + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  }
+  if (lg == 0) *lse_ptr = L;
+}
+
 template <int D>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s, u16* k1s, u16* v1s, int qt, int b,
                                          int h, const u16* qb, const u16* kb, const u16* vb) {
@@ -184,36 +220,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   }
   __syncthreads();  // the next call of this function reuses the buffers
 
-  // Epilogue: normalise, optionally merge into the running result, store.
-  const float l_tot = half_sum(st.l);
-  if (!qok) return;
-  const float lse_this = (l_tot > 0.f) ? fmaf(st.m, p.scale, logf(l_tot)) : neg_inf();
-  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Sq + qi;
-  float w_old = 0.f, w_new = 1.f, L = lse_this;
-  if (p.accumulate) merge_weights(*lse_ptr, lse_this, w_old, w_new, L);
-  w_new *= inv;
-  const int64_t orow = (int64_t)b * p.o.sb + (int64_t)qi * p.o.ss + (int64_t)h * p.o.sh;
-  const int64_t frow = (int64_t)b * p.o_final.sb + (int64_t)qi * p.o_final.ss + (int64_t)h * p.o_final.sh;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + j * 8 + lg * 4;
-      f32x4 v = {oacc[db][4 * j] * w_new, oacc[db][4 * j + 1] * w_new, oacc[db][4 * j + 2] * w_new,
-                 oacc[db][4 * j + 3] * w_new};
-      if (p.o_f32) {
-        f32x4* dst = (f32x4*)((float*)p.o.ptr + orow + d);
-        if (p.accumulate && w_old != 0.f) v += w_old * (*dst);
-        *dst = v;
-      } else {
-        *(u32x2*)((u16*)p.o.ptr + orow + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
-      if (p.o_final.ptr)
-        *(u32x2*)((u16*)p.o_final.ptr + frow + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    }
-  }
-  if (lg == 0) *lse_ptr = L;
+  fwd_store<D>(p, oacc, st, qi, qok, b, h, lg);
 }
 
 template <int D>
@@ -244,7 +251,145 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// ------------------------------------------------------ fused chunk table --
+//
+// The same tile step over the keys of several chunks, in chunk order, in one
+// launch: the online softmax state and O^T stay in registers from the first
+// chunk to the last, and the result is written once.  Each chunk's causal
+// visibility is classified from its own global position; chunks or tiles no
+// query of the tile sees are skipped.  The next tile (possibly the first of a
+// later chunk) streams into the other LDS buffer while the current one is
+// used; the loads are untracked by the compiler and waited for explicitly.
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Barrier for LDS data only; the tile prefetch stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D>
+__device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTable& ct, u16* k_s, u16* v_s, int qt,
+                                               int b, int h, int hk, const u16* qb) {
+  constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int q0 = qt * BM;
+  const int qi = q0 + wave * 32 + lr;
+  const bool qok = qi < p.Sq;
+  const int q_last = min(q0 + BM, p.Sq) - 1;
+
+  // Keys [0, kv_end) of chunk c are visible to some query of this tile, keys
+  // [0, full_end) to all of them.
+  auto chunk_range = [&](int c, int& kv_end, int& full_end) {
+    const int len = ct.len[c];
+    kv_end = full_end = len;
+    if (p.causal) {
+      const int64_t dl = ct.q_pos0 - ct.pos0[c];
+      kv_end = (int)max<int64_t>(0, min<int64_t>(dl + q_last + 1, len));
+      full_end = (int)max<int64_t>(0, min<int64_t>(dl + q0 + 1, len));
+    }
+  };
+  auto n_tiles_of = [&](int c) {
+    int e, f;
+    chunk_range(c, e, f);
+    return (e + BN - 1) / BN;
+  };
+  auto first_from = [&](int c) {
+    while (c < ct.n && n_tiles_of(c) == 0) ++c;
+    return c;
+  };
+
+  bf16x8 qf[NS];
+  {
+    const u16* qrow = qb + (int64_t)qi * p.q.ss + lg * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = qok ? as_bf16x8(*(const u32x4*)(qrow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  wait_vm<0>();  // the query rows are complete before any tile load is in flight
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  RowState st{neg_inf(), 0.f};
+  const float sl2 = p.scale_log2;
+  RowFrag<D> rf;
+  TrFrag<D> tf;
+  rf.init(lane);
+  tf.init(lane);
+
+  auto issue = [&](int c, int tile, int slot) {
+    const u16* kb = (const u16*)ct.k[c] + (int64_t)b * ct.kb[c] + (int64_t)hk * p.k.sh;
+    const u16* vb = (const u16*)ct.v[c] + (int64_t)b * ct.vb[c] + (int64_t)hk * p.v.sh;
+    issue_swtile<D, 4, true>(k_s + slot * SZ, kb, p.k.ss, tile * BN, ct.len[c], wave, lane);
+    issue_swtile<D, 4, true>(v_s + slot * SZ, vb, p.v.ss, tile * BN, ct.len[c], wave, lane);
+  };
+
+  int c = first_from(0), t = 0, slot = 0;
+  if (c < ct.n) {
+    issue(c, 0, 0);
+    wait_vm<0>();
+    lds_barrier();
+  }
+  while (c < ct.n) {
+    int kv_end, full_end;
+    chunk_range(c, kv_end, full_end);
+    // Next tile in sequence: the rest of this chunk, then the next chunk with visible keys.
+    int nc = c, nt = t + 1;
+    if (nt * BN >= kv_end) {
+      nc = first_from(c + 1);
+      nt = 0;
+    }
+    if (nc < ct.n) issue(nc, nt, slot ^ 1);
+    int64_t lim64 = (int64_t)ct.len[c] - 1;  // this lane's last visible key of chunk c
+    if (p.causal) lim64 = min<int64_t>(ct.q_pos0 - ct.pos0[c] + qi, lim64);
+    tile_step<D>(k_s + slot * SZ, v_s + slot * SZ, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf,
+                 lane);
+    wait_vm<0>();  // the next tile, the only load in flight
+    lds_barrier();
+    c = nc;
+    t = nt;
+    slot ^= 1;
+  }
+  fwd_store<D>(p, oacc, st, qi, qok, b, h, lg);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void fwd_chunks_kernel(FwdParams p, ChunkTable ct) {
+  __shared__ __attribute__((aligned(16))) u16 k_s[2 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v_s[2 * SwTile<D>::SIZE];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = lin % p.n_units;
+  const int bh = lin / p.n_units;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int hk = h / p.group;
+  const u16* qb = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
+  // Balanced: pair a late and an early query tile; otherwise causal grids run
+  // the heaviest tiles first.
+  const int last = p.n_qtiles - 1 - unit;
+  const int n = (p.balanced && last != unit) ? 2 : 1;
+  for (int k = 0; k < n; ++k) {
+    const int qt = p.balanced ? (k == 0 ? last : unit) : (p.causal ? last : unit);
+    fwd_chunk_tile<D>(p, ct, k_s, v_s, qt, b, h, hk, qb);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fwd_chunks_bf16(const FwdParams& p0, const ChunkTable& ct, int D, hipStream_t s) {
+  FwdParams p = p0;
+  p.n_qtiles = (p.Sq + BM - 1) / BM;
+  p.n_units = p.balanced ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  const int64_t grid = (int64_t)p.B * p.Hq * p.n_units;
+  if (grid == 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL(fwd_chunks_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, ct);
+  else
+    hipLaunchKernelGGL(fwd_chunks_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, ct);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
   FwdParams p = p0;

@@ -53,6 +53,25 @@ def shard_forward(q, k, v, chunk, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0
     return (o_out if o_out is not None else o_run), lse, o_run
 
 
+def shard_forward_fused(q, k, v, chunk, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0, stream=None,
+                        o_out=None, lse=None):
+    """The same result as shard_forward in one launch over the chunk table (bf16 only).
+
+    k and v are split into views of `chunk` keys; the kernel keeps each query's
+    running (O, LSE) on chip across the chunks.  Returns (o_out, lse).
+    """
+    b, sq, hq, d = q.shape
+    sk = k.shape[1]
+    dev = q.device
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device=dev) if lse is None else lse
+    o_out = torch.empty((b, sq, hq, d), dtype=q.dtype, device=dev) if o_out is None else o_out
+    bounds = chunk_bounds(sk, chunk)
+    B.attn_fwd_chunks(q, [k[:, a:e] for a, e in bounds], [v[:, a:e] for a, e in bounds], o_out, lse,
+                      chunk_pos0=[k_pos0 + a for a, _ in bounds], q_pos0=q_pos0, causal=causal, scale=scale,
+                      stream=stream)
+    return o_out, lse
+
+
 def shard_forward_partials(q, k, v, chunk, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0, tree=False,
                            stream=None):
     """Per-chunk partials into a stacked fp32 buffer, then one merge call.  Returns (o, lse, parts)."""

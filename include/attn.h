@@ -65,7 +65,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -119,6 +119,60 @@ typedef struct attn_fwd_args {
 } attn_fwd_args;
 
 ATTN_API int attn_fwd_partial(const attn_fwd_args* args, void* stream);
+
+#define ATTN_MAX_CHUNKS 64
+
+/*
+ * attn_fwd_chunks: the forward of a query shard over a sequence of key/value
+ * chunks in one call -- the aggregation of local results of the BurstAttention
+ * and ring-attention pages, with the running (O, LSE) of each query kept on
+ * chip across the chunks instead of being merged through memory chunk by
+ * chunk.  The result equals attn_fwd_partial over the union of the chunks'
+ * keys (key j of chunk c sits at global position chunk_pos0[c] + j), which is
+ * also what chained attn_fwd_partial(ACCUMULATE) calls over the chunks give.
+ *
+ * Chunk c is a key tensor k_chunks[c] and a value tensor v_chunks[c], both
+ * [batch, chunk_len[c], heads_kv, head_dim] bf16.  Their sequence and head
+ * element strides are the shared k_stride[1..2] / v_stride[1..2]; the batch
+ * stride is chunk_k_bstride[c] / chunk_v_bstride[c], or k_stride[0] /
+ * v_stride[0] for every chunk when those arrays are NULL (so separately
+ * allocated chunks of different lengths can be passed).  k_chunks, v_chunks,
+ * chunk_len, chunk_pos0 and the batch-stride arrays are HOST arrays of
+ * n_chunks entries (read during the call; the device pointers they hold must
+ * stay valid until the stream work finishes).  A
+ * chunk of length 0 is skipped.  dtype must be ATTN_DTYPE_BF16.  o, lse,
+ * o_final, ACCUMULATE and BALANCED behave as in attn_fwd_partial; a query that
+ * sees no key of any chunk gets O = 0, LSE = -inf (or, with ACCUMULATE, keeps
+ * its running result).
+ */
+typedef struct attn_fwd_chunks_args {
+  uint32_t struct_size;
+  uint32_t dtype; /* ATTN_DTYPE_BF16 */
+  int32_t batch, heads_q, heads_kv, seqlen_q, head_dim;
+  int32_t n_chunks; /* 0 .. ATTN_MAX_CHUNKS */
+  const void* q;
+  int64_t q_stride[3];
+  const void* const* k_chunks;  /* host array of n_chunks device pointers */
+  const void* const* v_chunks;  /* host array of n_chunks device pointers */
+  const int32_t* chunk_len;     /* host array: keys in each chunk (>= 0) */
+  const int64_t* chunk_pos0;    /* host array: global position of each chunk's key 0 */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  const int64_t* chunk_k_bstride; /* host array or NULL: batch stride of each key chunk */
+  const int64_t* chunk_v_bstride; /* host array or NULL: batch stride of each value chunk */
+  void* o;
+  int64_t o_stride[3];
+  uint32_t o_dtype; /* ATTN_DTYPE_F32 or ATTN_DTYPE_BF16 (the latter only without ACCUMULATE) */
+  float* lse;       /* [batch, heads_q, seqlen_q] */
+  void* o_final;    /* optional bf16 copy of the output, NULL to skip */
+  int64_t o_final_stride[3];
+  int64_t q_pos0;
+  int32_t causal;
+  float scale;
+  uint32_t flags; /* ATTN_FWD_ACCUMULATE, ATTN_FWD_BALANCED */
+} attn_fwd_chunks_args;
+
+ATTN_API int attn_fwd_chunks(const attn_fwd_chunks_args* args, void* stream);
 
 /* attn_merge_lse modes. */
 #define ATTN_MERGE_SEQUENTIAL 0 /* fold parts 0, 1, ..., n-1 in order */

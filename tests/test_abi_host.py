@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -50,8 +50,11 @@ def test_struct_layouts_match_c():
 #include "attn.h"
 #define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F))
 int main(void) {
-  printf("fwd %zu\nmerge %zu\nbwd %zu\ndecode %zu\n", sizeof(attn_fwd_args), sizeof(attn_merge_args),
-         sizeof(attn_bwd_args), sizeof(attn_decode_args));
+  printf("fwd %zu\nmerge %zu\nbwd %zu\ndecode %zu\nchunks %zu\n", sizeof(attn_fwd_args), sizeof(attn_merge_args),
+         sizeof(attn_bwd_args), sizeof(attn_decode_args), sizeof(attn_fwd_chunks_args));
+  P(attn_fwd_chunks_args, k_chunks); P(attn_fwd_chunks_args, chunk_pos0); P(attn_fwd_chunks_args, v_stride);
+  P(attn_fwd_chunks_args, o_final_stride); P(attn_fwd_chunks_args, q_pos0); P(attn_fwd_chunks_args, flags);
+  P(attn_fwd_chunks_args, chunk_v_bstride); P(attn_fwd_chunks_args, o);
   P(attn_fwd_args, flags); P(attn_fwd_args, o_final_stride); P(attn_fwd_args, q_pos0);
   P(attn_merge_args, mode); P(attn_merge_args, lse_out);
   P(attn_bwd_args, flags); P(attn_bwd_args, dv_stride); P(attn_bwd_args, dq_acc);
@@ -70,8 +73,9 @@ int main(void) {
     assert int(got["merge"]) == ctypes.sizeof(B.MergeArgs)
     assert int(got["bwd"]) == ctypes.sizeof(B.BwdArgs)
     assert int(got["decode"]) == ctypes.sizeof(B.DecodeArgs)
+    assert int(got["chunks"]) == ctypes.sizeof(B.FwdChunksArgs)
     cls = {"attn_fwd_args": B.FwdArgs, "attn_merge_args": B.MergeArgs, "attn_bwd_args": B.BwdArgs,
-           "attn_decode_args": B.DecodeArgs}
+           "attn_decode_args": B.DecodeArgs, "attn_fwd_chunks_args": B.FwdChunksArgs}
     for key, val in got.items():
         if "." in key:
             t, f = key.split(".")
@@ -79,7 +83,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -217,6 +221,57 @@ def test_bwd_rejects(lib, kw, code, msg):
     a = bwd_args(**kw)
     assert lib.attn_bwd(ctypes.byref(a), None) == code
     assert msg in lib.attn_last_error().decode()
+
+
+def chunks_args(n=2, lens=(64, 0), **kw):
+    a = B.FwdChunksArgs()
+    a.struct_size = ctypes.sizeof(B.FwdChunksArgs)
+    a.dtype = B.ATTN_DTYPE_BF16
+    a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.head_dim = 1, 2, 2, 32, 64
+    a.q = a.o = a.lse = FAKE
+    a.o_dtype = B.ATTN_DTYPE_F32
+    st = B.I64x3(64 * 2 * 64, 2 * 64, 64)
+    a.q_stride = a.o_stride = a.k_stride = a.v_stride = st
+    a.n_chunks = n
+    a._keep = ((ctypes.c_void_p * 2)(FAKE, FAKE), (ctypes.c_void_p * 2)(FAKE, FAKE),
+               (ctypes.c_int32 * 2)(*lens), (ctypes.c_int64 * 2)(0, 64))
+    a.k_chunks, a.v_chunks, a.chunk_len, a.chunk_pos0 = a._keep
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+CHUNKS_BAD = [
+    (dict(n_chunks=65), B.ATTN_ERR_INVALID_ARG, "n_chunks"),
+    (dict(n_chunks=-1), B.ATTN_ERR_INVALID_ARG, "n_chunks"),
+    (dict(dtype=B.ATTN_DTYPE_F32), B.ATTN_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(flags=1 << 7), B.ATTN_ERR_INVALID_ARG, "flag"),
+    (dict(flags=B.ATTN_FWD_ACCUMULATE, o_dtype=B.ATTN_DTYPE_BF16), B.ATTN_ERR_INVALID_ARG, "fp32 running"),
+    (dict(k_chunks=None), B.ATTN_ERR_INVALID_ARG, "chunk arrays"),
+    (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse is NULL"),
+    (dict(k_stride=B.I64x3(64 * 2 * 64, 2 * 64, 3)), B.ATTN_ERR_UNSUPPORTED, "k_chunks[0] stride"),
+    (dict(head_dim=96), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(chunk_k_bstride=(ctypes.c_int64 * 2)(5, 5)), B.ATTN_ERR_UNSUPPORTED, "k_chunks[0] stride[0]"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", CHUNKS_BAD, ids=[m for _, _, m in CHUNKS_BAD])
+def test_fwd_chunks_rejects(lib, kw, code, msg):
+    a = chunks_args(**kw)
+    assert lib.attn_fwd_chunks(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_fwd_chunks_rejects_negative_length(lib):
+    a = chunks_args(lens=(64, -5))
+    assert lib.attn_fwd_chunks(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "chunk_len[1]" in lib.attn_last_error().decode()
+
+
+def test_fwd_chunks_empty_query_is_noop(lib):
+    # No query rows: nothing is launched and no pointer is dereferenced.
+    a = chunks_args(seqlen_q=0, q=None, o=None, lse=None)
+    assert lib.attn_fwd_chunks(ctypes.byref(a), None) == B.ATTN_OK
 
 
 def decode_args(**kw):

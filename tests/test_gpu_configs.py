@@ -77,19 +77,21 @@ def test_shard_fwd_128k(shard_inputs):
     o, lse, o_run = shard.shard_forward(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
     log("shard_fwd_128k: per-chunk partials + one sequential merge")
     o2, lse2, _ = shard.shard_forward_partials(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
+    log("shard_fwd_128k: fused chunk table, one launch")
+    o3, lse3 = shard.shard_forward_fused(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
     torch.cuda.synchronize()
     assert o.shape == (1, 4096, 32, 128) and o.dtype == torch.bfloat16
     # Sampled rows of every head against the oracle.  Keys past the shard's last
     # position are invisible to every query; the oracle sees them all anyway.
     runs = _runs(w.S_q, [0, 1000, 2048, 4080], 16)
-    o_np, l_np, o2_np, l2_np = to_np(o), to_np(lse), to_np(o2), to_np(lse2)
+    o_np, l_np, o2_np, l2_np, o3_np, l3_np = to_np(o), to_np(lse), to_np(o2), to_np(lse2), to_np(o3), to_np(lse3)
     errs = {"O": 0.0, "LSE": 0.0}
     rms_o = []
     for h in range(w.H_q):
         kh, vh = _f64(kb[0, :, h]), _f64(vb[0, :, h])
         for a, e in runs:
             O_ref, L_ref = oracle.attention_head(_f64(qb[0, a:e, h]), kh, vh, w.scale, True, w.q_pos0 + a, 0)
-            for got_o, got_l in ((o_np, l_np), (o2_np, l2_np)):
+            for got_o, got_l in ((o_np, l_np), (o2_np, l2_np), (o3_np, l3_np)):
                 errs["O"] = max(errs["O"], np.abs(got_o[0, a:e, h] - O_ref).max())
                 errs["LSE"] = max(errs["LSE"], np.abs(got_l[0, h, a:e] - L_ref).max())
             rms_o.append(np.sqrt(np.mean(O_ref ** 2)))

@@ -85,6 +85,92 @@ def test_fwd_strided_views_and_scale():
     check("LSE", lse, L_ref, L_TOL)
 
 
+def _oracle_over_chunks(qh, chunks, scale, causal, q_pos0):
+    """Oracle attention over a list of (k, v, pos0) chunks: each chunk on its own, then merged."""
+    parts = []
+    for kh, vh, pos0 in chunks:
+        if kh.shape[1] == 0:
+            continue
+        O, L = oracle.attention(qh, kh, vh, scale, causal, q_pos0, pos0)
+        parts.append((O, np.transpose(L, (0, 2, 1))))
+    if not parts:
+        Bn, Sq, Hq, D = qh.shape
+        return np.zeros((Bn, Sq, Hq, D)), np.full((Bn, Hq, Sq), -np.inf)
+    O, L = oracle.merge(parts)
+    return O, np.transpose(L, (0, 2, 1))
+
+
+# (B, Sq, Hq, Hkv, D, chunk lengths, chunk positions, q_pos0, causal, balanced)
+FUSED_CASES = [
+    # contiguous chunks, ragged lengths, an empty chunk, causal with a partly visible diagonal
+    (1, 200, 2, 2, 128, (64, 100, 0, 37), (0, 64, 164, 164), 100, True, False),
+    # chunks out of position order, grouped heads, head_dim 64
+    (2, 130, 4, 2, 64, (129, 200), (1000, 0), 1100, True, False),
+    # non-causal, one long chunk
+    (1, 64, 2, 1, 128, (300,), (0,), 0, False, False),
+    # a chunk entirely after every query (skipped) and one every query sees
+    (1, 96, 2, 2, 128, (128, 64), (5000, 0), 200, True, True),
+    # the shard layout: 8 chunks of 64 keys, queries in the middle of the range
+    (1, 256, 2, 2, 128, (64,) * 8, tuple(64 * i for i in range(8)), 192, True, True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=_ids(FUSED_CASES))
+def test_fwd_chunks_fused(case):
+    """One launch over a chunk table against the oracle over the same chunks, for fp32 and
+    bf16 outputs; with ACCUMULATE the chunks merge into a running result from an earlier call."""
+    Bn, Sq, Hq, Hkv, D, lens, pos, qp, causal, bal = case
+    log(f"fwd chunks {case}")
+    q, qh = seq_tensor(109, 0, Bn, Sq, Hq, D, "bf16")
+    chunks, chunks_h = [], []
+    for c, L in enumerate(lens):
+        k, kh = seq_tensor(109, 10 + 2 * c, Bn, L, Hkv, D, "bf16")
+        v, vh = seq_tensor(109, 11 + 2 * c, Bn, L, Hkv, D, "bf16")
+        chunks.append((k, v))
+        chunks_h.append((kh, vh, pos[c]))
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = _oracle_over_chunks(qh, chunks_h, scale, causal, qp)
+    ks, vs = [k for k, _ in chunks], [v for _, v in chunks]
+    for odt in (torch.float32, torch.bfloat16):
+        o = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=odt, device="cuda")
+        lse = torch.full((Bn, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
+        B.attn_fwd_chunks(q, ks, vs, o, lse, chunk_pos0=pos, q_pos0=qp, causal=causal, balanced=bal)
+        torch.cuda.synchronize()
+        check(f"O ({odt})", o, O_ref, O_TOL, scale_by_max=True)
+        check("LSE", lse, L_ref, L_TOL)
+    # ACCUMULATE: a running result over extra keys at other positions, then the chunk table.
+    ke, keh = seq_tensor(109, 90, Bn, 77, Hkv, D, "bf16")
+    ve, veh = seq_tensor(109, 91, Bn, 77, Hkv, D, "bf16")
+    o = torch.empty((Bn, Sq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Bn, Hq, Sq), dtype=torch.float32, device="cuda")
+    B.attn_fwd_partial(q, ke, ve, o, lse, q_pos0=qp, k_pos0=-500, causal=causal)
+    of = torch.empty((Bn, Sq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    B.attn_fwd_chunks(q, ks, vs, o, lse, chunk_pos0=pos, q_pos0=qp, causal=causal, accumulate=True, o_final=of)
+    torch.cuda.synchronize()
+    O_acc, L_acc = _oracle_over_chunks(qh, [(keh, veh, -500)] + chunks_h, scale, causal, qp)
+    check("O accumulate", o, O_acc, O_TOL, scale_by_max=True)
+    check("O final bf16", of, O_acc, O_TOL, scale_by_max=True)
+    check("LSE accumulate", lse, L_acc, L_TOL)
+
+
+def test_fwd_chunks_matches_chained_partials():
+    """The fused call and chained attn_fwd_partial(ACCUMULATE) calls over the same chunks agree."""
+    log("fwd chunks vs chained")
+    Bn, Sq, H, D = 1, 160, 2, 128
+    q, _ = seq_tensor(110, 0, Bn, Sq, H, D, "bf16")
+    k, _ = seq_tensor(110, 1, Bn, 640, H, D, "bf16")
+    v, _ = seq_tensor(110, 2, Bn, 640, H, D, "bf16")
+    bounds = [(0, 128), (128, 300), (300, 640)]
+    ks, vs = [k[:, a:e] for a, e in bounds], [v[:, a:e] for a, e in bounds]
+    o1 = torch.empty((Bn, Sq, H, D), dtype=torch.float32, device="cuda")
+    l1 = torch.empty((Bn, H, Sq), dtype=torch.float32, device="cuda")
+    B.attn_fwd_chunks(q, ks, vs, o1, l1, chunk_pos0=[a for a, _ in bounds], q_pos0=400, causal=True)
+    _, l2, o2 = shard.shard_forward(q, k, v, 128, q_pos0=400, causal=True)
+    torch.cuda.synchronize()
+    check("O fused vs chained", o1, to_np(o2), O_TOL, scale_by_max=True)
+    check("LSE fused vs chained", l1, to_np(l2), L_TOL)
+
+
 # (Sq, Sk, chunk, causal, q_pos0, Hq, Hkv, D, dtype)
 CHUNK_CASES = [
     (256, 256, 64, False, 0, 1, 1, 64, "f32"),
