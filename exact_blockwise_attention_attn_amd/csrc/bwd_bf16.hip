@@ -16,13 +16,14 @@
 //   double buffered); the transposed operands Q^T, dO^T are read from the same
 //   row-major tiles with ds_read_b64_tr_b16.
 //
-//   dQ kernel (query-outer).  A workgroup owns 128 queries (32 per wavefront,
-//   Q and dO in registers) and walks the key tiles.  Scores are formed
-//   transposed, S^T = K Q^T, one query per lane, so the row statistics (LSE,
-//   delta) are per-lane scalars and dS^T feeds dQ^T += K^T dS^T straight from
-//   registers; K^T is read from the row-major key tile with the transposing
-//   LDS read.  dQ is added into an fp32 accumulator that persists across key
-//   chunks and is cast once at the end.
+//   dQ kernel (query-outer).  A workgroup owns 128 queries (32 per wavefront
+//   pair, Q and dO in registers) and walks the key tiles; the two wavefronts
+//   of a pair split each tile's keys.  Scores are formed transposed,
+//   S^T = K Q^T, one query per lane, so the row statistics (LSE, delta) are
+//   per-lane scalars and dS^T feeds dQ^T += K^T dS^T straight from registers;
+//   K^T is read from the row-major key tile with the transposing LDS read.  dQ
+//   is added into an fp32 accumulator that persists across key chunks and is
+//   cast once at the end.
 //
 // The dQ pass recomputes S and dP (7 contractions in all instead of 5); that
 // is the price of determinism without atomics.
@@ -294,28 +295,36 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
 
 // --------------------------------------------------------------------- dQ --
 //
-// Eight wavefronts in four pairs; pair w%4 owns queries q0 + 32*(w%4) .. +31.
-// Key/value tiles of 64 rows stream through a 3-stage LDS ring, one tile per
-// step.  At step t:
-//   * the "S" wavefront (w < 4) holds Q in registers, forms S^T = K Q^T for
-//     tile t (one query per lane, two 32-key blocks), P = exp(S - LSE) with
-//     the mask, and hands P to its partner through LDS;
-//   * the "dP" wavefront (w >= 4) holds dO and the whole dQ^T accumulator. It
-//     first finishes tile t - 1 (one step behind, so that P is published):
-//     reads P, forms dS = P (dP - delta) and runs dQ^T += K^T dS^T; then it
-//     forms dP^T = V dO^T for tile t.
-// The S wavefront carries the exponentials, the dP wavefront two thirds of the
-// contractions; a pair shares one SIMD, whose matrix core they keep busy in
-// turn.  One LDS-only barrier per step publishes P and the next tile.
+// Eight wavefronts in four pairs; pair w%4 owns queries q0 + 32*(w%4) .. +31
+// and holds their Q and dO rows in registers.  Key/value tiles of 64 rows
+// stream through a 3-stage LDS ring; wavefront w takes keys 32*(w/4) .. +31 of
+// every tile and runs the whole chain for them on its own: S^T = K Q^T and
+// dP^T = V dO^T (one query per lane), P = exp(S - LSE) with the mask,
+// dS = P (dP - delta), dQ^T += K^T dS^T.  The two wavefronts of a pair share
+// no data until the end, where their dQ^T partials are added through LDS.
 
 constexpr int DQ_NT = 512;
+constexpr int DQ_STAGES = 3;
 
-template <int D, bool SW>
-__device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, u32x4 (*pex)[2][4][64], int wave,
-                                        int lane, int b, int h, int q0) {
+template <int D>
+__global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
   constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
-  const int lr = lane & 31, lg = lane >> 5, pair = wave & 3;
-  const int hk = h / p.group;
+  constexpr int NLD = 2 * (SwTile<D>::RUNS / 8);  // loads per tile per wavefront
+  // Key ring, then value ring; after the loop the start holds the partial dQ^T
+  // exchange (4 pairs x NDB x 16 x 64 floats, at most 64 KB <= the rings' size).
+  __shared__ __attribute__((aligned(16))) u16 tiles[2 * DQ_STAGES * SZ];
+  static_assert(4 * NDB * 16 * 64 * 4 <= 2 * DQ_STAGES * SZ * 2, "exchange must fit in the rings");
+  u16* const k_s = tiles;
+  u16* const v_s = tiles + DQ_STAGES * SZ;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lr = lane & 31, lg = lane >> 5, pair = wave & 3, kh = wave >> 2;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = lin % p.n_qtiles;
+  const int bh = lin / p.n_qtiles;
+  const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
+  // Causal: late query tiles see the most keys; start with them.
+  const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
+  const int q0 = qt * QBM;
   const int qi = q0 + pair * 32 + lr;
   const bool qok = qi < p.Sq;
   const u16* kb = (const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
@@ -330,145 +339,129 @@ __device__ __forceinline__ void dq_role(const BwdParams& p, u16* k_s, u16* v_s, 
   }
   const int n = (kv_end + QBN - 1) / QBN;
 
-  // Register operand (Q rows or dO rows of this lane's query) and statistic.
-  bf16x8 op[NS];
+  bf16x8 qf[NS], dof[NS];
   {
-    const View& src = SW ? p.q : p.dout;
-    const u16* row = (const u16*)src.ptr + (int64_t)b * src.sb + (int64_t)h * src.sh + (int64_t)qi * src.ss + lg * 8;
+    const u16* qrow = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh + (int64_t)qi * p.q.ss + lg * 8;
+    const u16* drow =
+        (const u16*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh + (int64_t)qi * p.dout.ss + lg * 8;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      op[s] = qok ? as_bf16x8(*(const u32x4*)(row + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = qok ? as_bf16x8(*(const u32x4*)(qrow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      dof[s] = qok ? as_bf16x8(*(const u32x4*)(drow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
   }
   // Statistics rows exist up to Sq_pad >= Sq; rows past Sq hold LSE = +inf, delta = 0.
   const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
-  const float stat = SW ? (qi < p.Sq_pad ? stb[qi] : pos_inf()) : (qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f);
+  const float lse2 = qi < p.Sq_pad ? stb[qi] : pos_inf();
+  const float dlt = qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f;
   const float sl2 = p.scale_log2;
   RowFrag<D> rf;
-  rf.init(lane);
   TrFrag<D> tf;
-  if constexpr (!SW) tf.init(lane);
+  rf.init(lane);
+  tf.init(lane);
   // Complete these loads here: left to the compiler, the wait for them sits at
-  // their first use inside the loop, where it would also drain every tile
-  // prefetch in flight on each pass.
+  // their first use inside the loop and drains the tile prefetches there.
   wait_vm<0>();
 
-  f32x16 acc[SW ? 1 : NDB];  // dQ^T (dP wavefront)
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int db = 0; db < (SW ? 1 : NDB); ++db) acc[db] = f32x16{};
-  f32x16 dp_prev[2] = {f32x16{}, f32x16{}};
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  // Tile u into slot u % 3, K and V rows; untracked loads, waited for below.
   auto issue = [&](int tile) {
-    const int slot = tile % 3;
+    const int slot = tile % DQ_STAGES;
     issue_swtile<D, 8, true>(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, wave, lane);
     issue_swtile<D, 8, true>(v_s + slot * SZ, vb, p.v.ss, tile * QBN, p.Sk, wave, lane);
   };
-
   if (n > 0) {
     issue(0);
-    wait_vm<0>();
+    if (n > 1) {
+      issue(1);
+      wait_vm<NLD>();
+    } else {
+      wait_vm<0>();
+    }
     lds_barrier();
   }
-  for (int t = 0; n > 0 && t <= n; ++t) {
-    // Tile t + 1 takes the slot of tile t - 2, last read (by the dP
-    // wavefront, one step behind) before the previous barrier.
-    if (t + 1 < n) issue(t + 1);
-    if constexpr (!SW) {
-      if (t > 0) {
-        // dS for tile t - 1 from the published P and last step's dP, then
-        // dQ^T += K^T dS^T over its four 16-key slabs.
-        const int tp = t - 1;
-        const u16* kt = k_s + (tp % 3) * SZ;
+  for (int t = 0; t < n; ++t) {
+    // Tile t + 2 takes the slot of tile t - 1, which every wavefront finished
+    // before the previous barrier.
+    if (t + 2 < n) issue(t + 2);
+    const u16* kt = k_s + (t % DQ_STAGES) * SZ;
+    const u16* vt = v_s + (t % DQ_STAGES) * SZ;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
-          float ds[8];
+    for (int s = 0; s < NS; ++s) {
+      sc = mfma32(rf.get(kt, kh, s), qf[s], sc);
+      dp = mfma32(rf.get(vt, kh, s), dof[s], dp);
+    }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_prev[ks >> 1][(ks & 1) * 8 + e] - stat);
-          const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-          __builtin_amdgcn_s_setprio(1);
+    for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -lse2));
+    const int key0 = QBN * t + 32 * kh;
+    if (key0 + 32 > full_end) {
+      // Key of register i: key0 + 8(i/4) + 4lg + i%4; hidden when it exceeds
+      // lim64.  The sign of the difference gives a bit mask.
+      const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, 32)) - 4 * lg;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, ks, db), sb, acc[db]);
-          __builtin_amdgcn_s_setprio(0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const unsigned keep = ~(unsigned)((rel - (8 * (i >> 2) + (i & 3))) >> 31);
+        sc[i] = __uint_as_float(__float_as_uint(sc[i]) & keep);
       }
     }
-    if (t < n) {
-      // S^T = K Q^T (S wavefront) or dP^T = V dO^T (dP wavefront): lane =
-      // query, registers = two 32-key blocks.
-      const u16* rows = (SW ? k_s : v_s) + (t % 3) * SZ;
-      f32x16 sc[2] = {f32x16{}, f32x16{}};
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+    for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] - dlt);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) sc[kb2] = mfma32(rf.get(rows, kb2, s), op[s], sc[kb2]);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      if constexpr (SW) {
+    for (int hs = 0; hs < 2; ++hs) {
+      const bf16x8 sb = slab8(sc, hs * 8);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[kb2][i] = exp2_fast(fmaf(sc[kb2][i], sl2, -stat));
-        if (QBN * t + QBN > full_end) {
-          // Key of register i of block kb2: 64t + 32kb2 + 8(i/4) + 4lg + i%4;
-          // hidden when it exceeds lim64.  The sign of the difference gives a
-          // bit mask.
-          const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - QBN * t, QBN)) - 4 * lg;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const unsigned keep = ~(unsigned)((rel - (32 * kb2 + 8 * (i >> 2) + (i & 3))) >> 31);
-              sc[kb2][i] = __uint_as_float(__float_as_uint(sc[kb2][i]) & keep);
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, slab8(sc[ks >> 1], (ks & 1) * 8));
-      } else {
-        dp_prev[0] = sc[0];
-        dp_prev[1] = sc[1];
-      }
+      for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, kh * 2 + hs, db), sb, acc[db]);
     }
-    wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
+    __builtin_amdgcn_s_setprio(0);
+    // Tile t + 1 must have landed before the barrier that starts its step.
+    if (t + 2 < n) wait_vm<NLD>();
+    else wait_vm<0>();
     lds_barrier();
   }
 
-  if constexpr (!SW) {
-    if (!qok) return;
-    float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
-    u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
-                             : nullptr;
+  // Add the pair's two partials: the key-half-1 wavefront hands its dQ^T to
+  // its partner through LDS (the tile ring is free now).
+  float* red = (float*)tiles + pair * (NDB * 16 * 64);
+  if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + j * 8 + lg * 4;
-        f32x4 v = {acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale, acc[db][4 * j + 2] * p.scale,
-                   acc[db][4 * j + 3] * p.scale};
-        if (!p.dq_overwrite) v += *(const f32x4*)(accp + d);
-        *(f32x4*)(accp + d) = v;
-        if (dqp) *(u32x2*)(dqp + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      }
+      for (int i = 0; i < 16; i += 4)
+        *(f32x4*)(red + (db * 16 + i) * 64 + lane * 4) = f32x4{acc[db][i], acc[db][i + 1], acc[db][i + 2], acc[db][i + 3]};
+  }
+  lds_barrier();
+  if (kh == 1 || !qok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const f32x4 o = *(const f32x4*)(red + (db * 16 + i) * 64 + lane * 4);
+      acc[db][i] += o[0];
+      acc[db][i + 1] += o[1];
+      acc[db][i + 2] += o[2];
+      acc[db][i + 3] += o[3];
+    }
+  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
+  u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
+                           : nullptr;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = db * 32 + j * 8 + lg * 4;
+      f32x4 v = {acc[db][4 * j] * p.scale, acc[db][4 * j + 1] * p.scale, acc[db][4 * j + 2] * p.scale,
+                 acc[db][4 * j + 3] * p.scale};
+      if (!p.dq_overwrite) v += *(const f32x4*)(accp + d);
+      *(f32x4*)(accp + d) = v;
+      if (dqp) *(u32x2*)(dqp + d) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
-}
-
-template <int D>
-__global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) u16 k_s[3 * SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u16 v_s[3 * SwTile<D>::SIZE];
-  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];  // [pair][step parity][slab][lane]
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = lin % p.n_qtiles;
-  const int bh = lin / p.n_qtiles;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  // Causal: late query tiles see the most keys; start with them.
-  const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
-  if (wave < 4) dq_role<D, true>(p, k_s, v_s, pex_s, wave, lane, b, h, qt * QBM);
-  else dq_role<D, false>(p, k_s, v_s, pex_s, wave, lane, b, h, qt * QBM);
 }
 
 }  // namespace
