@@ -31,6 +31,8 @@
 // Around each block of matrix products a wavefront raises its issue priority
 // (s_setprio), so that while one wavefront of a SIMD has products ready the
 // matrix core is fed first and its partner's vector work fills the gaps.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 #include "tile_lds.h"
@@ -367,27 +369,34 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  auto issue = [&](int tile) {
-    const int slot = tile % DQ_STAGES;
-    issue_swtile<D, 8, true>(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, wave, lane);
-    issue_swtile<D, 8, true>(v_s + slot * SZ, vb, p.v.ss, tile * QBN, p.Sk, wave, lane);
+  TileSrc<D, 8> ksrc, vsrc;
+  const bool kfast = TileSrc<D, 8>::fits(p.k.ss), vfast = TileSrc<D, 8>::fits(p.v.ss);
+  ksrc.init(p.k.ss, wave, lane);
+  vsrc.init(p.v.ss, wave, lane);
+  auto issue = [&](int tile, int slot) {
+    ksrc.issue(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, kfast, wave, lane);
+    vsrc.issue(v_s + slot * SZ, vb, p.v.ss, tile * QBN, p.Sk, vfast, wave, lane);
   };
   if (n > 0) {
-    issue(0);
+    issue(0, 0);
     if (n > 1) {
-      issue(1);
+      issue(1, 1);
       wait_vm<NLD>();
     } else {
       wait_vm<0>();
     }
     lds_barrier();
   }
-  for (int t = 0; t < n; ++t) {
+  // One step per key tile.  The ring slot is a compile-time constant so that
+  // it folds into the LDS reads' immediate offsets; only tiles that reach past
+  // full_end (the last key every query of the tile sees) apply the mask.
+  auto step = [&](int t, auto slot_c, auto masked_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
     // Tile t + 2 takes the slot of tile t - 1, which every wavefront finished
     // before the previous barrier.
-    if (t + 2 < n) issue(t + 2);
-    const u16* kt = k_s + (t % DQ_STAGES) * SZ;
-    const u16* vt = v_s + (t % DQ_STAGES) * SZ;
+    if (t + 2 < n) issue(t + 2, (SLOT + 2) % DQ_STAGES);
+    const u16* kt = k_s + SLOT * SZ;
+    const u16* vt = v_s + SLOT * SZ;
     f32x16 sc = f32x16{}, dp = f32x16{};
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -398,10 +407,10 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -lse2));
-    const int key0 = QBN * t + 32 * kh;
-    if (key0 + 32 > full_end) {
+    if constexpr (decltype(masked_c)::value) {
       // Key of register i: key0 + 8(i/4) + 4lg + i%4; hidden when it exceeds
       // lim64.  The sign of the difference gives a bit mask.
+      const int key0 = QBN * t + 32 * kh;
       const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, 32)) - 4 * lg;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -423,6 +432,25 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
     if (t + 2 < n) wait_vm<NLD>();
     else wait_vm<0>();
     lds_barrier();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  static_assert(DQ_STAGES == 3, "the loop below is unrolled over three ring slots");
+  // Whole tiles at or below full_end need no mask.
+  const int n_full = min(n, full_end / QBN);
+  int t = 0;
+  for (; t + 3 <= n_full; t += 3) {
+    step(t, I0{}, std::false_type{});
+    step(t + 1, I1{}, std::false_type{});
+    step(t + 2, I2{}, std::false_type{});
+  }
+  // The last few tiles (at most two unmasked ones, then the masked ones).
+  for (; t < n; ++t) {
+    const int slot = t % DQ_STAGES;
+    if (slot == 0) step(t, I0{}, std::true_type{});
+    else if (slot == 1) step(t, I1{}, std::true_type{});
+    else step(t, I2{}, std::true_type{});
   }
 
   // Add the pair's two partials: the key-half-1 wavefront hands its dQ^T to

@@ -89,6 +89,52 @@ __device__ __forceinline__ void issue_swtile(u16* lds, const u16* g, int64_t ss,
   }
 }
 
+// As dma16_untracked, with the source given as a wave-uniform base (held in
+// scalar registers) plus a per-lane 32-bit byte offset: the load adds them
+// itself, so issuing it takes no vector arithmetic.
+__device__ __forceinline__ void dma16_untracked_s(const void* sbase, unsigned voff, lds_void* lds_base,
+                                                  unsigned off = 0) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"((unsigned)(size_t)lds_base), "s"(off)
+               : "memory", "m0", "scc");
+}
+
+// Per-lane byte offsets of the 64-row tile copy (the pattern issue_swtile
+// follows), computed once, so that each later load is the tile's first row
+// (wave-uniform) plus this lane's offset.  Usable while the tile's last byte
+// lies within 4 GiB of its first row (the offsets are 32-bit), which fits()
+// tells; tiles that run past the last row fall back to issue_swtile, which
+// clamps rows.
+template <int D, int NW>
+struct TileSrc {
+  static constexpr int N = SwTile<D>::RUNS / NW;  // loads per wavefront per tile
+  unsigned off[N];
+  __device__ __forceinline__ static bool fits(int64_t ss) { return ss >= 0 && ss <= (int64_t{1} << 24); }
+  __device__ __forceinline__ void init(int64_t ss, int wave, int lane) {
+    using T = SwTile<D>;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int slot = (wave + i * NW) * 64 + lane;
+      const int r = slot / T::CH;
+      off[i] = (unsigned)(((int64_t)r * ss + ((slot % T::CH) ^ swz<D>(r)) * 8) * 2);
+    }
+  }
+  // Copy rows [row0, row0 + 64) of g (row stride ss) into lds, untracked.
+  // fast: fits(ss) held when the offsets were made.
+  __device__ __forceinline__ void issue(u16* lds, const u16* g, int64_t ss, int row0, int nrows, bool fast, int wave,
+                                        int lane) const {
+    if (fast && row0 + 64 <= nrows) {
+      const u16* base = g + (int64_t)row0 * ss;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        dma16_untracked_s(base, off[i], (lds_void*)(lds + i * NW * 512), (unsigned)wave * 1024u);
+    } else {
+      issue_swtile<D, NW, true>(lds, g, ss, row0, nrows, wave, lane);
+    }
+  }
+};
+
 // Per-lane offsets of the row-read operand fragments: row (32*blk + lane%32),
 // logical chunk 2*s + lane/32, for s = 0 .. D/16-1.  The block of 32 rows adds
 // 32*D elements (an immediate), since the swizzle repeats every 16 rows.
