@@ -112,17 +112,30 @@ def bench_main(args, stream):
     (t_f, t_b), wall = time_calls([fwd, bwd], args.steps, args.warmup, stream)
     f_fwd = causal_flops(B, H, S, D)
     f_bwd = 2.5 * f_fwd
-    return {
+    res = {
         "B": B, "H": H, "S": S, "D": D, "fwd_ms": t_f, "bwd_ms": t_b, "step_ms": wall, "event_ms": t_f + t_b,
         "flops_step": f_fwd + f_bwd, "fwd_tflops": f_fwd / t_f / 1e9, "bwd_tflops": f_bwd / t_b / 1e9,
         "tflops": (f_fwd + f_bwd) / wall / 1e9,
     }
+    if args.only is None:
+        # The same calls without the balanced pairing (heaviest tiles first), timed after the
+        # headline steps: the effect of balancing causal work across workgroups.
+        def fwd_u():
+            shard.causal_attention_forward(q, k, v, balanced=False, o=o, lse=lse, stream=stream)
+
+        def bwd_u():
+            shard.causal_attention_backward(q, k, v, o, do, lse, balanced=False, stream=stream, dq=dq, dk=dk, dv=dv,
+                                            dq_acc=dq_acc, workspace=ws)
+
+        (t_fu, t_bu), _ = time_calls([fwd_u, bwd_u], max(2, args.steps // 3), 1, stream)
+        res["unbalanced"] = {"fwd_ms": t_fu, "bwd_ms": t_bu}
+    return res
 
 
 def bench_shard(args, stream, do_bwd):
     import torch
 
-    from exact_blockwise_attention_attn_amd import shard
+    from exact_blockwise_attention_attn_amd import binding, shard
 
     H, D, SQ, SK, CH, QP = 32, 128, 4096, 131072, 4096, 65536
     g = torch.Generator(device="cuda")
@@ -140,13 +153,28 @@ def bench_shard(args, stream, do_bwd):
     def fwd_fused():
         shard.shard_forward_fused(q, k, v, CH, q_pos0=QP, causal=True, stream=stream, lse=lse, o_out=o)
 
+    # The partials-then-merge form: 17 live chunks into stacked fp32 partials, then one merge call.
+    live = [(a, a + CH) for a in range(0, SK, CH) if a <= QP + SQ - 1]
+    o_parts = torch.empty((len(live), 1, SQ, H, D), dtype=torch.float32, device="cuda")
+    lse_parts = torch.empty((len(live), 1, H, SQ), dtype=torch.float32, device="cuda")
+
+    def partials():
+        for i, (a, e) in enumerate(live):
+            binding.attn_fwd_partial(q, k[:, a:e], v[:, a:e], o_parts[i], lse_parts[i], q_pos0=QP, k_pos0=a,
+                                     causal=True, stream=stream)
+
+    def merge():
+        binding.attn_merge_lse(o_parts, lse_parts, o, lse, stream=stream)
+
     f_fwd = 4.0 * SQ * SK * D * H / 2.0  # the stated convention: halved for causal
     if not do_bwd:
-        (t, tf), _ = time_calls([fwd, fwd_fused], max(3, args.steps), 1, stream)
+        (t, tf, tp, tm), _ = time_calls([fwd, fwd_fused, partials, merge], max(3, args.steps), 1, stream)
         return {"workload": "shard_fwd_128k", "ms": t, "tflops": f_fwd / t / 1e9,
-                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": 17,
+                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": len(live),
                 "fused_chunk_table": {"ms": tf, "tflops": f_fwd / tf / 1e9,
-                                      "frac_mfma": f_fwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
+                                      "frac_mfma": f_fwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS},
+                "partials_then_merge": {"partials_ms": tp, "merge_ms": tm, "merge_gbs":
+                                        (len(live) + 0.5) * SQ * H * D * 4 / tm / 1e6}}
     fwd()
     do = randn_bf16((1, SQ, H, D), g)
     dq = torch.empty_like(q)
@@ -280,7 +308,9 @@ def main():
                      "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": BWD_CALL_HBM_BYTES},
         "kernels": {"fwd_call_ms": round(m["fwd_ms"], 3), "bwd_call_ms": round(m["bwd_ms"], 3),
                     "fwd_tflops": round(m["fwd_tflops"], 2), "bwd_tflops": round(m["bwd_tflops"], 2),
-                    "event_ms_per_step": round(m["event_ms"], 3)},
+                    "event_ms_per_step": round(m["event_ms"], 3),
+                    **({"unbalanced_fwd_call_ms": round(m["unbalanced"]["fwd_ms"], 3),
+                        "unbalanced_bwd_call_ms": round(m["unbalanced"]["bwd_ms"], 3)} if "unbalanced" in m else {})},
         "secondary": secondary,
         "cpu_baseline": cpu,
     }
