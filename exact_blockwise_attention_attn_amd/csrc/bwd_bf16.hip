@@ -127,6 +127,9 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
   const int n_qt = (p.Sq + KBM - 1) / KBM;
   const int64_t key_lim = (int64_t)kj - p.delta_pos;  // query index must be >= this (causal)
   const float sl2 = p.scale_log2;
+  // Query tiles before t_mask hold queries that some key of this tile hides
+  // from (i < i_full); only those steps apply the causal mask.
+  const int t_mask = p.causal ? min(n_qt, (i_full + KBM - 1) / KBM) : 0;
 
   for (int hh = 0; hh < p.group; ++hh) {
     const int h = hk * p.group + hh;
@@ -150,7 +153,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
     wait_vm<0>();
     lds_barrier();
     f32x16 dpa[2] = {f32x16{}, f32x16{}}, dpb[2] = {f32x16{}, f32x16{}};
-    auto step = [&](int t, f32x16* dp_in, f32x16* dp_out) {
+    auto step = [&](int t, f32x16* dp_in, f32x16* dp_out, auto masked_c) {
       // Tile t + 1 takes the slot of tile t - 2, last read (by the dS
       // wavefront) before the previous barrier.
       if (t + 1 < n_qt) issue(t + 1);
@@ -182,8 +185,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
               for (int e = 0; e < 4; ++e) sc[qb2][g4 * 4 + e] = exp2_fast(fmaf(sc[qb2][g4 * 4 + e], sl2, -l4[e]));
             }
           }
-          const int i0 = t * KBM;
-          if (p.causal && i0 < i_full) {
+          if constexpr (decltype(masked_c)::value) {
+            const int i0 = t * KBM;
             // Causal mask: query i0 + q is hidden from this lane's key when
             // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a
             // bit mask, which keeps the 32 decisions in vector registers.
@@ -240,10 +243,16 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
       wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
       lds_barrier();
     };
-    for (int t = t_start; t <= n_qt; t += 2) {
-      step(t, dpa, dpb);
-      if (t + 1 > n_qt) break;
-      step(t + 1, dpb, dpa);
+    // Steps go in pairs so that dpa and dpb keep their roles; the masked
+    // pairs come first (masking a tile that needs none keeps every entry).
+    int t = t_start;
+    for (; t <= n_qt && t < t_mask; t += 2) {
+      step(t, dpa, dpb, std::true_type{});
+      if (t + 1 <= n_qt) step(t + 1, dpb, dpa, std::true_type{});
+    }
+    for (; t <= n_qt; t += 2) {
+      step(t, dpa, dpb, std::false_type{});
+      if (t + 1 <= n_qt) step(t + 1, dpb, dpa, std::false_type{});
     }
   }
 

@@ -37,14 +37,6 @@ constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kRescaleSlack = 8.0f;  // exp2 units a row max may grow before O is rescaled
 
-// Issue the global->LDS copy of one 64-row tile of K and of V.
-template <int D>
-__device__ __forceinline__ void issue_tile(u16* ks, u16* vs, const u16* kb, const u16* vb, int64_t k_ss,
-                                           int64_t v_ss, int key0, int Sk, int wave, int lane) {
-  issue_swtile<D, 4>(ks, kb, k_ss, key0, Sk, wave, lane);
-  issue_swtile<D, 4>(vs, vb, v_ss, key0, Sk, wave, lane);
-}
-
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float half_max(float x) {
@@ -170,8 +162,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
                                          int h, const u16* qb, const u16* kb, const u16* vb) {
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lr = lane & 31, lg = lane >> 5;
 
   const int q0 = qt * BM;
   const int qi = q0 + wave * 32 + lr;
@@ -188,7 +180,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
     lim64 = min<int64_t>(p.delta + qi, lim64);
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
-  if (n_tiles > 0) issue_tile<D>(k0s, v0s, kb, vb, p.k.ss, p.v.ss, 0, p.Sk, wave, lane);
+  TileSrc<D, 4> ksrc, vsrc;
+  const bool kfast = TileSrc<D, 4>::fits(p.k.ss), vfast = TileSrc<D, 4>::fits(p.v.ss);
+  ksrc.init(p.k.ss, wave, lane);
+  vsrc.init(p.v.ss, wave, lane);
+  auto issue = [&](u16* ks, u16* vs, int key0) {
+    ksrc.issue(ks, kb, p.k.ss, key0, p.Sk, kfast, wave, lane);
+    vsrc.issue(vs, vb, p.v.ss, key0, p.Sk, vfast, wave, lane);
+  };
+  if (n_tiles > 0) issue(k0s, v0s, 0);
 
   bf16x8 qf[NS];
   {
@@ -210,12 +210,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   for (int t = 0; t < n_tiles; t += 2) {
     wait_loads();
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile<D>(k1s, v1s, kb, vb, p.k.ss, p.v.ss, (t + 1) * BN, p.Sk, wave, lane);
+    if (t + 1 < n_tiles) issue(k1s, v1s, (t + 1) * BN);
     tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf, lane);
     if (t + 1 >= n_tiles) break;
     wait_loads();
     __syncthreads();
-    if (t + 2 < n_tiles) issue_tile<D>(k0s, v0s, kb, vb, p.k.ss, p.v.ss, (t + 2) * BN, p.Sk, wave, lane);
+    if (t + 2 < n_tiles) issue(k0s, v0s, (t + 2) * BN);
     tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, rf, tf, lane);
   }
   __syncthreads();  // the next call of this function reuses the buffers
