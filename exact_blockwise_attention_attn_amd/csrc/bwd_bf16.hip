@@ -40,6 +40,18 @@
 namespace attn {
 namespace {
 
+#ifndef KV_AHEAD
+#define KV_AHEAD 4
+#endif
+#ifndef KV_AHEAD_T
+#define KV_AHEAD_T 2
+#endif
+#ifndef DQ_AHEAD
+#define DQ_AHEAD 4
+#endif
+#ifndef DQ_AHEAD_T
+#define DQ_AHEAD_T 3
+#endif
 constexpr int NT = 256;
 constexpr int KBN = 128;  // keys per dK/dV workgroup
 constexpr int KBM = 64;   // queries per tile in the dK/dV kernel
@@ -164,10 +176,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
         // registers = two 32-query blocks.
         const u16* rows = (PW ? q_s : d_s) + slot * SZ;
         __builtin_amdgcn_s_setprio(1);
+        {
+          // Operand j = 2 si + qb2, read AH ahead of the MFMA that uses it;
+          // the hard scheduling boundaries hold each read in its slot.
+          constexpr int NJ = 2 * NS, AH = KV_AHEAD;
+          bf16x8 f[NJ];
 #pragma unroll
-        for (int si = 0; si < NS; ++si) {
+          for (int j = 0; j < AH; ++j) f[j] = rf.get(rows, j & 1, j >> 1);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int qb2 = 0; qb2 < 2; ++qb2) sc[qb2] = mfma32(rf.get(rows, qb2, si), kv[si], sc[qb2]);
+          for (int j = 0; j < NJ; ++j) {
+            if (j + AH < NJ) f[j + AH] = rf.get(rows, (j + AH) & 1, (j + AH) >> 1);
+            sc[j & 1] = mfma32(f[j], kv[j >> 1], sc[j & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         __builtin_amdgcn_s_setprio(0);
         if constexpr (!PW) {
@@ -204,13 +226,25 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
           // P in bf16, one B operand per 16-query slab: published for the
           // partner and used right away for dV^T += dO^T P.
           const u16* dsrc = d_s + slot * SZ;
-          __builtin_amdgcn_s_setprio(1);
+          bf16x8 pb[4];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 pb = slab8(sc[ks >> 1], (ks & 1) * 8);
-            pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, pb);
+            pb[ks] = slab8(sc[ks >> 1], (ks & 1) * 8);
+            pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, pb[ks]);
+          }
+          __builtin_amdgcn_s_setprio(1);
+          {
+            constexpr int NJ = 4 * NDB, AH = KV_AHEAD_T;
+            bf16x8 f[NJ];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(dsrc, ks, db), pb, acc[db]);
+            for (int j = 0; j < AH; ++j) f[j] = tf.get(dsrc, j / NDB, j % NDB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              if (j + AH < NJ) f[j + AH] = tf.get(dsrc, (j + AH) / NDB, (j + AH) % NDB);
+              acc[j % NDB] = mfma32(f[j], pb[j / NDB], acc[j % NDB]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           __builtin_amdgcn_s_setprio(0);
         }
@@ -222,6 +256,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
           const int tp = t - 1, sp = tp % 3;
           const float* st = st_s[sp];
           const u16* qsrc = q_s + sp * SZ;
+          bf16x8 sbs[4];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
@@ -232,12 +267,23 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
             float ds[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_in[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
-            const bf16x8 sb = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(qsrc, ks, db), sb, acc[db]);
-            __builtin_amdgcn_s_setprio(0);
+            sbs[ks] = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
           }
+          __builtin_amdgcn_s_setprio(1);
+          {
+            constexpr int NJ = 4 * NDB, AH = KV_AHEAD_T;
+            bf16x8 f[NJ];
+#pragma unroll
+            for (int j = 0; j < AH; ++j) f[j] = tf.get(qsrc, j / NDB, j % NDB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              if (j + AH < NJ) f[j + AH] = tf.get(qsrc, (j + AH) / NDB, (j + AH) % NDB);
+              acc[j % NDB] = mfma32(f[j], sbs[j / NDB], acc[j % NDB]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
@@ -408,10 +454,22 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
     const u16* vt = v_s + SLOT * SZ;
     f32x16 sc = f32x16{}, dp = f32x16{};
     __builtin_amdgcn_s_setprio(1);
+    {
+      // Operand j: key rows (even j) or value rows (odd j) of slab j/2, read
+      // AH ahead of the MFMA that uses them; the hard scheduling boundaries
+      // hold each read in its slot.
+      constexpr int NJ = 2 * NS, AH = DQ_AHEAD;
+      bf16x8 f[NJ];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sc = mfma32(rf.get(kt, kh, s), qf[s], sc);
-      dp = mfma32(rf.get(vt, kh, s), dof[s], dp);
+      for (int j = 0; j < AH; ++j) f[j] = rf.get((j & 1) ? vt : kt, kh, j >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + AH < NJ) f[j + AH] = rf.get(((j + AH) & 1) ? vt : kt, kh, (j + AH) >> 1);
+        if (j & 1) dp = mfma32(f[j], dof[j >> 1], dp);
+        else sc = mfma32(f[j], qf[j >> 1], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -429,12 +487,20 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] - dlt);
+    const bf16x8 sb[2] = {slab8(sc, 0), slab8(sc, 8)};
     __builtin_amdgcn_s_setprio(1);
+    {
+      constexpr int NJ = 2 * NDB, AH = DQ_AHEAD_T;
+      bf16x8 f[NJ];
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const bf16x8 sb = slab8(sc, hs * 8);
+      for (int j = 0; j < AH; ++j) f[j] = tf.get(kt, kh * 2 + j / NDB, j % NDB);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = mfma32(tf.get(kt, kh * 2 + hs, db), sb, acc[db]);
+      for (int j = 0; j < NJ; ++j) {
+        if (j + AH < NJ) f[j + AH] = tf.get(kt, kh * 2 + (j + AH) / NDB, (j + AH) % NDB);
+        acc[j % NDB] = mfma32(f[j], sb[j / NDB], acc[j % NDB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     // Tile t + 1 must have landed before the barrier that starts its step.

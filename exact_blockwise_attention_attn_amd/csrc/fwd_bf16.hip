@@ -35,6 +35,12 @@ namespace {
 constexpr int BM = 128;  // queries per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup
+#ifndef SB_AHEAD_PV
+#define SB_AHEAD_PV 3
+#endif
+#ifndef SB_AHEAD
+#define SB_AHEAD 4
+#endif
 constexpr float kRescaleSlack = 8.0f;  // exp2 units a row max may grow before O is rescaled
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
@@ -62,11 +68,19 @@ __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf
   const int lr = lane & 31, lg = lane >> 5;
 
   f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  {
+    // Operand j = 2s + kb2.  Keep AH reads in flight ahead of the MFMA that
+    // uses them: the hard scheduling boundaries hold each read in its slot.
+    constexpr int NJ = 2 * NS, AH = SB_AHEAD;
+    bf16x8 kf[NJ];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+    for (int j = 0; j < AH; ++j) kf[j] = rf.get(ks, j & 1, j >> 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = mfma32(rf.get(ks, kb2, s), qf[s], sacc[kb2]);
+    for (int j = 0; j < NJ; ++j) {
+      if (j + AH < NJ) kf[j + AH] = rf.get(ks, (j + AH) & 1, (j + AH) >> 1);
+      sacc[j & 1] = mfma32(kf[j], qf[j >> 1], sacc[j & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (need_mask) {
@@ -111,13 +125,26 @@ __device__ __forceinline__ void tile_step(const u16* ks, const u16* vs, const bf
   st.l += rs;
 
   // O^T += V^T P^T over four 16-key slabs; V^T comes from the transposing read.
+  bf16x8 pb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int kb2 = ks >> 1, o = (ks & 1) * 8;
-    const bf16x8 pb = cvt_bf16x8(sacc[kb2][o + 0], sacc[kb2][o + 1], sacc[kb2][o + 2], sacc[kb2][o + 3],
-                                 sacc[kb2][o + 4], sacc[kb2][o + 5], sacc[kb2][o + 6], sacc[kb2][o + 7]);
+    pb[ks] = cvt_bf16x8(sacc[kb2][o + 0], sacc[kb2][o + 1], sacc[kb2][o + 2], sacc[kb2][o + 3],
+                        sacc[kb2][o + 4], sacc[kb2][o + 5], sacc[kb2][o + 6], sacc[kb2][o + 7]);
+  }
+  {
+    // Operand j = NDB ks + db, read AH fragments ahead as for the scores.
+    constexpr int NJ = 4 * NDB, AH = SB_AHEAD_PV;
+    bf16x8 vf[NJ];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(tf.get(vs, ks, db), pb, oacc[db]);
+    for (int j = 0; j < AH; ++j) vf[j] = tf.get(vs, j / NDB, j % NDB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + AH < NJ) vf[j + AH] = tf.get(vs, (j + AH) / NDB, (j + AH) % NDB);
+      oacc[j % NDB] = mfma32(vf[j], pb[j / NDB], oacc[j % NDB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
