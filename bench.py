@@ -186,10 +186,16 @@ def bench_shard(args, stream, do_bwd):
         shard.shard_backward(q, k, v, o, do, lse, CH, q_pos0=QP, causal=True, stream=stream, dq=dq, dk=dk, dv=dv,
                              dq_acc=dq_acc, workspace=ws)
 
-    (t,), _ = time_calls([bwd], max(3, args.steps), 1, stream)
+    def bwd_fused():
+        shard.shard_backward_fused(q, k, v, o, do, lse, CH, q_pos0=QP, causal=True, stream=stream, dq=dq, dk=dk,
+                                   dv=dv, dq_acc=dq_acc, workspace=ws)
+
+    (t, tf), _ = time_calls([bwd, bwd_fused], max(3, args.steps), 1, stream)
     f_bwd = 2.5 * f_fwd
     return {"workload": "shard_bwd_128k", "ms": t, "tflops": f_bwd / t / 1e9,
-            "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+            "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "fused_chunk_table": {"ms": tf, "tflops": f_bwd / tf / 1e9,
+                                  "frac_mfma": f_bwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
 
 
 def bench_decode(args, stream):

@@ -106,6 +106,27 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class BwdChunksArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("dtype", c_u32),
+        ("batch", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32), ("seqlen_q", c_i32), ("head_dim", c_i32),
+        ("n_chunks", c_i32),
+        ("q", c_vp), ("q_stride", I64x3),
+        ("o", c_vp), ("o_stride", I64x3),
+        ("dout", c_vp), ("do_stride", I64x3),
+        ("lse", c_vp), ("workspace", c_vp), ("workspace_bytes", ctypes.c_size_t), ("dq_acc", c_vp),
+        ("dq", c_vp), ("dq_stride", I64x3),
+        ("k_chunks", ctypes.POINTER(c_vp)), ("v_chunks", ctypes.POINTER(c_vp)),
+        ("dk_chunks", ctypes.POINTER(c_vp)), ("dv_chunks", ctypes.POINTER(c_vp)),
+        ("chunk_len", ctypes.POINTER(c_i32)), ("chunk_pos0", ctypes.POINTER(c_i64)),
+        ("k_stride", I64x3), ("v_stride", I64x3), ("dk_stride", I64x3), ("dv_stride", I64x3),
+        ("chunk_k_bstride", ctypes.POINTER(c_i64)), ("chunk_v_bstride", ctypes.POINTER(c_i64)),
+        ("chunk_dk_bstride", ctypes.POINTER(c_i64)), ("chunk_dv_bstride", ctypes.POINTER(c_i64)),
+        ("q_pos0", c_i64),
+        ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+    ]
+
+
 class DecodeArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_u32),
@@ -126,6 +147,7 @@ EXPORTED = [
     "attn_fwd_chunks",
     "attn_merge_lse",
     "attn_bwd",
+    "attn_bwd_chunks",
     "attn_decode_splitkv",
     "attn_bwd_workspace_size",
     "attn_decode_workspace_size",
@@ -164,6 +186,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                            ("attn_fwd_chunks", [ctypes.POINTER(FwdChunksArgs), c_vp]),
                            ("attn_merge_lse", [ctypes.POINTER(MergeArgs), c_vp]),
                            ("attn_bwd", [ctypes.POINTER(BwdArgs), c_vp]),
+                           ("attn_bwd_chunks", [ctypes.POINTER(BwdChunksArgs), c_vp]),
                            ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp])):
             fn = getattr(lib, name)
             fn.argtypes = argt
@@ -337,6 +360,54 @@ def attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, *, dq=None, q_pos
     a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
                | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
     _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
+
+
+def _chunk_strides(ts, what):
+    """Shared (batch, seq, head) strides of the non-empty chunks, and a host array of per-chunk batch strides."""
+    n = len(ts)
+    live = [x for x in ts if x.shape[1] > 0]
+    st = _strides3(live[0]) if live else I64x3(0, 0, 0)
+    for x in live:
+        assert tuple(x.stride()[1:3]) == tuple(st)[1:], f"{what} chunks must share sequence and head strides"
+    bs = (c_i64 * max(n, 1))(*[x.stride(0) if x.numel() else 0 for x in ts])
+    return st, bs
+
+
+def attn_bwd_chunks(q, k_chunks, v_chunks, o, dout, lse, workspace, dq_acc, dk_chunks, dv_chunks, *,
+                    chunk_pos0, dq=None, q_pos0=0, causal=False, scale=0.0, compute_delta=False,
+                    dq_overwrite=False, finalize_dq=False, balanced=False, stream=None) -> None:
+    """Backward of q over a list of key/value chunks ([B, len_c, Hkv, D] bf16 each), dK/dV per chunk; see include/attn.h."""
+    n = len(k_chunks)
+    assert len(v_chunks) == n and len(dk_chunks) == n and len(dv_chunks) == n and len(chunk_pos0) == n
+    for k, v, dk, dv in zip(k_chunks, v_chunks, dk_chunks, dv_chunks):
+        assert k.shape == v.shape == dk.shape == dv.shape, "chunk tensors and their gradients must match in shape"
+    a = BwdChunksArgs()
+    a.struct_size = ctypes.sizeof(BwdChunksArgs)
+    a.dtype = _dtype_code(q)
+    a.batch, a.seqlen_q, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k_chunks[0].shape[2] if n else q.shape[2]
+    a.n_chunks = n
+    a.q, a.q_stride = _ptr(q), _strides3(q)
+    a.o, a.o_stride = _ptr(o), _strides3(o)
+    a.dout, a.do_stride = _ptr(dout), _strides3(dout)
+    a.lse, a.dq_acc = _ptr(lse), _ptr(dq_acc)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.dq, a.dq_stride = _ptr(dq), _strides3(dq)
+    arr = lambda ts: (c_vp * max(n, 1))(*[_ptr(x) for x in ts])  # noqa: E731
+    a.k_chunks, a.v_chunks, a.dk_chunks, a.dv_chunks = arr(k_chunks), arr(v_chunks), arr(dk_chunks), arr(dv_chunks)
+    a.chunk_len = (c_i32 * max(n, 1))(*[k.shape[1] for k in k_chunks])
+    a.chunk_pos0 = (c_i64 * max(n, 1))(*[int(x) for x in chunk_pos0])
+    a.k_stride, a.chunk_k_bstride = _chunk_strides(k_chunks, "key")
+    a.v_stride, a.chunk_v_bstride = _chunk_strides(v_chunks, "value")
+    a.dk_stride, a.chunk_dk_bstride = _chunk_strides(dk_chunks, "dk")
+    a.dv_stride, a.chunk_dv_bstride = _chunk_strides(dv_chunks, "dv")
+    a.q_pos0 = int(q_pos0)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+    _check(load().attn_bwd_chunks(ctypes.byref(a), _stream(stream)))
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seqlens=None, scale=0.0,

@@ -357,6 +357,111 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   return ok();
 }
 
+int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_bwd_chunks_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_bwd_chunks_args));
+  if (a->dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported (bf16 only)", a->dtype);
+  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED;
+  if (a->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
+  if (a->n_chunks < 0 || a->n_chunks > ATTN_MAX_CHUNKS)
+    return fail(ATTN_ERR_INVALID_ARG, "n_chunks must be in [0, %d]", ATTN_MAX_CHUNKS);
+  TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, 0, a->head_dim));
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  const bool has_q = a->seqlen_q > 0;
+  const bool finalize = a->flags & ATTN_BWD_FINALIZE_DQ;
+  TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
+  TRY(check_view("o", a->o, a->o_stride, 3, a->dtype, has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)));
+  TRY(check_view("dout", a->dout, a->do_stride, 3, a->dtype, has_q));
+  TRY(check_view("dq", a->dq, a->dq_stride, 3, a->dtype, has_q && finalize));
+  if (has_q && (!a->lse || !a->dq_acc)) return fail(ATTN_ERR_INVALID_ARG, "lse and dq_acc must not be NULL");
+  if (has_q && (!aligned16(a->lse) || !aligned16(a->dq_acc)))
+    return fail(ATTN_ERR_UNSUPPORTED, "lse and dq_acc must be 16-byte aligned");
+  if (has_q) {
+    const size_t need = attn_bwd_workspace_size(a->batch, a->heads_q, a->seqlen_q);
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if ((uintptr_t)a->workspace & 255u) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  if (a->n_chunks > 0 && (!a->k_chunks || !a->v_chunks || !a->dk_chunks || !a->dv_chunks || !a->chunk_len ||
+                          !a->chunk_pos0))
+    return fail(ATTN_ERR_INVALID_ARG, "chunk arrays must not be NULL");
+  attn::BwdChunkTable ct{};
+  ct.kv.q_pos0 = a->q_pos0;
+  int64_t key_tiles = 0;
+  for (int c = 0; c < a->n_chunks; ++c) {
+    if (a->chunk_len[c] < 0) return fail(ATTN_ERR_INVALID_ARG, "chunk_len[%d] is negative", c);
+    if (a->chunk_len[c] == 0) continue;
+    auto bs = [&](const int64_t* arr, const int64_t* st) { return arr ? arr[c] : st[0]; };
+    const int64_t ks[3] = {bs(a->chunk_k_bstride, a->k_stride), a->k_stride[1], a->k_stride[2]};
+    const int64_t vs[3] = {bs(a->chunk_v_bstride, a->v_stride), a->v_stride[1], a->v_stride[2]};
+    const int64_t dks[3] = {bs(a->chunk_dk_bstride, a->dk_stride), a->dk_stride[1], a->dk_stride[2]};
+    const int64_t dvs[3] = {bs(a->chunk_dv_bstride, a->dv_stride), a->dv_stride[1], a->dv_stride[2]};
+    char name[32];
+    snprintf(name, sizeof name, "k_chunks[%d]", c);
+    TRY(check_view(name, a->k_chunks[c], ks, 3, a->dtype, true));
+    snprintf(name, sizeof name, "v_chunks[%d]", c);
+    TRY(check_view(name, a->v_chunks[c], vs, 3, a->dtype, true));
+    snprintf(name, sizeof name, "dk_chunks[%d]", c);
+    TRY(check_view(name, a->dk_chunks[c], dks, 3, a->dtype, true));
+    snprintf(name, sizeof name, "dv_chunks[%d]", c);
+    TRY(check_view(name, a->dv_chunks[c], dvs, 3, a->dtype, true));
+    ct.kv.k[ct.kv.n] = a->k_chunks[c];
+    ct.kv.v[ct.kv.n] = a->v_chunks[c];
+    ct.kv.kb[ct.kv.n] = ks[0];
+    ct.kv.vb[ct.kv.n] = vs[0];
+    ct.kv.len[ct.kv.n] = a->chunk_len[c];
+    ct.kv.pos0[ct.kv.n] = a->chunk_pos0[c];
+    ct.dk[ct.kv.n] = a->dk_chunks[c];
+    ct.dv[ct.kv.n] = a->dv_chunks[c];
+    ct.dkb[ct.kv.n] = dks[0];
+    ct.dvb[ct.kv.n] = dvs[0];
+    ++ct.kv.n;
+    key_tiles += (a->chunk_len[c] + 63) / 64;
+  }
+  const int64_t units = (int64_t)a->batch * a->heads_q * ((a->seqlen_q + 63) / 64) +
+                        (int64_t)a->batch * a->heads_kv * key_tiles;
+  if (units > 0x7fffffffLL) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  attn::BwdParams p{};
+  p.q = view(a->q, a->q_stride);
+  p.k = view(nullptr, a->k_stride);
+  p.v = view(nullptr, a->v_stride);
+  p.o = view(a->o, a->o_stride);
+  p.dout = view(a->dout, a->do_stride);
+  p.dq = mview(a->dq, a->dq_stride);
+  p.dk = mview(nullptr, a->dk_stride);
+  p.dv = mview(nullptr, a->dv_stride);
+  p.lse = a->lse;
+  p.stats = (float*)a->workspace;
+  p.Sq_pad = (a->seqlen_q + 63) / 64 * 64;
+  p.dq_acc = a->dq_acc;
+  p.B = a->batch;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.Sq = a->seqlen_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.causal = a->causal != 0;
+  p.dq_overwrite = (a->flags & ATTN_BWD_DQ_OVERWRITE) != 0;
+  p.finalize_dq = finalize;
+  p.balanced = (a->flags & ATTN_BWD_BALANCED) != 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)) {
+    e = attn::launch_bwd_prepare(p, a->head_dim, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunks prepare launch");
+  }
+  // Without queries the dK/dV kernel writes zeros for every chunk and no dQ pass runs.
+  e = attn::launch_bwd_chunks_bf16(p, ct, a->head_dim, s);
+  if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunks launch");
+  return ok();
+}
+
 size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
   if (batch < 1 || heads_q < 1 || seqlen_q < 0) return 0;
   const size_t sq_pad = ((size_t)seqlen_q + 63) / 64 * 64;

@@ -84,6 +84,20 @@ struct BwdParams {
   int n_qtiles, n_ktiles, n_units_k;  // filled in by the launchers
 };
 
+// Key/value chunks of a fused multi-chunk backward: the forward's chunk table
+// (keys, values, positions, lengths) plus each chunk's dK and dV outputs, with
+// batch strides dkb[c], dvb[c] and the sequence and head strides of
+// BwdParams::dk and BwdParams::dv.  unit0[c] is the first dK/dV work unit of
+// chunk c (a prefix sum over the chunks); n_units is the total.
+struct BwdChunkTable {
+  ChunkTable kv;
+  void* dk[kMaxChunks];
+  void* dv[kMaxChunks];
+  int64_t dkb[kMaxChunks], dvb[kMaxChunks];
+  int unit0[kMaxChunks + 1];
+  int n_units;
+};
+
 struct DecodeParams {
   const uint16_t* q;
   int64_t q_sb, q_sh;
@@ -117,6 +131,10 @@ hipError_t launch_merge(const MergeParams& p, int D, hipStream_t s);
 // visible.
 hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, int run_dq, hipStream_t s);
+// dK/dV of every chunk of the table and dQ over all of them, in two launches.
+// p supplies everything but the key/value tensors and their outputs; p.Sk and
+// p.delta_pos are ignored.  The table's unit0 and n_units are filled in here.
+hipError_t launch_bwd_chunks_bf16(const BwdParams& p, const BwdChunkTable& ct, int D, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int D, int run_dq, hipStream_t s);
 // Decode: split partials into the workspace, then the per-(b, h) tree merge.
 hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s);

@@ -350,6 +350,39 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
   else dkdv_unit<D, false>(p, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
 }
 
+// The same over the chunks of a table: work unit u of the whole grid belongs
+// to the chunk c with unit0[c] <= u < unit0[c + 1], and runs with that chunk's
+// key/value tensors, dK/dV outputs, length and position.
+template <int D>
+__global__ __launch_bounds__(DKV_NT) void dkdv_chunks_kernel(BwdParams p, BwdChunkTable ct) {
+  __shared__ __attribute__((aligned(16))) u16 q_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) float st_s[3][256];
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int gunit = lin % ct.n_units;
+  const int bh = lin / ct.n_units;
+  const int hk = bh % p.Hkv, b = bh / p.Hkv;
+  int c = 0;
+  while (c + 1 < ct.kv.n && ct.unit0[c + 1] <= gunit) ++c;
+  BwdParams pc = p;
+  pc.k.ptr = ct.kv.k[c];
+  pc.k.sb = ct.kv.kb[c];
+  pc.v.ptr = ct.kv.v[c];
+  pc.v.sb = ct.kv.vb[c];
+  pc.dk.ptr = ct.dk[c];
+  pc.dk.sb = ct.dkb[c];
+  pc.dv.ptr = ct.dv[c];
+  pc.dv.sb = ct.dvb[c];
+  pc.Sk = ct.kv.len[c];
+  pc.delta_pos = ct.kv.q_pos0 - ct.kv.pos0[c];
+  pc.n_ktiles = (pc.Sk + KBN - 1) / KBN;
+  const int unit = gunit - ct.unit0[c];
+  if (wave < 4) dkdv_unit<D, true>(pc, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
+  else dkdv_unit<D, false>(pc, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
+}
+
 // --------------------------------------------------------------------- dQ --
 //
 // Eight wavefronts in four pairs; pair w%4 owns queries q0 + 32*(w%4) .. +31
@@ -363,8 +396,18 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
 constexpr int DQ_NT = 512;
 constexpr int DQ_STAGES = 3;
 
-template <int D>
-__global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
+// The keys of a dQ pass come in segments (one tensor, or the chunks of a
+// table); seg(c, b, hk) gives segment c's key and value rows for (b, hk), its
+// length and the offset of the query positions from its key positions.
+struct KeySeg {
+  const u16* kb;
+  const u16* vb;
+  int Sk;
+  int64_t delta_pos;
+};
+
+template <int D, class Seg>
+__device__ __forceinline__ void dq_body(const BwdParams& p, int n_seg, Seg seg) {
   constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
   constexpr int NLD = 2 * (SwTile<D>::RUNS / 8);  // loads per tile per wavefront
   // Key ring, then value ring; after the loop the start holds the partial dQ^T
@@ -384,17 +427,7 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
   const int q0 = qt * QBM;
   const int qi = q0 + pair * 32 + lr;
   const bool qok = qi < p.Sq;
-  const u16* kb = (const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
-  const u16* vb = (const u16*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
   const int q_last = min(q0 + QBM, p.Sq) - 1;
-  int kv_end = p.Sk, full_end = p.Sk;
-  int64_t lim64 = (int64_t)p.Sk - 1;  // last key this lane's query sees
-  if (p.causal) {
-    kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q_last + 1, p.Sk));
-    full_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q0 + 1, p.Sk));
-    lim64 = min<int64_t>(p.delta_pos + qi, lim64);
-  }
-  const int n = (kv_end + QBN - 1) / QBN;
 
   bf16x8 qf[NS], dof[NS];
   {
@@ -428,104 +461,119 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
   const bool kfast = TileSrc<D, 8>::fits(p.k.ss), vfast = TileSrc<D, 8>::fits(p.v.ss);
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
-  auto issue = [&](int tile, int slot) {
-    ksrc.issue(k_s + slot * SZ, kb, p.k.ss, tile * QBN, p.Sk, kfast, wave, lane);
-    vsrc.issue(v_s + slot * SZ, vb, p.v.ss, tile * QBN, p.Sk, vfast, wave, lane);
-  };
-  if (n > 0) {
-    issue(0, 0);
-    if (n > 1) {
-      issue(1, 1);
-      wait_vm<NLD>();
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();
-  }
-  // One step per key tile.  The ring slot is a compile-time constant so that
-  // it folds into the LDS reads' immediate offsets; only tiles that reach past
-  // full_end (the last key every query of the tile sees) apply the mask.
-  auto step = [&](int t, auto slot_c, auto masked_c) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    // Tile t + 2 takes the slot of tile t - 1, which every wavefront finished
-    // before the previous barrier.
-    if (t + 2 < n) issue(t + 2, (SLOT + 2) % DQ_STAGES);
-    const u16* kt = k_s + SLOT * SZ;
-    const u16* vt = v_s + SLOT * SZ;
-    f32x16 sc = f32x16{}, dp = f32x16{};
-    __builtin_amdgcn_s_setprio(1);
-    {
-      // Operand j: key rows (even j) or value rows (odd j) of slab j/2, read
-      // AH ahead of the MFMA that uses them; the hard scheduling boundaries
-      // hold each read in its slot.
-      constexpr int NJ = 2 * NS, AH = DQ_AHEAD;
-      bf16x8 f[NJ];
-#pragma unroll
-      for (int j = 0; j < AH; ++j) f[j] = rf.get((j & 1) ? vt : kt, kh, j >> 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (j + AH < NJ) f[j + AH] = rf.get(((j + AH) & 1) ? vt : kt, kh, (j + AH) >> 1);
-        if (j & 1) dp = mfma32(f[j], dof[j >> 1], dp);
-        else sc = mfma32(f[j], qf[j >> 1], sc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -lse2));
-    if constexpr (decltype(masked_c)::value) {
-      // Key of register i: key0 + 8(i/4) + 4lg + i%4; hidden when it exceeds
-      // lim64.  The sign of the difference gives a bit mask.
-      const int key0 = QBN * t + 32 * kh;
-      const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, 32)) - 4 * lg;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const unsigned keep = ~(unsigned)((rel - (8 * (i >> 2) + (i & 3))) >> 31);
-        sc[i] = __uint_as_float(__float_as_uint(sc[i]) & keep);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] - dlt);
-    const bf16x8 sb[2] = {slab8(sc, 0), slab8(sc, 8)};
-    __builtin_amdgcn_s_setprio(1);
-    {
-      constexpr int NJ = 2 * NDB, AH = DQ_AHEAD_T;
-      bf16x8 f[NJ];
-#pragma unroll
-      for (int j = 0; j < AH; ++j) f[j] = tf.get(kt, kh * 2 + j / NDB, j % NDB);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (j + AH < NJ) f[j + AH] = tf.get(kt, kh * 2 + (j + AH) / NDB, (j + AH) % NDB);
-        acc[j % NDB] = mfma32(f[j], sb[j / NDB], acc[j % NDB]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // Tile t + 1 must have landed before the barrier that starts its step.
-    if (t + 2 < n) wait_vm<NLD>();
-    else wait_vm<0>();
-    lds_barrier();
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   static_assert(DQ_STAGES == 3, "the loop below is unrolled over three ring slots");
-  // Whole tiles at or below full_end need no mask.
-  const int n_full = min(n, full_end / QBN);
-  int t = 0;
-  for (; t + 3 <= n_full; t += 3) {
-    step(t, I0{}, std::false_type{});
-    step(t + 1, I1{}, std::false_type{});
-    step(t + 2, I2{}, std::false_type{});
-  }
-  // The last few tiles (at most two unmasked ones, then the masked ones).
-  for (; t < n; ++t) {
-    const int slot = t % DQ_STAGES;
-    if (slot == 0) step(t, I0{}, std::true_type{});
-    else if (slot == 1) step(t, I1{}, std::true_type{});
-    else step(t, I2{}, std::true_type{});
+
+  // dQ accumulates in registers over every segment.  A segment's last step
+  // waits for all its loads and ends with a barrier, so the next segment may
+  // refill the ring from slot 0.
+  for (int c = 0; c < n_seg; ++c) {
+    const KeySeg sg = seg(c, b, hk);
+    int kv_end = sg.Sk, full_end = sg.Sk;
+    int64_t lim64 = (int64_t)sg.Sk - 1;  // last key of the segment this lane's query sees
+    if (p.causal) {
+      kv_end = (int)max<int64_t>(0, min<int64_t>(sg.delta_pos + q_last + 1, sg.Sk));
+      full_end = (int)max<int64_t>(0, min<int64_t>(sg.delta_pos + q0 + 1, sg.Sk));
+      lim64 = min<int64_t>(sg.delta_pos + qi, lim64);
+    }
+    const int n = (kv_end + QBN - 1) / QBN;
+    auto issue = [&](int tile, int slot) {
+      ksrc.issue(k_s + slot * SZ, sg.kb, p.k.ss, tile * QBN, sg.Sk, kfast, wave, lane);
+      vsrc.issue(v_s + slot * SZ, sg.vb, p.v.ss, tile * QBN, sg.Sk, vfast, wave, lane);
+    };
+    if (n > 0) {
+      issue(0, 0);
+      if (n > 1) {
+        issue(1, 1);
+        wait_vm<NLD>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();
+    }
+    // One step per key tile.  The ring slot is a compile-time constant so that
+    // it folds into the LDS reads' immediate offsets; only tiles that reach past
+    // full_end (the last key every query of the tile sees) apply the mask.
+    auto step = [&](int t, auto slot_c, auto masked_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      // Tile t + 2 takes the slot of tile t - 1, which every wavefront finished
+      // before the previous barrier.
+      if (t + 2 < n) issue(t + 2, (SLOT + 2) % DQ_STAGES);
+      const u16* kt = k_s + SLOT * SZ;
+      const u16* vt = v_s + SLOT * SZ;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+      __builtin_amdgcn_s_setprio(1);
+      {
+        // Operand j: key rows (even j) or value rows (odd j) of slab j/2, read
+        // AH ahead of the MFMA that uses them; the hard scheduling boundaries
+        // hold each read in its slot.
+        constexpr int NJ = 2 * NS, AH = DQ_AHEAD;
+        bf16x8 f[NJ];
+#pragma unroll
+        for (int j = 0; j < AH; ++j) f[j] = rf.get((j & 1) ? vt : kt, kh, j >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (j + AH < NJ) f[j + AH] = rf.get(((j + AH) & 1) ? vt : kt, kh, (j + AH) >> 1);
+          if (j & 1) dp = mfma32(f[j], dof[j >> 1], dp);
+          else sc = mfma32(f[j], qf[j >> 1], sc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(fmaf(sc[i], sl2, -lse2));
+      if constexpr (decltype(masked_c)::value) {
+        // Key of register i: key0 + 8(i/4) + 4lg + i%4; hidden when it exceeds
+        // lim64.  The sign of the difference gives a bit mask.
+        const int key0 = QBN * t + 32 * kh;
+        const int rel = (int)max<int64_t>(-1, min<int64_t>(lim64 - key0, 32)) - 4 * lg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const unsigned keep = ~(unsigned)((rel - (8 * (i >> 2) + (i & 3))) >> 31);
+          sc[i] = __uint_as_float(__float_as_uint(sc[i]) & keep);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] - dlt);
+      const bf16x8 sb[2] = {slab8(sc, 0), slab8(sc, 8)};
+      __builtin_amdgcn_s_setprio(1);
+      {
+        constexpr int NJ = 2 * NDB, AH = DQ_AHEAD_T;
+        bf16x8 f[NJ];
+#pragma unroll
+        for (int j = 0; j < AH; ++j) f[j] = tf.get(kt, kh * 2 + j / NDB, j % NDB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (j + AH < NJ) f[j + AH] = tf.get(kt, kh * 2 + (j + AH) / NDB, (j + AH) % NDB);
+          acc[j % NDB] = mfma32(f[j], sb[j / NDB], acc[j % NDB]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // Tile t + 1 must have landed before the barrier that starts its step.
+      if (t + 2 < n) wait_vm<NLD>();
+      else wait_vm<0>();
+      lds_barrier();
+    };
+    // Whole tiles at or below full_end need no mask.
+    const int n_full = min(n, full_end / QBN);
+    int t = 0;
+    for (; t + 3 <= n_full; t += 3) {
+      step(t, I0{}, std::false_type{});
+      step(t + 1, I1{}, std::false_type{});
+      step(t + 2, I2{}, std::false_type{});
+    }
+    // The last few tiles (at most two unmasked ones, then the masked ones).
+    for (; t < n; ++t) {
+      const int slot = t % DQ_STAGES;
+      if (slot == 0) step(t, I0{}, std::true_type{});
+      else if (slot == 1) step(t, I1{}, std::true_type{});
+      else step(t, I2{}, std::true_type{});
+    }
   }
 
   // Add the pair's two partials: the key-half-1 wavefront hands its dQ^T to
@@ -567,6 +615,23 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
+  dq_body<D>(p, 1, [&](int, int b, int hk) {
+    return KeySeg{(const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh,
+                  (const u16*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh, p.Sk, p.delta_pos};
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(DQ_NT) void dq_chunks_kernel(BwdParams p, BwdChunkTable ct) {
+  dq_body<D>(p, ct.kv.n, [&](int c, int b, int hk) {
+    return KeySeg{(const u16*)ct.kv.k[c] + (int64_t)b * ct.kv.kb[c] + (int64_t)hk * p.k.sh,
+                  (const u16*)ct.kv.v[c] + (int64_t)b * ct.kv.vb[c] + (int64_t)hk * p.v.sh, ct.kv.len[c],
+                  ct.kv.q_pos0 - ct.kv.pos0[c]};
+  });
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s) {
@@ -589,6 +654,38 @@ hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s
       hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
     else
       hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_chunks_bf16(const BwdParams& p0, const BwdChunkTable& ct0, int D, hipStream_t s) {
+  BwdParams p = p0;
+  BwdChunkTable ct = ct0;
+  int units = 0;
+  for (int c = 0; c < ct.kv.n; ++c) {
+    ct.unit0[c] = units;
+    const int nk = (ct.kv.len[c] + KBN - 1) / KBN;
+    units += p.balanced ? (nk + 1) / 2 : nk;
+  }
+  ct.unit0[ct.kv.n] = units;
+  ct.n_units = units;
+  p.n_qtiles = (p.Sq + QBM - 1) / QBM;
+  const int64_t gk = (int64_t)p.B * p.Hkv * units;
+  if (gk > 0) {
+    if (D == 128)
+      hipLaunchKernelGGL(dkdv_chunks_kernel<128>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p, ct);
+    else
+      hipLaunchKernelGGL(dkdv_chunks_kernel<64>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p, ct);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
+  if (gq > 0) {
+    if (D == 128)
+      hipLaunchKernelGGL(dq_chunks_kernel<128>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p, ct);
+    else
+      hipLaunchKernelGGL(dq_chunks_kernel<64>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p, ct);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -122,6 +122,30 @@ def shard_backward(q, k, v, o, dout, lse, chunk, *, q_pos0=0, k_pos0=0, causal=F
     return dq, dk, dv
 
 
+def shard_backward_fused(q, k, v, o, dout, lse, chunk, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0,
+                         stream=None, dq=None, dk=None, dv=None, dq_acc=None, workspace=None):
+    """The same gradients as shard_backward from one call over the chunk table (bf16 only).
+
+    k, v, dk and dv are split into views of `chunk` keys; dK/dV of every chunk
+    come from one kernel launch, and dQ is summed over the chunks on chip and
+    written once.  Returns (dq, dk, dv).
+    """
+    b, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty((b, sk, hkv, d), dtype=q.dtype, device=dev) if dk is None else dk
+    dv = torch.empty((b, sk, hkv, d), dtype=q.dtype, device=dev) if dv is None else dv
+    dq_acc = torch.empty((b, sq, hq, d), dtype=torch.float32, device=dev) if dq_acc is None else dq_acc
+    workspace = bwd_workspace(b, hq, sq, dev) if workspace is None else workspace
+    bounds = chunk_bounds(sk, chunk)
+    views = lambda t: [t[:, a:e] for a, e in bounds]  # noqa: E731
+    B.attn_bwd_chunks(q, views(k), views(v), o, dout, lse, workspace, dq_acc, views(dk), views(dv),
+                      chunk_pos0=[k_pos0 + a for a, _ in bounds], dq=dq, q_pos0=q_pos0, causal=causal, scale=scale,
+                      compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=causal, stream=stream)
+    return dq, dk, dv
+
+
 def causal_attention_forward(q, k, v, *, scale=0.0, balanced=True, o=None, lse=None, stream=None):
     b, s, hq, d = q.shape
     o = torch.empty_like(q) if o is None else o

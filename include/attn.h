@@ -65,7 +65,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -266,6 +266,74 @@ typedef struct attn_bwd_args {
 } attn_bwd_args;
 
 ATTN_API int attn_bwd(const attn_bwd_args* args, void* stream);
+
+/*
+ * attn_bwd_chunks: the backward of a query shard over a sequence of key/value
+ * chunks in one call -- the per-chunk backward of the BurstAttention and
+ * ring-attention pages (each chunk's dK/dV from the global LSE and delta, dQ
+ * summed over the chunks), with dQ kept on chip across the chunks instead of
+ * passing through dq_acc once per chunk.  The result equals attn_bwd over the
+ * union of the chunks' keys (key j of chunk c at global position
+ * chunk_pos0[c] + j), which is also what chained attn_bwd calls over the chunks
+ * give:
+ *   dk_chunks[c], dv_chunks[c]  chunk c's key and value gradients (written; a
+ *                               chunk no query sees gets zeros),
+ *   dq_acc                      the sum of every chunk's dQ contribution,
+ *                               written once (added to its contents without
+ *                               ATTN_BWD_DQ_OVERWRITE),
+ *   dq                          dq_acc in bf16 with ATTN_BWD_FINALIZE_DQ.
+ * Chunks are given as in attn_fwd_chunks: k_chunks[c] and v_chunks[c] are
+ * [batch, chunk_len[c], heads_kv, head_dim] bf16 with the shared sequence and
+ * head strides k_stride[1..2] / v_stride[1..2] and batch stride
+ * chunk_k_bstride[c] / chunk_v_bstride[c] (k_stride[0] / v_stride[0] when the
+ * array is NULL); dk_chunks[c] and dv_chunks[c] likewise with dk_stride /
+ * dv_stride and chunk_dk_bstride / chunk_dv_bstride.  All chunk arrays are HOST
+ * arrays of n_chunks entries, read during the call (the device pointers they
+ * hold must stay valid until the stream work finishes); a chunk of length 0 is
+ * skipped.  q, o, dout, lse, workspace, dq_acc, dq, causal, scale and the flags
+ * mean what they mean for attn_bwd; dtype must be ATTN_DTYPE_BF16.  Launches:
+ * the statistics pass (with ATTN_BWD_COMPUTE_DELTA), one dK/dV kernel over the
+ * key tiles of all chunks, one dQ kernel over all chunks.  No floating-point
+ * atomics are used.
+ */
+typedef struct attn_bwd_chunks_args {
+  uint32_t struct_size;
+  uint32_t dtype; /* ATTN_DTYPE_BF16 */
+  int32_t batch, heads_q, heads_kv, seqlen_q, head_dim;
+  int32_t n_chunks; /* 0 .. ATTN_MAX_CHUNKS */
+  const void* q;
+  int64_t q_stride[3];
+  const void* o;
+  int64_t o_stride[3];
+  const void* dout;
+  int64_t do_stride[3];
+  const float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  float* dq_acc;
+  void* dq; /* used with ATTN_BWD_FINALIZE_DQ, else may be NULL */
+  int64_t dq_stride[3];
+  const void* const* k_chunks;  /* host array of n_chunks device pointers */
+  const void* const* v_chunks;  /* host array of n_chunks device pointers */
+  void* const* dk_chunks;       /* host array of n_chunks device pointers */
+  void* const* dv_chunks;       /* host array of n_chunks device pointers */
+  const int32_t* chunk_len;     /* host array: keys in each chunk (>= 0) */
+  const int64_t* chunk_pos0;    /* host array: global position of each chunk's key 0 */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t dk_stride[3];
+  int64_t dv_stride[3];
+  const int64_t* chunk_k_bstride;  /* host arrays or NULL: per-chunk batch strides */
+  const int64_t* chunk_v_bstride;
+  const int64_t* chunk_dk_bstride;
+  const int64_t* chunk_dv_bstride;
+  int64_t q_pos0;
+  int32_t causal;
+  float scale;
+  uint32_t flags; /* ATTN_BWD_* */
+} attn_bwd_chunks_args;
+
+ATTN_API int attn_bwd_chunks(const attn_bwd_chunks_args* args, void* stream);
 
 /*
  * attn_decode_splitkv: one query token per sequence over a KV cache.

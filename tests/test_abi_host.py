@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -50,8 +50,13 @@ def test_struct_layouts_match_c():
 #include "attn.h"
 #define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F))
 int main(void) {
-  printf("fwd %zu\nmerge %zu\nbwd %zu\ndecode %zu\nchunks %zu\n", sizeof(attn_fwd_args), sizeof(attn_merge_args),
-         sizeof(attn_bwd_args), sizeof(attn_decode_args), sizeof(attn_fwd_chunks_args));
+  printf("fwd %zu\nmerge %zu\nbwd %zu\ndecode %zu\nchunks %zu\nbwdchunks %zu\n", sizeof(attn_fwd_args),
+         sizeof(attn_merge_args), sizeof(attn_bwd_args), sizeof(attn_decode_args), sizeof(attn_fwd_chunks_args),
+         sizeof(attn_bwd_chunks_args));
+  P(attn_bwd_chunks_args, q); P(attn_bwd_chunks_args, dq_acc); P(attn_bwd_chunks_args, dq_stride);
+  P(attn_bwd_chunks_args, k_chunks); P(attn_bwd_chunks_args, dv_chunks); P(attn_bwd_chunks_args, chunk_pos0);
+  P(attn_bwd_chunks_args, dv_stride); P(attn_bwd_chunks_args, chunk_dv_bstride); P(attn_bwd_chunks_args, q_pos0);
+  P(attn_bwd_chunks_args, flags);
   P(attn_fwd_chunks_args, k_chunks); P(attn_fwd_chunks_args, chunk_pos0); P(attn_fwd_chunks_args, v_stride);
   P(attn_fwd_chunks_args, o_final_stride); P(attn_fwd_chunks_args, q_pos0); P(attn_fwd_chunks_args, flags);
   P(attn_fwd_chunks_args, chunk_v_bstride); P(attn_fwd_chunks_args, o);
@@ -74,8 +79,10 @@ int main(void) {
     assert int(got["bwd"]) == ctypes.sizeof(B.BwdArgs)
     assert int(got["decode"]) == ctypes.sizeof(B.DecodeArgs)
     assert int(got["chunks"]) == ctypes.sizeof(B.FwdChunksArgs)
+    assert int(got["bwdchunks"]) == ctypes.sizeof(B.BwdChunksArgs)
     cls = {"attn_fwd_args": B.FwdArgs, "attn_merge_args": B.MergeArgs, "attn_bwd_args": B.BwdArgs,
-           "attn_decode_args": B.DecodeArgs, "attn_fwd_chunks_args": B.FwdChunksArgs}
+           "attn_decode_args": B.DecodeArgs, "attn_fwd_chunks_args": B.FwdChunksArgs,
+           "attn_bwd_chunks_args": B.BwdChunksArgs}
     for key, val in got.items():
         if "." in key:
             t, f = key.split(".")
@@ -83,7 +90,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -272,6 +279,67 @@ def test_fwd_chunks_empty_query_is_noop(lib):
     # No query rows: nothing is launched and no pointer is dereferenced.
     a = chunks_args(seqlen_q=0, q=None, o=None, lse=None)
     assert lib.attn_fwd_chunks(ctypes.byref(a), None) == B.ATTN_OK
+
+
+def bwd_chunks_args(lens=(64, 0), **kw):
+    a = B.BwdChunksArgs()
+    a.struct_size = ctypes.sizeof(B.BwdChunksArgs)
+    a.dtype = B.ATTN_DTYPE_BF16
+    a.batch, a.heads_q, a.heads_kv, a.seqlen_q, a.head_dim = 1, 2, 2, 32, 64
+    for name in ("q", "o", "dout", "lse", "workspace", "dq_acc", "dq"):
+        setattr(a, name, FAKE)
+    a.workspace_bytes = 2 * 2 * 64 * 4
+    st = B.I64x3(64 * 2 * 64, 2 * 64, 64)
+    for name in ("q_stride", "o_stride", "do_stride", "dq_stride", "k_stride", "v_stride", "dk_stride", "dv_stride"):
+        setattr(a, name, st)
+    n = len(lens)
+    a.n_chunks = n
+    ptrs = lambda: (ctypes.c_void_p * n)(*([FAKE] * n))  # noqa: E731
+    a._keep = (ptrs(), ptrs(), ptrs(), ptrs(), (ctypes.c_int32 * n)(*lens), (ctypes.c_int64 * n)(*range(0, 64 * n, 64)))
+    a.k_chunks, a.v_chunks, a.dk_chunks, a.dv_chunks, a.chunk_len, a.chunk_pos0 = a._keep
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+BWD_CHUNKS_BAD = [
+    (dict(n_chunks=65), B.ATTN_ERR_INVALID_ARG, "n_chunks"),
+    (dict(n_chunks=-1), B.ATTN_ERR_INVALID_ARG, "n_chunks"),
+    (dict(dtype=B.ATTN_DTYPE_F32), B.ATTN_ERR_UNSUPPORTED, "bf16 only"),
+    (dict(flags=1 << 9), B.ATTN_ERR_INVALID_ARG, "flag"),
+    (dict(dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
+    (dict(workspace_bytes=1023), B.ATTN_ERR_WORKSPACE, "1023 given"),
+    (dict(workspace=FAKE + 16), B.ATTN_ERR_WORKSPACE, "256-byte"),
+    (dict(dq=None, flags=B.ATTN_BWD_FINALIZE_DQ), B.ATTN_ERR_INVALID_ARG, "dq is NULL"),
+    (dict(o=None, flags=B.ATTN_BWD_COMPUTE_DELTA), B.ATTN_ERR_INVALID_ARG, "o is NULL"),
+    (dict(dv_chunks=None), B.ATTN_ERR_INVALID_ARG, "chunk arrays"),
+    (dict(dk_stride=B.I64x3(64 * 2 * 64, 2 * 64, 3)), B.ATTN_ERR_UNSUPPORTED, "dk_chunks[0] stride"),
+    (dict(chunk_dv_bstride=(ctypes.c_int64 * 2)(6, 6)), B.ATTN_ERR_UNSUPPORTED, "dv_chunks[0] stride[0]"),
+    (dict(head_dim=96), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", BWD_CHUNKS_BAD, ids=[m for _, _, m in BWD_CHUNKS_BAD])
+def test_bwd_chunks_rejects(lib, kw, code, msg):
+    a = bwd_chunks_args(**kw)
+    assert lib.attn_bwd_chunks(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_bwd_chunks_rejects_negative_length_and_null_chunk(lib):
+    a = bwd_chunks_args(lens=(64, -5))
+    assert lib.attn_bwd_chunks(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "chunk_len[1]" in lib.attn_last_error().decode()
+    a = bwd_chunks_args(lens=(64, 64))
+    a.dk_chunks[1] = None
+    assert lib.attn_bwd_chunks(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "dk_chunks[1] is NULL" in lib.attn_last_error().decode()
+
+
+def test_bwd_chunks_nothing_to_do(lib):
+    # No query rows and no chunk: nothing is launched and no pointer is dereferenced.
+    a = bwd_chunks_args(lens=(), seqlen_q=0, q=None, o=None, dout=None, lse=None, dq_acc=None, workspace=None)
+    assert lib.attn_bwd_chunks(ctypes.byref(a), None) == B.ATTN_OK
 
 
 def decode_args(**kw):

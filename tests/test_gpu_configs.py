@@ -107,7 +107,13 @@ def test_shard_bwd_128k(shard_inputs):
     log("shard_bwd_128k: forward, then per-chunk backward from the saved O/LSE")
     o, lse, _ = shard.shard_forward(q, k, v, w.chunk, q_pos0=w.q_pos0, causal=True)
     dq, dk, dv = shard.shard_backward(q, k, v, o, do, lse, w.chunk, q_pos0=w.q_pos0, causal=True)
+    log("shard_bwd_128k: fused chunk table (attn_bwd_chunks), against the chained calls")
+    fq, fk, fv = shard.shard_backward_fused(q, k, v, o, do, lse, w.chunk, q_pos0=w.q_pos0, causal=True)
     torch.cuda.synchronize()
+    assert torch.equal(fk, dk) and torch.equal(fv, dv), "fused dK/dV differ from the per-chunk calls"
+    e = (fq.float() - dq.float()).abs().max().item()
+    log(f"  max|dQ fused - dQ chained| {e:.3e} (max|dQ| {dq.float().abs().max().item():.3e})")
+    assert e <= 2e-3
     last = w.q_pos0 + w.S_q  # keys at or after this position are invisible to the shard
     assert torch.all(dk[:, last:] == 0) and torch.all(dv[:, last:] == 0)
     # Sum rules on every head (fp64 sums of the bf16 outputs).

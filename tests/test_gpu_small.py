@@ -297,6 +297,76 @@ def test_bwd_chunked(dtype):
     assert torch.all(dk[:, Sq + qp:] == 0) and torch.all(dv[:, Sq + qp:] == 0), "invisible keys got gradient"
 
 
+@pytest.mark.parametrize("case", FUSED_CASES, ids=_ids(FUSED_CASES))
+def test_bwd_chunks_fused(case):
+    """One call over a chunk table against the oracle's per-chunk backward from the global O and
+    LSE: dK/dV of every chunk (zeros for a chunk no query sees), dQ summed over the chunks, also
+    added to a running dq_acc without DQ_OVERWRITE."""
+    Bn, Sq, Hq, Hkv, D, lens, pos, qp, causal, bal = case
+    log(f"bwd chunks {case}")
+    q, qh = seq_tensor(111, 0, Bn, Sq, Hq, D, "bf16")
+    do, doh = seq_tensor(111, 1, Bn, Sq, Hq, D, "bf16")
+    ks, vs, chunks_h = [], [], []
+    for c, L in enumerate(lens):
+        k, kh = seq_tensor(111, 10 + 2 * c, Bn, L, Hkv, D, "bf16")
+        v, vh = seq_tensor(111, 11 + 2 * c, Bn, L, Hkv, D, "bf16")
+        ks.append(k)
+        vs.append(v)
+        chunks_h.append((kh, vh, pos[c]))
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = _oracle_over_chunks(qh, chunks_h, scale, causal, qp)
+    dq_ref = np.zeros(qh.shape)
+    dkv_ref = []
+    for kh, vh, p0 in chunks_h:
+        a, bk, bv = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, scale, causal, qp, p0)
+        dq_ref += a
+        dkv_ref.append((bk, bv))
+    o = torch.empty((Bn, Sq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Bn, Hq, Sq), dtype=torch.float32, device="cuda")
+    B.attn_fwd_chunks(q, ks, vs, o, lse, chunk_pos0=pos, q_pos0=qp, causal=causal)
+    dks = [torch.full_like(k, float("nan")) for k in ks]
+    dvs = [torch.full_like(v, float("nan")) for v in vs]
+    dq = torch.full_like(q, float("nan"))
+    dq_acc = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((B.attn_bwd_workspace_size(Bn, Hq, Sq) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_bwd_chunks(q, ks, vs, o, do, lse, ws, dq_acc, dks, dvs, chunk_pos0=pos, dq=dq, q_pos0=qp, causal=causal,
+                      compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=bal)
+    torch.cuda.synchronize()
+    check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
+    check("dQ acc", dq_acc, dq_ref, G_TOL, scale_by_max=True)
+    for c, ((bk, bv), dk, dv) in enumerate(zip(dkv_ref, dks, dvs)):
+        check(f"dK[{c}]", dk, bk, G_TOL, scale_by_max=True)
+        check(f"dV[{c}]", dv, bv, G_TOL, scale_by_max=True)
+        if not np.any(bk) and not np.any(bv) and lens[c] > 0:
+            assert torch.all(dk == 0) and torch.all(dv == 0), f"chunk {c} is invisible but got gradient"
+    # Accumulate into a running dq_acc, statistics reused from the first call.
+    base = torch.randn((Bn, Sq, Hq, D), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+    dq_acc2 = base.clone()
+    B.attn_bwd_chunks(q, ks, vs, o, do, lse, ws, dq_acc2, dks, dvs, chunk_pos0=pos, dq=dq, q_pos0=qp, causal=causal,
+                      finalize_dq=True, balanced=bal)
+    torch.cuda.synchronize()
+    check("dQ acc added", dq_acc2 - base, dq_ref, G_TOL, scale_by_max=True)
+    check("dQ from added acc", dq, (base.cpu().double().numpy() + dq_ref), G_TOL, scale_by_max=True)
+
+
+def test_bwd_chunks_matches_chained_calls():
+    """The fused call and chained attn_bwd calls over the same chunks: identical dK/dV (the same
+    per-tile arithmetic), dQ equal up to the order of the fp32 additions across chunks."""
+    log("bwd chunks vs chained")
+    Bn, Sq, H, D, chunk, qp = 2, 192, 2, 128, 96, 300
+    Sk = 600
+    (q, k, v), _ = _inputs(112, Bn, Sq, Sk, H, H, D, "bf16")
+    do, _ = seq_tensor(112, 3, Bn, Sq, H, D, "bf16")
+    o, lse, _ = shard.shard_forward(q, k, v, chunk, q_pos0=qp, causal=True)
+    dq1, dk1, dv1 = shard.shard_backward(q, k, v, o, do, lse, chunk, q_pos0=qp, causal=True)
+    dq2, dk2, dv2 = shard.shard_backward_fused(q, k, v, o, do, lse, chunk, q_pos0=qp, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    err = (dq1.float() - dq2.float()).abs().max().item()
+    log(f"  max|dQ chained - dQ fused| = {err:.3e} (max|dQ| {dq1.float().abs().max().item():.3e})")
+    assert err <= 1e-2 * max(1.0, dq1.float().abs().max().item())
+
+
 def test_bwd_deterministic():
     log("bwd determinism")
     (q, k, v), _ = _inputs(107, 1, 300, 300, 2, 2, 128, "bf16")
