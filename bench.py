@@ -38,7 +38,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # runs of its kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
 # copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md): 14.26 GB read + 3.11 GB written.  Set to
 # None whenever these kernels change, until they are measured again.
-BWD_CALL_HBM_BYTES = 17368445952
+BWD_CALL_HBM_BYTES = None
 HBM_PEAK_GBS = 8000.0
 
 
