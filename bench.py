@@ -169,10 +169,13 @@ def bench_shard(args, stream, do_bwd):
     f_fwd = 4.0 * SQ * SK * D * H / 2.0  # the stated convention: halved for causal
     if not do_bwd:
         (t, tf, tp, tm), _ = time_calls([fwd, fwd_fused, partials, merge], max(3, args.steps), 1, stream)
-        return {"workload": "shard_fwd_128k", "ms": t, "tflops": f_fwd / t / 1e9,
-                "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32, "live_chunks": len(live),
-                "fused_chunk_table": {"ms": tf, "tflops": f_fwd / tf / 1e9,
-                                      "frac_mfma": f_fwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS},
+        # The headline figure is the chunk loop as one call over the chunk table (attn_fwd_chunks); the
+        # chained per-chunk calls and the partials-then-merge form are reported beside it.
+        return {"workload": "shard_fwd_128k", "method": "attn_fwd_chunks over the 32-chunk table", "ms": tf,
+                "tflops": f_fwd / tf / 1e9, "frac_mfma": f_fwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS, "chunks": 32,
+                "live_chunks": len(live),
+                "chained_accumulate": {"ms": t, "tflops": f_fwd / t / 1e9,
+                                       "frac_mfma": f_fwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS},
                 "partials_then_merge": {"partials_ms": tp, "merge_ms": tm, "merge_gbs":
                                         (len(live) + 0.5) * SQ * H * D * 4 / tm / 1e6}}
     fwd()
@@ -192,10 +195,10 @@ def bench_shard(args, stream, do_bwd):
 
     (t, tf), _ = time_calls([bwd, bwd_fused], max(3, args.steps), 1, stream)
     f_bwd = 2.5 * f_fwd
-    return {"workload": "shard_bwd_128k", "ms": t, "tflops": f_bwd / t / 1e9,
-            "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS,
-            "fused_chunk_table": {"ms": tf, "tflops": f_bwd / tf / 1e9,
-                                  "frac_mfma": f_bwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
+    return {"workload": "shard_bwd_128k", "method": "attn_bwd_chunks over the 32-chunk table", "ms": tf,
+            "tflops": f_bwd / tf / 1e9, "frac_mfma": f_bwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "chained_calls": {"ms": t, "tflops": f_bwd / t / 1e9,
+                              "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
 
 
 def bench_decode(args, stream):

@@ -347,11 +347,15 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
   rf.init(lane);
   tf.init(lane);
 
+  TileSrc<D, 4> ksrc, vsrc;
+  const bool kfast = TileSrc<D, 4>::fits(p.k.ss), vfast = TileSrc<D, 4>::fits(p.v.ss);
+  ksrc.init(p.k.ss, wave, lane);
+  vsrc.init(p.v.ss, wave, lane);
   auto issue = [&](int c, int tile, int slot) {
     const u16* kb = (const u16*)ct.k[c] + (int64_t)b * ct.kb[c] + (int64_t)hk * p.k.sh;
     const u16* vb = (const u16*)ct.v[c] + (int64_t)b * ct.vb[c] + (int64_t)hk * p.v.sh;
-    issue_swtile<D, 4, true>(k_s + slot * SZ, kb, p.k.ss, tile * BN, ct.len[c], wave, lane);
-    issue_swtile<D, 4, true>(v_s + slot * SZ, vb, p.v.ss, tile * BN, ct.len[c], wave, lane);
+    ksrc.issue(k_s + slot * SZ, kb, p.k.ss, tile * BN, ct.len[c], kfast, wave, lane);
+    vsrc.issue(v_s + slot * SZ, vb, p.v.ss, tile * BN, ct.len[c], vfast, wave, lane);
   };
 
   int c = first_from(0), t = 0, slot = 0;
