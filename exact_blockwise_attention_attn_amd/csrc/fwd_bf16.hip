@@ -25,6 +25,8 @@
 //   * causal tiles are classified per workgroup: tiles no query sees are never
 //     visited, tiles every query sees skip the mask, the rest are masked per
 //     element.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_internal.h"
 #include "tile_lds.h"
@@ -358,13 +360,16 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
     vsrc.issue(v_s + slot * SZ, vb, p.v.ss, tile * BN, ct.len[c], vfast, wave, lane);
   };
 
-  int c = first_from(0), t = 0, slot = 0;
+  int c = first_from(0), t = 0;
   if (c < ct.n) {
     issue(c, 0, 0);
     wait_vm<0>();
     lds_barrier();
   }
-  while (c < ct.n) {
+  // One step per tile; the loop is unrolled over the two LDS slots so that each
+  // step's slot is a compile-time constant folded into its LDS read offsets.
+  auto step = [&](auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
     int kv_end, full_end;
     chunk_range(c, kv_end, full_end);
     // Next tile in sequence: the rest of this chunk, then the next chunk with visible keys.
@@ -373,16 +378,20 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
       nc = first_from(c + 1);
       nt = 0;
     }
-    if (nc < ct.n) issue(nc, nt, slot ^ 1);
+    if (nc < ct.n) issue(nc, nt, SLOT ^ 1);
     int64_t lim64 = (int64_t)ct.len[c] - 1;  // this lane's last visible key of chunk c
     if (p.causal) lim64 = min<int64_t>(ct.q_pos0 - ct.pos0[c] + qi, lim64);
-    tile_step<D>(k_s + slot * SZ, v_s + slot * SZ, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf,
+    tile_step<D>(k_s + SLOT * SZ, v_s + SLOT * SZ, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf,
                  lane);
     wait_vm<0>();  // the next tile, the only load in flight
     lds_barrier();
     c = nc;
     t = nt;
-    slot ^= 1;
+  };
+  while (c < ct.n) {
+    step(std::integral_constant<int, 0>{});
+    if (c >= ct.n) break;
+    step(std::integral_constant<int, 1>{});
   }
   fwd_store<D>(p, oacc, st, qi, qok, b, h, lg);
 }
