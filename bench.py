@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "fp32_small", "copy"], default=None,
                     help="run a single workload (for profiling); 'copy' runs a plain 1 GiB device copy that "
                          "calibrates the HBM traffic counters")
     return ap.parse_args()
@@ -201,6 +201,35 @@ def bench_shard(args, stream, do_bwd):
                               "frac_mfma": f_bwd / t / 1e9 / MFMA_BF16_PEAK_TFLOPS}}
 
 
+def bench_fp32_small(args, stream):
+    """The fp32 workload (Q, K, V [256, 64], four chunks of 64, non-causal): latency of the chunk loops."""
+    import torch
+
+    from exact_blockwise_attention_attn_amd import shard
+
+    S, D, CH = 256, 64, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+    q, k, v, do = (torch.randn((1, S, 1, D), generator=g, device="cuda", dtype=torch.float32) for _ in range(4))
+    o = torch.empty_like(q)  # the fp32 running result is the output
+    lse = torch.empty((1, 1, S), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        shard.shard_forward(q, k, v, CH, stream=stream, o_run=o, lse=lse)
+
+    fwd()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.empty((1, S, 1, D), dtype=torch.float32, device="cuda")
+    ws = shard.bwd_workspace(1, 1, S, "cuda")
+
+    def bwd():
+        shard.shard_backward(q, k, v, o, do, lse, CH, stream=stream, dq=dq, dk=dk, dv=dv, dq_acc=dq_acc, workspace=ws)
+
+    (tf, tb), _ = time_calls([fwd, bwd], 100, 10, stream)
+    return {"workload": "fp32_s256_4chunks", "fwd_us": tf * 1e3, "bwd_us": tb * 1e3,
+            "note": "4 chained chunk calls each way; latency-bound, no roofline"}
+
+
 def bench_decode(args, stream):
     import torch
 
@@ -273,6 +302,9 @@ def main():
     if args.only == "decode":
         print(json.dumps(bench_decode(args, stream)), flush=True)
         return
+    if args.only == "fp32_small":
+        print(json.dumps(bench_fp32_small(args, stream)), flush=True)
+        return
     if args.only == "copy":
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -294,6 +326,7 @@ def main():
         torch.cuda.empty_cache()
         secondary["decode_gqa_128k"] = bench_decode(args, stream)
         torch.cuda.empty_cache()
+        secondary["fp32_s256_4chunks"] = bench_fp32_small(args, stream)
     cpu = None if (args.no_cpu_baseline or args.only) else cpu_baseline()
     bwd_achieved = m["bwd_tflops"]
     line = {

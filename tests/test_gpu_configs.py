@@ -25,7 +25,7 @@ import torch
 import oracle
 from exact_blockwise_attention_attn_amd import binding as B
 from exact_blockwise_attention_attn_amd import shard
-from seeded_inputs import WORKLOADS, bf16_bits_to_f32, normal_bf16
+from seeded_inputs import WORKLOADS, bf16_bits_to_f32, normal_bf16, normal_f32
 from tests.gpu_util import check, log, to_np
 
 pytestmark = pytest.mark.gpu
@@ -135,6 +135,30 @@ def test_shard_bwd_128k(shard_inputs):
             e = _rel_fro(got, ref)
             log(f"    {name} relative Frobenius error {e:.3e}")
             assert e < 2e-2
+
+
+def test_fp32_s256_4chunks():
+    """The fp32 workload in full: Q, K, V, dO [256, 64] fp32, four key chunks of 64, non-causal.
+    Forward chunk by chunk (fused accumulate, and per-chunk partials merged sequentially and as
+    a tree), backward chunk by chunk from the final (O, LSE); every output against the oracle at
+    the graded bounds and at 1e-4, the fp32 self-check."""
+    w = WORKLOADS["fp32_s256_4chunks"]
+    log("fp32_s256_4chunks: generating inputs")
+    x = [normal_f32(w.wid, t, 0, (w.S_q, w.H_q, w.D))[None] for t in range(4)]
+    q, k, v, do = (torch.from_numpy(a).cuda() for a in x)
+    qh, kh, vh, doh = (a.astype(np.float64) for a in x)
+    O_ref, L_ref = oracle.attention(qh, kh, vh, w.scale, w.causal)
+    dq_r, dk_r, dv_r = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, w.scale, w.causal)
+    o, lse, o_run = shard.shard_forward(q, k, v, w.chunk, causal=w.causal)
+    parts = [shard.shard_forward_partials(q, k, v, w.chunk, causal=w.causal, tree=t) for t in (False, True)]
+    dq, dk, dv = shard.shard_backward(q, k, v, o, do, lse, w.chunk, causal=w.causal)
+    torch.cuda.synchronize()
+    for bound in (None, 1e-4):
+        for name, got, ref, tol in (("O", o, O_ref, 1e-2), ("O running", o_run, O_ref, 1e-2),
+                                    ("O merged sequential", parts[0][0], O_ref, 1e-2),
+                                    ("O merged tree", parts[1][0], O_ref, 1e-2), ("LSE", lse, L_ref, 1e-3),
+                                    ("dQ", dq, dq_r, 2e-2), ("dK", dk, dk_r, 2e-2), ("dV", dv, dv_r, 2e-2)):
+            check(f"{name} (bound {bound or tol})", got, ref, bound or tol)
 
 
 def test_decode_gqa_128k():
