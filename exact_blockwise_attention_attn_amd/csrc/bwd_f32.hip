@@ -2,8 +2,8 @@
 // rowsum(dO * O) and the rescaled LSE) and the fp32 backward kernels (vector
 // ALUs, fp32 end to end).
 //
-// fp32 dQ kernel: one thread per query row; key/value tiles staged in LDS.
-// fp32 dK/dV kernel: one thread per key row; query tiles (q, dO, LSE, delta)
+// fp32 dQ kernel: 16 threads per query row; key/value tiles staged in LDS.
+// fp32 dK/dV kernel: 16 threads per key row; query tiles (q, dO, LSE, delta)
 // staged in LDS, looping over every query head that reads the key/value head.
 // Both recompute P = exp(s - LSE) from the saved LSE; neither re-runs the forward.
 #include "attn_device.h"
@@ -67,106 +67,130 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------- fp32 dQ ----
+//
+// Both fp32 kernels give each row (a query for dQ, a key for dK/dV) 16
+// threads: thread c of a row holds features c*F .. c*F+F-1 (F = D/16) of the
+// row's operands and accumulators, the two dot products of a pair are summed
+// over the row's 16 lanes, and each thread updates its own features.  Tiles of
+// the other side's rows are staged in LDS and read by all rows.
 
-constexpr int FBM = 64;  // rows per workgroup (one per thread)
-constexpr int FTK = 32;  // rows per staged tile
+constexpr int TPR = 16;            // threads per row
+constexpr int FROWS = 16;          // rows per workgroup
+constexpr int FNT = TPR * FROWS;   // threads per workgroup
+constexpr int FTK = 32;            // rows per staged tile
+
+// Sum over the 16 lanes of this thread's row group.
+__device__ __forceinline__ float row_sum(float x) {
+  x += __shfl_xor(x, 8, TPR);
+  x += __shfl_xor(x, 4, TPR);
+  x += __shfl_xor(x, 2, TPR);
+  x += __shfl_xor(x, 1, TPR);
+  return x;
+}
 
 template <int D>
-__global__ __launch_bounds__(FBM) void dq_f32_kernel(BwdParams p) {
-  __shared__ float ks[FTK][D];
-  __shared__ float vs[FTK][D];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
+  constexpr int F = D / TPR;
+  __shared__ __attribute__((aligned(16))) float ks[FTK][D];
+  __shared__ __attribute__((aligned(16))) float vs[FTK][D];
+  const int tid = threadIdx.x, r = tid / TPR, c = tid % TPR, f0 = c * F;
   const int qt = blockIdx.x % p.n_qtiles;
   const int bh = blockIdx.x / p.n_qtiles;
   const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
-  const int qi = qt * FBM + tid;
+  const int qi = qt * FROWS + r;
   const bool qok = qi < p.Sq;
   const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
   const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
   const float* kb = (const float*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
   const float* vb = (const float*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
-  float q[D], dO[D], dq[D];
+  float q[F], dO[F], dq[F];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    q[d] = qok ? qb[(int64_t)qi * p.q.ss + d] : 0.f;
-    dO[d] = qok ? dob[(int64_t)qi * p.dout.ss + d] : 0.f;
-    dq[d] = 0.f;
+  for (int f = 0; f < F; ++f) {
+    q[f] = qok ? qb[(int64_t)qi * p.q.ss + f0 + f] : 0.f;
+    dO[f] = qok ? dob[(int64_t)qi * p.dout.ss + f0 + f] : 0.f;
+    dq[f] = 0.f;
   }
   const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + qi;
   const float lse = qok ? p.lse[srow] : neg_inf();
   const float dlt = qok ? p.stats[((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad + qi] : 0.f;
   const bool live = lse != neg_inf();
-  const int q_last = min(qt * FBM + FBM, p.Sq) - 1;
+  const int q_last = min(qt * FROWS + FROWS, p.Sq) - 1;
   int kv_end = p.Sk;
-  int64_t lim = (int64_t)p.Sk - 1;
+  int64_t lim = (int64_t)p.Sk - 1;  // last key this row sees
   if (p.causal) {
     kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q_last + 1, p.Sk));
     lim = min<int64_t>(p.delta_pos + qi, lim);
   }
   for (int key0 = 0; key0 < kv_end; key0 += FTK) {
     __syncthreads();
-    for (int e = tid; e < FTK * D; e += FBM) {
-      const int r = e / D, c = e % D;
-      const int key = key0 + r;
+    for (int e = tid; e < FTK * D; e += FNT) {
+      const int rr = e / D, cc = e % D;
+      const int key = key0 + rr;
       const bool ok = key < p.Sk;
-      ks[r][c] = ok ? kb[(int64_t)key * p.k.ss + c] : 0.f;
-      vs[r][c] = ok ? vb[(int64_t)key * p.v.ss + c] : 0.f;
+      ks[rr][cc] = ok ? kb[(int64_t)key * p.k.ss + cc] : 0.f;
+      vs[rr][cc] = ok ? vb[(int64_t)key * p.v.ss + cc] : 0.f;
     }
     __syncthreads();
+    // Every lane runs every step (the row sums exchange data across lanes);
+    // pairs a row does not see get P = 0.
     for (int j = 0; j < FTK; ++j) {
-      if (!live || key0 + j > lim) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s = fmaf(q[d], ks[j][d], s);
-        dp = fmaf(dO[d], vs[j][d], dp);
+      for (int f = 0; f < F; ++f) {
+        s = fmaf(q[f], ks[j][f0 + f], s);
+        dp = fmaf(dO[f], vs[j][f0 + f], dp);
       }
-      const float pj = expf(s * p.scale - lse);
+      s = row_sum(s);
+      dp = row_sum(dp);
+      const bool vis = live && key0 + j <= lim;
+      const float pj = vis ? expf(s * p.scale - lse) : 0.f;
       const float ds = pj * (dp - dlt);
 #pragma unroll
-      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, ks[j][d], dq[d]);
+      for (int f = 0; f < F; ++f) dq[f] = fmaf(ds, ks[j][f0 + f], dq[f]);
     }
   }
   if (!qok) return;
-  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
-  float* dqp = p.finalize_dq ? (float*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
-                             : nullptr;
+  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D + f0;
+  float* dqp = p.finalize_dq
+                   ? (float*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh + f0
+                   : nullptr;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    float v = dq[d] * p.scale;
-    if (!p.dq_overwrite) v += accp[d];
-    accp[d] = v;
-    if (dqp) dqp[d] = v;
+  for (int f = 0; f < F; ++f) {
+    float v = dq[f] * p.scale;
+    if (!p.dq_overwrite) v += accp[f];
+    accp[f] = v;
+    if (dqp) dqp[f] = v;
   }
 }
 
 // ---------------------------------------------------------- fp32 dK/dV ----
 
 template <int D>
-__global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
-  __shared__ float qs[FTK][D];
-  __shared__ float dos[FTK][D];
+__global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
+  constexpr int F = D / TPR;
+  __shared__ __attribute__((aligned(16))) float qs[FTK][D];
+  __shared__ __attribute__((aligned(16))) float dos[FTK][D];
   __shared__ float ls[FTK];
   __shared__ float ds_[FTK];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, r = tid / TPR, c = tid % TPR, f0 = c * F;
   const int kt = blockIdx.x % p.n_ktiles;
   const int bh = blockIdx.x / p.n_ktiles;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  const int kj = kt * FBM + tid;
+  const int kj = kt * FROWS + r;
   const bool kok = kj < p.Sk;
   const float* kb = (const float*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
   const float* vb = (const float*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
-  float k[D], v[D], dk[D], dv[D];
+  float k[F], v[F], dk[F], dv[F];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    k[d] = kok ? kb[(int64_t)kj * p.k.ss + d] : 0.f;
-    v[d] = kok ? vb[(int64_t)kj * p.v.ss + d] : 0.f;
-    dk[d] = 0.f;
-    dv[d] = 0.f;
+  for (int f = 0; f < F; ++f) {
+    k[f] = kok ? kb[(int64_t)kj * p.k.ss + f0 + f] : 0.f;
+    v[f] = kok ? vb[(int64_t)kj * p.v.ss + f0 + f] : 0.f;
+    dk[f] = 0.f;
+    dv[f] = 0.f;
   }
   const int64_t need = (int64_t)kj - p.delta_pos;  // causal: query index must be >= need
   int i_start = 0;
-  if (p.causal) i_start = (int)min<int64_t>(p.Sq, max<int64_t>(0, (int64_t)kt * FBM - p.delta_pos));
+  if (p.causal) i_start = (int)min<int64_t>(p.Sq, max<int64_t>(0, (int64_t)kt * FROWS - p.delta_pos));
   i_start = (i_start / FTK) * FTK;
   for (int hh = 0; hh < p.group; ++hh) {
     const int h = hk * p.group + hh;
@@ -176,12 +200,12 @@ __global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
     const float* dltb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad;
     for (int i0 = i_start; i0 < p.Sq; i0 += FTK) {
       __syncthreads();
-      for (int e = tid; e < FTK * D; e += FBM) {
-        const int r = e / D, c = e % D;
-        const int i = i0 + r;
+      for (int e = tid; e < FTK * D; e += FNT) {
+        const int rr = e / D, cc = e % D;
+        const int i = i0 + rr;
         const bool ok = i < p.Sq;
-        qs[r][c] = ok ? qb[(int64_t)i * p.q.ss + c] : 0.f;
-        dos[r][c] = ok ? dob[(int64_t)i * p.dout.ss + c] : 0.f;
+        qs[rr][cc] = ok ? qb[(int64_t)i * p.q.ss + cc] : 0.f;
+        dos[rr][cc] = ok ? dob[(int64_t)i * p.dout.ss + cc] : 0.f;
       }
       if (tid < FTK) {
         const int i = i0 + tid;
@@ -189,32 +213,34 @@ __global__ __launch_bounds__(FBM) void dkdv_f32_kernel(BwdParams p) {
         ds_[tid] = (i < p.Sq) ? dltb[i] : 0.f;
       }
       __syncthreads();
-      for (int r = 0; r < FTK; ++r) {
-        const float lse = ls[r];
-        if (lse == neg_inf() || (p.causal && (int64_t)(i0 + r) < need)) continue;
+      for (int rr = 0; rr < FTK; ++rr) {
         float s = 0.f, dp = 0.f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          s = fmaf(k[d], qs[r][d], s);
-          dp = fmaf(v[d], dos[r][d], dp);
+        for (int f = 0; f < F; ++f) {
+          s = fmaf(k[f], qs[rr][f0 + f], s);
+          dp = fmaf(v[f], dos[rr][f0 + f], dp);
         }
-        const float pj = expf(s * p.scale - lse);
-        const float ds = pj * (dp - ds_[r]);
+        s = row_sum(s);
+        dp = row_sum(dp);
+        const float lse = ls[rr];
+        const bool vis = kok && lse != neg_inf() && !(p.causal && (int64_t)(i0 + rr) < need);
+        const float pj = vis ? expf(s * p.scale - lse) : 0.f;
+        const float ds = pj * (dp - ds_[rr]);
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-          dv[d] = fmaf(pj, dos[r][d], dv[d]);
-          dk[d] = fmaf(ds, qs[r][d], dk[d]);
+        for (int f = 0; f < F; ++f) {
+          dv[f] = fmaf(pj, dos[rr][f0 + f], dv[f]);
+          dk[f] = fmaf(ds, qs[rr][f0 + f], dk[f]);
         }
       }
     }
   }
   if (!kok) return;
-  float* dkp = (float*)p.dk.ptr + (int64_t)b * p.dk.sb + (int64_t)kj * p.dk.ss + (int64_t)hk * p.dk.sh;
-  float* dvp = (float*)p.dv.ptr + (int64_t)b * p.dv.sb + (int64_t)kj * p.dv.ss + (int64_t)hk * p.dv.sh;
+  float* dkp = (float*)p.dk.ptr + (int64_t)b * p.dk.sb + (int64_t)kj * p.dk.ss + (int64_t)hk * p.dk.sh + f0;
+  float* dvp = (float*)p.dv.ptr + (int64_t)b * p.dv.sb + (int64_t)kj * p.dv.ss + (int64_t)hk * p.dv.sh + f0;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    dkp[d] = dk[d] * p.scale;
-    dvp[d] = dv[d];
+  for (int f = 0; f < F; ++f) {
+    dkp[f] = dk[f] * p.scale;
+    dvp[f] = dv[f];
   }
 }
 
@@ -236,19 +262,19 @@ hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_
 
 hipError_t launch_bwd_f32(const BwdParams& p0, int D, int run_dq, hipStream_t s) {
   BwdParams p = p0;
-  p.n_ktiles = (p.Sk + FBM - 1) / FBM;
-  p.n_qtiles = (p.Sq + FBM - 1) / FBM;
+  p.n_ktiles = (p.Sk + FROWS - 1) / FROWS;
+  p.n_qtiles = (p.Sq + FROWS - 1) / FROWS;
   const int64_t gk = (int64_t)p.B * p.Hkv * p.n_ktiles;
   if (gk > 0) {
-    if (D == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3((unsigned)gk), dim3(FBM), 0, s, p);
-    else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3((unsigned)gk), dim3(FBM), 0, s, p);
+    if (D == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3((unsigned)gk), dim3(FNT), 0, s, p);
+    else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3((unsigned)gk), dim3(FNT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (run_dq && gq > 0) {
-    if (D == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)gq), dim3(FBM), 0, s, p);
-    else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)gq), dim3(FBM), 0, s, p);
+    if (D == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)gq), dim3(FNT), 0, s, p);
+    else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)gq), dim3(FNT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
