@@ -24,6 +24,7 @@ to bf16; they are resident in HBM before timing starts.
 from __future__ import annotations
 
 import argparse
+import itertools
 import json
 import math
 import os
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "fp32_small", "copy"], default=None,
+    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "fp32_small", "varlen", "copy"], default=None,
                     help="run a single workload (for profiling); 'copy' runs a plain 1 GiB device copy that "
                          "calibrates the HBM traffic counters")
     return ap.parse_args()
@@ -230,6 +231,44 @@ def bench_fp32_small(args, stream):
             "note": "4 chained chunk calls each way; latency-bound, no roofline"}
 
 
+VARLEN_LENGTHS = (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10)  # x 512 tokens: every k in 1..16 once
+
+
+def bench_varlen(args, stream):
+    """Packed variable-length batch: 16 causal sequences of 512 k tokens (k = 1..16), H = 32, d = 128, bf16."""
+    import torch
+
+    from exact_blockwise_attention_attn_amd import binding
+
+    H, D = 32, 128
+    lens = [512 * k for k in VARLEN_LENGTHS]
+    cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device="cuda")
+    T, mx = sum(lens), max(lens)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8)
+    q, k, v, do = (randn_bf16((T, H, D), g) for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(binding.attn_bwd_workspace_size(len(lens), H, mx), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        binding.attn_fwd_varlen(q, k, v, o, lse, cu, cu, mx, mx, causal=True, balanced=True, stream=stream)
+
+    def bwd():
+        binding.attn_bwd_varlen(q, k, v, o, do, lse, ws, dq_acc, dk, dv, cu, cu, mx, mx, dq=dq, causal=True,
+                                compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=True, stream=stream)
+
+    (tf, tb), _ = time_calls([fwd, bwd], max(3, args.steps), 1, stream)
+    f_fwd = sum(causal_flops(1, H, L, D) for L in lens)
+    f_bwd = 2.5 * f_fwd
+    return {"workload": "varlen_packed_70k", "sequences": len(lens), "tokens": T, "fwd_ms": tf, "bwd_ms": tb,
+            "tflops": (f_fwd + f_bwd) / (tf + tb) / 1e9,
+            "frac_mfma": (f_fwd + f_bwd) / (tf + tb) / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "fwd_tflops": f_fwd / tf / 1e9, "bwd_tflops": f_bwd / tb / 1e9}
+
+
 def bench_decode(args, stream):
     import torch
 
@@ -305,6 +344,9 @@ def main():
     if args.only == "fp32_small":
         print(json.dumps(bench_fp32_small(args, stream)), flush=True)
         return
+    if args.only == "varlen":
+        print(json.dumps(bench_varlen(args, stream)), flush=True)
+        return
     if args.only == "copy":
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -327,6 +369,8 @@ def main():
         secondary["decode_gqa_128k"] = bench_decode(args, stream)
         torch.cuda.empty_cache()
         secondary["fp32_s256_4chunks"] = bench_fp32_small(args, stream)
+        secondary["varlen_packed_70k"] = bench_varlen(args, stream)
+        torch.cuda.empty_cache()
     cpu = None if (args.no_cpu_baseline or args.only) else cpu_baseline()
     bwd_achieved = m["bwd_tflops"]
     line = {

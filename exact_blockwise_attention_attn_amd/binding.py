@@ -55,6 +55,7 @@ class FwdArgs(ctypes.Structure):
         ("o_final", c_vp), ("o_final_stride", I64x3),
         ("q_pos0", c_i64), ("k_pos0", c_i64),
         ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+        ("cu_seqlens_q", c_vp), ("cu_seqlens_k", c_vp),
     ]
 
 
@@ -103,6 +104,7 @@ class BwdArgs(ctypes.Structure):
         ("dv", c_vp), ("dv_stride", I64x3),
         ("q_pos0", c_i64), ("k_pos0", c_i64),
         ("causal", c_i32), ("scale", c_f32), ("flags", c_u32),
+        ("cu_seqlens_q", c_vp), ("cu_seqlens_k", c_vp),
     ]
 
 
@@ -408,6 +410,76 @@ def attn_bwd_chunks(q, k_chunks, v_chunks, o, dout, lse, workspace, dq_acc, dk_c
     a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
                | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
     _check(load().attn_bwd_chunks(ctypes.byref(a), _stream(stream)))
+
+
+def _packed3(t):
+    """Element strides (batch, seq, head) of a packed [total, heads, dim] tensor; the batch stride is unused."""
+    if t is None:
+        return I64x3(0, 0, 0)
+    assert t.dim() == 3 and t.stride(2) == 1
+    return I64x3(0, t.stride(0), t.stride(1))
+
+
+def _check_offsets(cu, name):
+    assert cu.dtype == torch.int32 and cu.dim() == 1 and cu.is_contiguous() and cu.is_cuda, \
+        f"{name} must be a contiguous int32 device tensor of batch + 1 offsets"
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                    scale=0.0, accumulate=False, balanced=False, o_final=None, stream=None) -> None:
+    """Packed variable-length batch: q, o [total_q, Hq, D], k, v [total_k, Hkv, D], lse fp32 [total_q, Hq]."""
+    _check_offsets(cu_seqlens_q, "cu_seqlens_q")
+    _check_offsets(cu_seqlens_k, "cu_seqlens_k")
+    a = FwdArgs()
+    a.struct_size = ctypes.sizeof(FwdArgs)
+    a.dtype = _dtype_code(q)
+    a.batch = cu_seqlens_q.numel() - 1
+    _, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k.shape[1]
+    a.seqlen_q, a.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    a.q, a.q_stride = _ptr(q), _packed3(q)
+    a.k, a.k_stride = _ptr(k), _packed3(k)
+    a.v, a.v_stride = _ptr(v), _packed3(v)
+    a.o, a.o_stride, a.o_dtype = _ptr(o), _packed3(o), _dtype_code(o)
+    a.lse = _ptr(lse)
+    a.o_final, a.o_final_stride = _ptr(o_final), _packed3(o_final)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = (ATTN_FWD_ACCUMULATE if accumulate else 0) | (ATTN_FWD_BALANCED if balanced else 0)
+    a.cu_seqlens_q, a.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    _check(load().attn_fwd_partial(ctypes.byref(a), _stream(stream)))
+
+
+def attn_bwd_varlen(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, *, dq=None, causal=False, scale=0.0, compute_delta=False, dq_overwrite=False,
+                    finalize_dq=False, balanced=False, stream=None) -> None:
+    """Packed variable-length batch backward; layouts as attn_fwd_varlen, dq_acc fp32 [total_q, Hq, D]."""
+    _check_offsets(cu_seqlens_q, "cu_seqlens_q")
+    _check_offsets(cu_seqlens_k, "cu_seqlens_k")
+    a = BwdArgs()
+    a.struct_size = ctypes.sizeof(BwdArgs)
+    a.dtype = _dtype_code(q)
+    a.batch = cu_seqlens_q.numel() - 1
+    _, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k.shape[1]
+    a.seqlen_q, a.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    a.q, a.q_stride = _ptr(q), _packed3(q)
+    a.k, a.k_stride = _ptr(k), _packed3(k)
+    a.v, a.v_stride = _ptr(v), _packed3(v)
+    a.o, a.o_stride = _ptr(o), _packed3(o)
+    a.dout, a.do_stride = _ptr(dout), _packed3(dout)
+    a.lse, a.dq_acc = _ptr(lse), _ptr(dq_acc)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.dq, a.dq_stride = _ptr(dq), _packed3(dq)
+    a.dk, a.dk_stride = _ptr(dk), _packed3(dk)
+    a.dv, a.dv_stride = _ptr(dv), _packed3(dv)
+    a.causal = int(bool(causal))
+    a.scale = float(scale)
+    a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+    a.cu_seqlens_q, a.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seqlens=None, scale=0.0,

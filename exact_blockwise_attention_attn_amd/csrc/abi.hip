@@ -71,6 +71,21 @@ int check_dims(int32_t batch, int32_t hq, int32_t hkv, int32_t sq, int32_t sk, i
   return ATTN_OK;
 }
 
+// Packed variable-length mode: both offset arrays or neither, 4-byte aligned,
+// bf16, positions zero.
+int check_varlen(const int32_t* cu_q, const int32_t* cu_k, uint32_t dtype, int64_t q_pos0, int64_t k_pos0,
+                 bool* varlen) {
+  *varlen = cu_q || cu_k;
+  if (!*varlen) return ATTN_OK;
+  if (!cu_q || !cu_k) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be given together");
+  if (((uintptr_t)cu_q | (uintptr_t)cu_k) & 3u) return fail(ATTN_ERR_UNSUPPORTED, "cu_seqlens are not 4-byte aligned");
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "variable-length batches are bf16 only");
+  if (q_pos0 != 0 || k_pos0 != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "variable-length batches take their positions from the lengths: "
+                                      "q_pos0 and k_pos0 must be 0");
+  return ATTN_OK;
+}
+
 #define TRY(x)              \
   do {                      \
     int rc_ = (x);          \
@@ -115,6 +130,8 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim));
   float scale;
   TRY(check_scale(a->scale, a->head_dim, &scale));
+  bool varlen;
+  TRY(check_varlen(a->cu_seqlens_q, a->cu_seqlens_k, a->dtype, a->q_pos0, a->k_pos0, &varlen));
   const bool has_q = a->seqlen_q > 0, has_k = a->seqlen_k > 0;
   TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
   TRY(check_view("k", a->k, a->k_stride, 3, a->dtype, has_q && has_k));
@@ -134,6 +151,11 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   p.o = mview(a->o, a->o_stride);
   p.o_final = mview(a->o_final, a->o_final_stride);
   p.lse = a->lse;
+  p.lse_sb = varlen ? 0 : (int64_t)a->heads_q * a->seqlen_q;
+  p.lse_sh = varlen ? 1 : a->seqlen_q;
+  p.lse_ss = varlen ? a->heads_q : 1;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
   p.B = a->batch;
   p.Hq = a->heads_q;
   p.Hkv = a->heads_kv;
@@ -148,8 +170,9 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  // A chunk that no query sees leaves a running result unchanged.
-  const bool invisible = a->seqlen_k == 0 || (p.causal && p.delta + (a->seqlen_q - 1) < 0);
+  // A chunk that no query sees leaves a running result unchanged (per sequence
+  // in a variable-length batch, where the kernel decides).
+  const bool invisible = !varlen && (a->seqlen_k == 0 || (p.causal && p.delta + (a->seqlen_q - 1) < 0));
   if (invisible && accumulate && !a->o_final) return ok();
 
   hipStream_t s = (hipStream_t)stream;
@@ -219,6 +242,9 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   p.o = mview(a->o, a->o_stride);
   p.o_final = mview(a->o_final, a->o_final_stride);
   p.lse = a->lse;
+  p.lse_sb = (int64_t)a->heads_q * a->seqlen_q;
+  p.lse_sh = a->seqlen_q;
+  p.lse_ss = 1;
   p.B = a->batch;
   p.Hq = a->heads_q;
   p.Hkv = a->heads_kv;
@@ -290,6 +316,8 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim));
   float scale;
   TRY(check_scale(a->scale, a->head_dim, &scale));
+  bool varlen;
+  TRY(check_varlen(a->cu_seqlens_q, a->cu_seqlens_k, a->dtype, a->q_pos0, a->k_pos0, &varlen));
   const bool has_q = a->seqlen_q > 0, has_k = a->seqlen_k > 0;
   const bool finalize = a->flags & ATTN_BWD_FINALIZE_DQ;
   TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
@@ -324,6 +352,11 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   p.dk = mview(a->dk, a->dk_stride);
   p.dv = mview(a->dv, a->dv_stride);
   p.lse = a->lse;
+  p.lse_sb = varlen ? 0 : (int64_t)a->heads_q * a->seqlen_q;
+  p.lse_sh = varlen ? 1 : a->seqlen_q;
+  p.lse_ss = varlen ? a->heads_q : 1;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
   p.stats = (float*)a->workspace;
   p.Sq_pad = (a->seqlen_q + 63) / 64 * 64;
   p.dq_acc = a->dq_acc;
@@ -350,7 +383,7 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "attn_bwd prepare launch");
   }
   // dQ needs a pass unless this chunk is invisible and dq_acc is left as it is.
-  const bool invisible = !has_k || (p.causal && p.delta_pos + (a->seqlen_q - 1) < 0);
+  const bool invisible = !varlen && (!has_k || (p.causal && p.delta_pos + (a->seqlen_q - 1) < 0));
   const int run_dq = has_q && (!invisible || p.dq_overwrite || finalize);
   e = bf16 ? attn::launch_bwd_bf16(p, D, run_dq, s) : attn::launch_bwd_f32(p, D, run_dq, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
@@ -435,6 +468,9 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   p.dk = mview(nullptr, a->dk_stride);
   p.dv = mview(nullptr, a->dv_stride);
   p.lse = a->lse;
+  p.lse_sb = (int64_t)a->heads_q * a->seqlen_q;
+  p.lse_sh = a->seqlen_q;
+  p.lse_ss = 1;
   p.stats = (float*)a->workspace;
   p.Sq_pad = (a->seqlen_q + 63) / 64 * 64;
   p.dq_acc = a->dq_acc;

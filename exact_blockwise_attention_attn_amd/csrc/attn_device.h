@@ -75,6 +75,24 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (bid % kXcd) * (n / kXcd) + bid / kXcd;
 }
 
+// Packed variable-length batches: the sequences differ in work, so giving each
+// XCD a contiguous range of them (as xcd_remap does) unbalances the XCDs.
+// Instead XCD x takes the heads h = x (mod 8) of every sequence, in (sequence,
+// head, unit) order, so every XCD carries the same share of every sequence
+// while the units of one (sequence, head) still share an XCD and its L2.  With
+// a head count that is not a multiple of 8 the order is the plain one.
+struct SeqHeadUnit {
+  int b, h, unit;
+};
+__device__ __forceinline__ SeqHeadUnit varlen_order(int bid, int H, int n_units) {
+  constexpr int kXcd = 8;
+  if (H % kXcd) return SeqHeadUnit{bid / (H * n_units), (bid / n_units) % H, bid % n_units};
+  const int x = bid % kXcd, s = bid / kXcd;
+  const int per_b = (H / kXcd) * n_units;  // workgroups of one sequence on one XCD
+  const int r = s % per_b;
+  return SeqHeadUnit{s / per_b, (r / n_units) * kXcd + x, r % n_units};
+}
+
 // Log-sum-exp merge of (La, Oa) with (Lb, Ob); -inf parts contribute nothing.
 __device__ __forceinline__ void merge_weights(float La, float Lb, float& wa, float& wb, float& L) {
   float mx = fmaxf(La, Lb);

@@ -23,6 +23,13 @@ struct FwdParams {
   MView o;
   MView o_final;  // ptr == nullptr to skip
   float* lse;
+  int64_t lse_sb, lse_sh, lse_ss;  // element strides of lse over (batch, head, query)
+  // Packed variable-length batches: sequence b's queries are rows cu_q[b] ..
+  // cu_q[b + 1] - 1 of q and o, its keys rows cu_k[b] .. cu_k[b + 1] - 1 of k
+  // and v (device arrays; nullptr for the dense layout).  Sq and Sk are then
+  // the longest lengths, and each sequence's queries sit at the end of its keys.
+  const int* cu_q;
+  const int* cu_k;
   int B, Hq, Hkv, Sq, Sk;
   int group;        // Hq / Hkv
   int64_t delta;    // q_pos0 - k_pos0: key j is visible to query i iff j <= delta + i (causal)
@@ -67,6 +74,12 @@ struct BwdParams {
   View q, k, v, o, dout;
   MView dq, dk, dv;
   const float* lse;
+  int64_t lse_sb, lse_sh, lse_ss;  // element strides of lse over (batch, head, query)
+  // Packed variable-length batches, as in FwdParams; dq_acc is then
+  // [total queries, Hq, D] and the statistics of sequence b start at
+  // b * Hq * 2 * Sq_pad with Sq_pad from the longest sequence.
+  const int* cu_q;
+  const int* cu_k;
   // Per-row statistics workspace: for each (b, h), Sq_pad floats of LSE*log2(e)
   // (+inf on rows that see no key and on padding rows) followed by Sq_pad
   // floats of delta (0 on padding rows).  Sq_pad = Sq rounded up to 64.

@@ -407,7 +407,7 @@ struct KeySeg {
 };
 
 template <int D, class Seg>
-__device__ __forceinline__ void dq_body(const BwdParams& p, int n_seg, Seg seg) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int unit, int n_seg, Seg seg) {
   constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
   constexpr int NLD = 2 * (SwTile<D>::RUNS / 8);  // loads per tile per wavefront
   // Key ring, then value ring; after the loop the start holds the partial dQ^T
@@ -418,10 +418,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int n_seg, Seg seg) 
   u16* const v_s = tiles + DQ_STAGES * SZ;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 31, lg = lane >> 5, pair = wave & 3, kh = wave >> 2;
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int unit = lin % p.n_qtiles;
-  const int bh = lin / p.n_qtiles;
-  const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
+  const int hk = h / p.group;
   // Causal: late query tiles see the most keys; start with them.
   const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
   const int q0 = qt * QBM;
@@ -617,7 +614,10 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int n_seg, Seg seg) 
 
 template <int D>
 __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
-  dq_body<D>(p, 1, [&](int, int b, int hk) {
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = lin % p.n_qtiles;
+  const int bh = lin / p.n_qtiles;
+  dq_body<D>(p, bh / p.Hq, bh % p.Hq, unit, 1, [&](int, int b, int hk) {
     return KeySeg{(const u16*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh,
                   (const u16*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh, p.Sk, p.delta_pos};
   });
@@ -625,10 +625,65 @@ __global__ __launch_bounds__(DQ_NT) void dq_bf16_kernel(BwdParams p) {
 
 template <int D>
 __global__ __launch_bounds__(DQ_NT) void dq_chunks_kernel(BwdParams p, BwdChunkTable ct) {
-  dq_body<D>(p, ct.kv.n, [&](int c, int b, int hk) {
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = lin % p.n_qtiles;
+  const int bh = lin / p.n_qtiles;
+  dq_body<D>(p, bh / p.Hq, bh % p.Hq, unit, ct.kv.n, [&](int c, int b, int hk) {
     return KeySeg{(const u16*)ct.kv.k[c] + (int64_t)b * ct.kv.kb[c] + (int64_t)hk * p.k.sh,
                   (const u16*)ct.kv.v[c] + (int64_t)b * ct.kv.vb[c] + (int64_t)hk * p.v.sh, ct.kv.len[c],
                   ct.kv.q_pos0 - ct.kv.pos0[c]};
+  });
+}
+
+// Packed variable-length batches: the workgroup's sequence b is read from the
+// offsets, every pointer is moved to the sequence's first row, and the tile
+// code runs with that sequence's lengths (clamped to the declared longest ones)
+// and its queries aligned to the end of its keys.  Units past the sequence's
+// tiles exit at once, before any barrier.
+__device__ __forceinline__ BwdParams varlen_seq(const BwdParams& p, int b, int D) {
+  const int q_beg = p.cu_q[b], k_beg = p.cu_k[b];
+  BwdParams s = p;
+  s.Sq = min(max(p.cu_q[b + 1] - q_beg, 0), p.Sq);
+  s.Sk = min(max(p.cu_k[b + 1] - k_beg, 0), p.Sk);
+  s.delta_pos = (int64_t)s.Sk - s.Sq;
+  s.q.ptr = (const u16*)p.q.ptr + (int64_t)q_beg * p.q.ss;
+  s.dout.ptr = (const u16*)p.dout.ptr + (int64_t)q_beg * p.dout.ss;
+  s.k.ptr = (const u16*)p.k.ptr + (int64_t)k_beg * p.k.ss;
+  s.v.ptr = (const u16*)p.v.ptr + (int64_t)k_beg * p.v.ss;
+  s.dk.ptr = (u16*)p.dk.ptr + (int64_t)k_beg * p.dk.ss;
+  s.dv.ptr = (u16*)p.dv.ptr + (int64_t)k_beg * p.dv.ss;
+  if (p.dq.ptr) s.dq.ptr = (u16*)p.dq.ptr + (int64_t)q_beg * p.dq.ss;
+  s.dq_acc = p.dq_acc + (int64_t)q_beg * p.Hq * D;
+  s.stats = p.stats + (int64_t)b * p.Hq * 2 * p.Sq_pad;
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(DKV_NT) void dkdv_varlen_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) u16 q_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) float st_s[3][256];
+  __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hkv, p.n_units_k);
+  const int unit = w.unit, hk = w.h, b = w.b;
+  BwdParams s = varlen_seq(p, b, D);
+  s.n_ktiles = (s.Sk + KBN - 1) / KBN;
+  if (unit >= (p.balanced ? (s.n_ktiles + 1) / 2 : s.n_ktiles)) return;
+  if (wave < 4) dkdv_unit<D, true>(s, q_s, d_s, st_s, pex_s, wave, lane, unit, 0, hk);
+  else dkdv_unit<D, false>(s, q_s, d_s, st_s, pex_s, wave, lane, unit, 0, hk);
+}
+
+template <int D>
+__global__ __launch_bounds__(DQ_NT) void dq_varlen_kernel(BwdParams p) {
+  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hq, p.n_qtiles);
+  const int unit = w.unit, h = w.h, b = w.b;
+  BwdParams s = varlen_seq(p, b, D);
+  s.n_qtiles = (s.Sq + QBM - 1) / QBM;
+  if (unit >= s.n_qtiles) return;
+  dq_body<D>(s, 0, h, unit, 1, [&](int, int, int hk) {
+    return KeySeg{(const u16*)s.k.ptr + (int64_t)hk * s.k.sh, (const u16*)s.v.ptr + (int64_t)hk * s.v.sh, s.Sk,
+                  s.delta_pos};
   });
 }
 
@@ -640,20 +695,23 @@ hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s
   p.n_units_k = p.balanced ? (p.n_ktiles + 1) / 2 : p.n_ktiles;
   p.n_qtiles = (p.Sq + QBM - 1) / QBM;
   const int64_t gk = (int64_t)p.B * p.Hkv * p.n_units_k;
+  const bool vl = p.cu_q != nullptr;
   if (gk > 0) {
     if (D == 128)
-      hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p);
+      hipLaunchKernelGGL(vl ? dkdv_varlen_kernel<128> : dkdv_bf16_kernel<128>, dim3((unsigned)gk), dim3(DKV_NT), 0,
+                         s, p);
     else
-      hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3((unsigned)gk), dim3(DKV_NT), 0, s, p);
+      hipLaunchKernelGGL(vl ? dkdv_varlen_kernel<64> : dkdv_bf16_kernel<64>, dim3((unsigned)gk), dim3(DKV_NT), 0, s,
+                         p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (run_dq && gq > 0) {
     if (D == 128)
-      hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
+      hipLaunchKernelGGL(vl ? dq_varlen_kernel<128> : dq_bf16_kernel<128>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
     else
-      hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
+      hipLaunchKernelGGL(vl ? dq_varlen_kernel<64> : dq_bf16_kernel<64>, dim3((unsigned)gq), dim3(DQ_NT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;

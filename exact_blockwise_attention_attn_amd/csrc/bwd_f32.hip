@@ -26,16 +26,23 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
   const int c = (int)(gid % TPR);
   const int64_t rows = (int64_t)p.B * p.Hq * p.Sq_pad;
   const bool ok = row < rows;
-  int i = 0;
-  int64_t bh = 0;
+  int i = 0, h = 0, b = 0, sq = 0;
+  int64_t bh = 0, r0 = 0;  // r0: first row of the sequence (packed variable-length batches)
   float acc = 0.f;
   if (ok) {
     i = (int)(row % p.Sq_pad);
     bh = row / p.Sq_pad;
-    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    if (i < p.Sq) {
-      const int64_t oo = (int64_t)b * p.o.sb + (int64_t)i * p.o.ss + (int64_t)h * p.o.sh + c * 8;
-      const int64_t od = (int64_t)b * p.dout.sb + (int64_t)i * p.dout.ss + (int64_t)h * p.dout.sh + c * 8;
+    h = (int)(bh % p.Hq);
+    b = (int)(bh / p.Hq);
+    sq = p.Sq;
+    if (p.cu_q) {
+      r0 = p.cu_q[b];
+      sq = min(max(p.cu_q[b + 1] - p.cu_q[b], 0), p.Sq);  // never past the declared longest length
+      b = 0;
+    }
+    if (i < sq) {
+      const int64_t oo = (int64_t)b * p.o.sb + (r0 + i) * p.o.ss + (int64_t)h * p.o.sh + c * 8;
+      const int64_t od = (int64_t)b * p.dout.sb + (r0 + i) * p.dout.ss + (int64_t)h * p.dout.sh + c * 8;
       if (BF16) {
         const u32x4 a = *(const u32x4*)((const u16*)p.o.ptr + oo);
         const u32x4 g = *(const u32x4*)((const u16*)p.dout.ptr + od);
@@ -57,12 +64,12 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
   if (ok && c == 0) {
     float* base = p.stats + bh * 2 * p.Sq_pad;
     float l2 = pos_inf();
-    if (i < p.Sq) {
-      const float lse = p.lse[bh * p.Sq + i];
+    if (i < sq) {
+      const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (r0 + i) * p.lse_ss];
       l2 = (lse == neg_inf()) ? pos_inf() : lse * kLog2e;
     }
     base[i] = l2;
-    base[p.Sq_pad + i] = (i < p.Sq) ? acc : 0.f;
+    base[p.Sq_pad + i] = (i < sq) ? acc : 0.f;
   }
 }
 
@@ -110,8 +117,7 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
     dO[f] = qok ? dob[(int64_t)qi * p.dout.ss + f0 + f] : 0.f;
     dq[f] = 0.f;
   }
-  const int64_t srow = ((int64_t)b * p.Hq + h) * p.Sq + qi;
-  const float lse = qok ? p.lse[srow] : neg_inf();
+  const float lse = qok ? p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss] : neg_inf();
   const float dlt = qok ? p.stats[((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad + qi] : 0.f;
   const bool live = lse != neg_inf();
   const int q_last = min(qt * FROWS + FROWS, p.Sq) - 1;
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
     const int h = hk * p.group + hh;
     const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
-    const float* lseb = p.lse + ((int64_t)b * p.Hq + h) * p.Sq;
+    const float* lseb = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
     const float* dltb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad;
     for (int i0 = i_start; i0 < p.Sq; i0 += FTK) {
       __syncthreads();
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
       }
       if (tid < FTK) {
         const int i = i0 + tid;
-        ls[tid] = (i < p.Sq) ? lseb[i] : neg_inf();
+        ls[tid] = (i < p.Sq) ? lseb[(int64_t)i * p.lse_ss] : neg_inf();
         ds_[tid] = (i < p.Sq) ? dltb[i] : 0.f;
       }
       __syncthreads();

@@ -159,7 +159,7 @@ __device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x16* oacc
   if (!qok) return;
   const float lse_this = (l_tot > 0.f) ? fmaf(st.m, p.scale, logf(l_tot)) : neg_inf();
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Sq + qi;
+  float* lse_ptr = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss;
   float w_old = 0.f, w_new = 1.f, L = lse_this;
   if (p.accumulate) merge_weights(*lse_ptr, lse_this, w_old, w_new, L);
   w_new *= inv;
@@ -277,6 +277,45 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
     // Causal: heaviest tiles first, so the light ones fill the tail.
     const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
     fwd_tile<D>(p, k0s, v0s, k1s, v1s, qt, b, h, qb, kb, vb);
+  }
+}
+
+// Packed variable-length batches: workgroup (sequence b, head h, unit) runs the
+// same tiles with every pointer moved to the sequence's first row, that
+// sequence's lengths, and its queries aligned to the end of its keys (query i
+// sees keys j <= i + Sk_b - Sq_b).  Lengths are clamped to the declared longest
+// ones; units past a sequence's tiles exit at once.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void fwd_varlen_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
+  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hq, p.n_units);
+  const int unit = w.unit, h = w.h, b = w.b;
+  const int hk = h / p.group;
+  const int q_beg = p.cu_q[b], k_beg = p.cu_k[b];
+  FwdParams s = p;
+  s.Sq = min(max(p.cu_q[b + 1] - q_beg, 0), p.Sq);
+  s.Sk = min(max(p.cu_k[b + 1] - k_beg, 0), p.Sk);
+  s.delta = (int64_t)s.Sk - s.Sq;
+  s.n_qtiles = (s.Sq + BM - 1) / BM;
+  const int64_t o_el = p.o_f32 ? 4 : 2;
+  s.o.ptr = (char*)p.o.ptr + (int64_t)q_beg * p.o.ss * o_el;
+  if (p.o_final.ptr) s.o_final.ptr = (u16*)p.o_final.ptr + (int64_t)q_beg * p.o_final.ss;
+  s.lse = p.lse + (int64_t)q_beg * p.lse_ss;
+  const u16* qb = (const u16*)p.q.ptr + (int64_t)q_beg * p.q.ss + (int64_t)h * p.q.sh;
+  const u16* kb = (const u16*)p.k.ptr + (int64_t)k_beg * p.k.ss + (int64_t)hk * p.k.sh;
+  const u16* vb = (const u16*)p.v.ptr + (int64_t)k_beg * p.v.ss + (int64_t)hk * p.v.sh;
+  if (p.balanced) {
+    const int t0 = unit, t1 = s.n_qtiles - 1 - unit;
+    if (t1 < t0) return;
+    fwd_tile<D>(s, k0s, v0s, k1s, v1s, t1, 0, h, qb, kb, vb);
+    if (t0 != t1) fwd_tile<D>(s, k0s, v0s, k1s, v1s, t0, 0, h, qb, kb, vb);
+  } else {
+    if (unit >= s.n_qtiles) return;
+    const int qt = p.causal ? s.n_qtiles - 1 - unit : unit;
+    fwd_tile<D>(s, k0s, v0s, k1s, v1s, qt, 0, h, qb, kb, vb);
   }
 }
 
@@ -437,6 +476,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
   p.n_units = p.balanced ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   const int64_t grid = (int64_t)p.B * p.Hq * p.n_units;
   if (grid == 0) return hipSuccess;
+  if (p.cu_q) {
+    if (D == 128)
+      hipLaunchKernelGGL(fwd_varlen_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    else
+      hipLaunchKernelGGL(fwd_varlen_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+  }
   if (D == 128)
     hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);
   else

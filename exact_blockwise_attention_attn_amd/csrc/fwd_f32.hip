@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   if (!qok) return;
   const float lse_this = (m_run == neg_inf()) ? neg_inf() : m_run + logf(l_run);
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
-  float* lse_ptr = p.lse + ((int64_t)b * p.Hq + h) * p.Sq + qi;
+  float* lse_ptr = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss;
   // The row's 16 lanes are in one wavefront: all read the running LSE before lane 0 writes it.
   float w_old = 0.f, w_new = 1.f, L = lse_this;
   if (p.accumulate) merge_weights(*lse_ptr, lse_this, w_old, w_new, L);

@@ -65,7 +65,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -95,6 +95,21 @@ extern "C" {
  * merged one; a chunk that no query can see then changes nothing.  If o_final is
  * not NULL, the (merged) output is also written there as bf16.
  * Aliasing: o, lse and o_final must not overlap q, k, v or each other.
+ *
+ * Packed variable-length batches (cu_seqlens_q and cu_seqlens_k not NULL; the
+ * variable-length form of the pages' per-device shards): `batch` sequences
+ * are packed along the sequence axis.  cu_seqlens_q and cu_seqlens_k are
+ * device int32 arrays of batch + 1 non-decreasing offsets starting at 0;
+ * sequence b's queries are rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 of q
+ * and o, its keys rows cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of k and v,
+ * and the batch strides are ignored.  seqlen_q and seqlen_k must be at least
+ * the longest query and key lengths (they size the launch; longer sequences
+ * are cut to them).  Sequence b's query i sits at position
+ * i + len_k(b) - len_q(b) and key j at position j (the queries are the last
+ * len_q(b) positions of the sequence), so q_pos0 and k_pos0 must be 0.  lse is
+ * then [total queries, heads_q] fp32.  dtype must be ATTN_DTYPE_BF16.  The
+ * offsets are read on the device; offsets outside the tensors are the
+ * caller's error and are not detected.
  */
 typedef struct attn_fwd_args {
   uint32_t struct_size;
@@ -116,6 +131,8 @@ typedef struct attn_fwd_args {
   int32_t causal;
   float scale;
   uint32_t flags; /* ATTN_FWD_* */
+  const int32_t* cu_seqlens_q; /* packed variable-length batches: device [batch + 1], or NULL */
+  const int32_t* cu_seqlens_k; /* device [batch + 1], or NULL */
 } attn_fwd_args;
 
 ATTN_API int attn_fwd_partial(const attn_fwd_args* args, void* stream);
@@ -228,12 +245,19 @@ ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
  * 256-byte aligned) holds the per-row statistics: for each (b, h) in row-major
  * order, Sq_pad = round_up(seqlen_q, 64) floats of LSE * log2(e) (+inf for rows
  * with LSE = -inf and for padding rows) followed by Sq_pad floats of delta (0 on
- * padding rows).  ATTN_BWD_COMPUTE_DELTA fills it; later calls for other key
+ * padding rows; in a packed variable-length batch b is the sequence, and rows
+ * past its length are padding).  ATTN_BWD_COMPUTE_DELTA fills it; later calls for other key
  * chunks of the same o, dout and lse may reuse it without the flag.  A row with
  * LSE = -inf must have no visible key; it contributes nothing.  A chunk no query
  * sees writes dk = dv = 0 and adds nothing to dq.  Results do not depend on
  * scheduling: no floating-point atomics are used.  dq, dk, dv are written in
  * `dtype`.
+ *
+ * Packed variable-length batches (cu_seqlens_q and cu_seqlens_k not NULL) are
+ * laid out and positioned as for attn_fwd_partial: q, o, dout, dq rows and k,
+ * v, dk, dv rows are packed per sequence, lse is [total queries, heads_q],
+ * dq_acc is [total queries, heads_q, head_dim] fp32 contiguous, seqlen_q and
+ * seqlen_k are the longest lengths, and q_pos0 = k_pos0 = 0.  bf16 only.
  */
 typedef struct attn_bwd_args {
   uint32_t struct_size;
@@ -263,6 +287,8 @@ typedef struct attn_bwd_args {
   int32_t causal;
   float scale;
   uint32_t flags; /* ATTN_BWD_* */
+  const int32_t* cu_seqlens_q; /* packed variable-length batches: device [batch + 1], or NULL */
+  const int32_t* cu_seqlens_k; /* device [batch + 1], or NULL */
 } attn_bwd_args;
 
 ATTN_API int attn_bwd(const attn_bwd_args* args, void* stream);

@@ -61,6 +61,8 @@ int main(void) {
   P(attn_fwd_chunks_args, o_final_stride); P(attn_fwd_chunks_args, q_pos0); P(attn_fwd_chunks_args, flags);
   P(attn_fwd_chunks_args, chunk_v_bstride); P(attn_fwd_chunks_args, o);
   P(attn_fwd_args, flags); P(attn_fwd_args, o_final_stride); P(attn_fwd_args, q_pos0);
+  P(attn_fwd_args, cu_seqlens_q); P(attn_fwd_args, cu_seqlens_k);
+  P(attn_bwd_args, cu_seqlens_q); P(attn_bwd_args, cu_seqlens_k);
   P(attn_merge_args, mode); P(attn_merge_args, lse_out);
   P(attn_bwd_args, flags); P(attn_bwd_args, dv_stride); P(attn_bwd_args, dq_acc);
   P(attn_bwd_args, workspace); P(attn_bwd_args, workspace_bytes);
@@ -90,7 +92,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -279,6 +281,36 @@ def test_fwd_chunks_empty_query_is_noop(lib):
     # No query rows: nothing is launched and no pointer is dereferenced.
     a = chunks_args(seqlen_q=0, q=None, o=None, lse=None)
     assert lib.attn_fwd_chunks(ctypes.byref(a), None) == B.ATTN_OK
+
+
+VARLEN_BAD = [
+    (dict(cu_seqlens_k=None), B.ATTN_ERR_INVALID_ARG, "given together"),
+    (dict(cu_seqlens_q=FAKE + 2), B.ATTN_ERR_UNSUPPORTED, "4-byte aligned"),
+    (dict(q_pos0=5), B.ATTN_ERR_INVALID_ARG, "q_pos0 and k_pos0 must be 0"),
+    (dict(dtype=B.ATTN_DTYPE_F32), B.ATTN_ERR_UNSUPPORTED, "bf16 only"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", VARLEN_BAD, ids=[m for _, _, m in VARLEN_BAD])
+def test_varlen_rejects(lib, kw, code, msg):
+    kw = dict(kw)
+    kw.setdefault("cu_seqlens_q", FAKE)
+    kw.setdefault("cu_seqlens_k", FAKE + 256)
+    a = bwd_args(**kw)
+    assert lib.attn_bwd(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+    f = B.FwdArgs()
+    f.struct_size = ctypes.sizeof(B.FwdArgs)
+    f.dtype = kw.get("dtype", B.ATTN_DTYPE_BF16)
+    f.batch, f.heads_q, f.heads_kv, f.seqlen_q, f.seqlen_k, f.head_dim = 2, 2, 2, 32, 32, 64
+    f.q = f.k = f.v = f.o = f.lse = FAKE
+    f.o_dtype = B.ATTN_DTYPE_F32
+    st = B.I64x3(0, 2 * 64, 64)
+    f.q_stride = f.k_stride = f.v_stride = f.o_stride = st
+    f.q_pos0 = kw.get("q_pos0", 0)
+    f.cu_seqlens_q, f.cu_seqlens_k = kw["cu_seqlens_q"], kw["cu_seqlens_k"]
+    assert lib.attn_fwd_partial(ctypes.byref(f), None) == code
+    assert msg in lib.attn_last_error().decode()
 
 
 def bwd_chunks_args(lens=(64, 0), **kw):

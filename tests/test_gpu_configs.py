@@ -161,6 +161,62 @@ def test_fp32_s256_4chunks():
             check(f"{name} (bound {bound or tol})", got, ref, bound or tol)
 
 
+VARLEN_K = (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10)  # sequence lengths / 512, as benchmarked
+
+
+def test_varlen_packed_70k():
+    """The packed variable-length workload at its benchmarked size: 16 causal sequences of
+    512 k tokens (k = 1..16), H = 32, d = 128.  Every sequence and head: row 0 equals v_0 and
+    the two gradient sum rules; two (sequence, head) pairs in full against the oracle."""
+    H, D, wid = 32, 128, 6
+    lens = [512 * k for k in VARLEN_K]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, mx = int(cu[-1]), max(lens)
+    log(f"varlen_packed_70k: {len(lens)} sequences, {T} tokens")
+    bits = [normal_bf16(wid, t, 1, (T, H, D), threads=16)[0] for t in range(4)]
+    q, k, v, do = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
+    cud = torch.from_numpy(cu).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    B.attn_fwd_varlen(q, k, v, o, lse, cud, cud, mx, mx, causal=True, balanced=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_acc = torch.empty((T, H, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.attn_bwd_workspace_size(len(lens), H, mx), dtype=torch.uint8, device="cuda")
+    B.attn_bwd_varlen(q, k, v, o, do, lse, ws, dq_acc, dk, dv, cud, cud, mx, mx, dq=dq, causal=True,
+                      compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=True)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(D)
+    starts = torch.from_numpy(cu[:-1].astype(np.int64)).cuda()
+    assert torch.equal(o[starts], v[starts]), "row 0 of every sequence must equal its v_0 exactly"
+    lse0 = np.einsum("shd,shd->sh", _f64(bits[0][cu[:-1]]), _f64(bits[1][cu[:-1]])) * scale
+    check("LSE row 0, every sequence and head", lse[starts], lse0, 1e-3)
+    worst_k = worst_v = 0.0
+    for a, e in zip(cu[:-1], cu[1:]):
+        worst_k = max(worst_k, _sum_rule_quiet(dk[a:e][None], 0.0))
+        worst_v = max(worst_v, _sum_rule_quiet(dv[a:e][None], do[a:e][None].double().sum(1)))
+    log(f"  sum rules over 16 sequences x 32 heads: dK {worst_k:.3e}, dV {worst_v:.3e}")
+    assert worst_k < 1e-2 and worst_v < 1e-2
+    for s, h in ((4, 3), (6, 30)):  # a 512-token and a 2048-token sequence
+        a, e = int(cu[s]), int(cu[s + 1])
+        log(f"  oracle forward + backward for sequence {s} ({e - a} tokens), head {h}")
+        qh, kh, vh, doh = (_f64(b[a:e, h]) for b in bits)
+        O_ref, L_ref = oracle.attention_head(qh, kh, vh, scale, True)
+        check("O", o[a:e, h], O_ref, 1e-2)
+        check("LSE", lse[a:e, h], L_ref, 1e-3)
+        dq_r, dk_r, dv_r = oracle.attention_backward_head(qh, kh, vh, O_ref, doh, L_ref, scale, True)
+        for name, got, ref in (("dQ", dq[a:e, h], dq_r), ("dK", dk[a:e, h], dk_r), ("dV", dv[a:e, h], dv_r)):
+            check(name, got, ref, 2e-2)
+            err = _rel_fro(got, ref)
+            log(f"    {name} relative Frobenius error {err:.3e}")
+            assert err < 2e-2
+
+
+def _sum_rule_quiet(grads, target):
+    s = grads.double().sum(1)
+    a = grads.double().abs().sum(1)
+    return ((s - target).abs() / a.clamp_min(1e-30)).max().item()
+
+
 def test_decode_gqa_128k():
     w = WORKLOADS["decode_gqa_128k"]
     log("decode_gqa_128k: generating the 8 GiB KV cache")

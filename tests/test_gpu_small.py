@@ -367,6 +367,70 @@ def test_bwd_chunks_matches_chained_calls():
     assert err <= 1e-2 * max(1.0, dq1.float().abs().max().item())
 
 
+# (per-sequence (len_q, len_k), Hq, Hkv, D, causal, balanced)
+VARLEN_CASES = [
+    # equal lengths as in packed training, including an empty and a one-token sequence
+    (((200, 200), (1, 1), (0, 0), (130, 130), (64, 64)), 2, 2, 128, True, False),
+    # queries at the end of longer key sequences, grouped heads, head_dim 64
+    (((17, 300), (128, 129), (65, 65)), 4, 2, 64, True, True),
+    # more queries than keys: the first len_q - len_k queries see nothing
+    (((100, 60), (33, 200)), 2, 1, 128, True, False),
+    # non-causal
+    (((77, 250), (256, 3)), 2, 2, 128, False, False),
+]
+
+
+def _varlen_inputs(wid, lens, Hq, Hkv, D):
+    """Packed [total, heads, D] bf16 tensors and per-sequence fp64 views, plus offsets."""
+    cu_q = np.concatenate([[0], np.cumsum([a for a, _ in lens])]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum([b for _, b in lens])]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q, qh = seq_tensor(wid, 0, 1, tq, Hq, D, "bf16")
+    k, kh = seq_tensor(wid, 1, 1, tk, Hkv, D, "bf16")
+    v, vh = seq_tensor(wid, 2, 1, tk, Hkv, D, "bf16")
+    do, doh = seq_tensor(wid, 3, 1, tq, Hq, D, "bf16")
+    dev = [x[0] for x in (q, k, v, do)]
+    host = [x[0] for x in (qh, kh, vh, doh)]
+    return dev, host, torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda(), cu_q, cu_k
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=_ids(VARLEN_CASES))
+def test_varlen_fwd_bwd(case):
+    """Packed variable-length batch, forward and backward, against the oracle run on each
+    sequence alone with its queries at the end of its keys."""
+    lens, Hq, Hkv, D, causal, bal = case
+    log(f"varlen {case}")
+    (q, k, v, do), (qh, kh, vh, doh), cuq, cuk, cu_q, cu_k = _varlen_inputs(113, lens, Hq, Hkv, D)
+    mq, mk = max(a for a, _ in lens), max(b for _, b in lens)
+    scale = 1 / math.sqrt(D)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    o = torch.full((tq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((tq, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_fwd_varlen(q, k, v, o, lse, cuq, cuk, mq, mk, causal=causal, balanced=bal)
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    dq_acc = torch.full((tq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((B.attn_bwd_workspace_size(len(lens), Hq, mq) // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    B.attn_bwd_varlen(q, k, v, o, do, lse, ws, dq_acc, dk, dv, cuq, cuk, mq, mk, dq=dq, causal=causal,
+                      compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=bal)
+    torch.cuda.synchronize()
+    for s, (a0, a1, b0, b1) in enumerate(zip(cu_q[:-1], cu_q[1:], cu_k[:-1], cu_k[1:])):
+        if a1 == a0 and b1 == b0:
+            continue
+        qs, ks, vs, dos = qh[None, a0:a1], kh[None, b0:b1], vh[None, b0:b1], doh[None, a0:a1]
+        qp = int(b1 - b0) - int(a1 - a0)
+        O_ref, L_ref = oracle.attention(qs, ks, vs, scale, causal, qp, 0)
+        dq_r, dk_r, dv_r = oracle.attention_backward(qs, ks, vs, O_ref, dos, L_ref, scale, causal, qp, 0)
+        check(f"seq {s} O", o[a0:a1], O_ref[0], O_TOL, scale_by_max=True)
+        check(f"seq {s} LSE", lse[a0:a1], L_ref[0].T, L_TOL)
+        check(f"seq {s} dQ", dq[a0:a1], dq_r[0], G_TOL, scale_by_max=True)
+        check(f"seq {s} dQ acc", dq_acc[a0:a1], dq_r[0], G_TOL, scale_by_max=True)
+        check(f"seq {s} dK", dk[b0:b1], dk_r[0], G_TOL, scale_by_max=True)
+        check(f"seq {s} dV", dv[b0:b1], dv_r[0], G_TOL, scale_by_max=True)
+
+
 def test_bwd_deterministic():
     log("bwd determinism")
     (q, k, v), _ = _inputs(107, 1, 300, 300, 2, 2, 128, "bf16")
