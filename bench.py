@@ -231,17 +231,15 @@ def bench_fp32_small(args, stream):
             "note": "4 chained chunk calls each way; latency-bound, no roofline"}
 
 
-VARLEN_LENGTHS = (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10)  # x 512 tokens: every k in 1..16 once
-
-
 def bench_varlen(args, stream):
     """Packed variable-length batch: 16 causal sequences of 512 k tokens (k = 1..16), H = 32, d = 128, bf16."""
     import torch
 
     from exact_blockwise_attention_attn_amd import binding
+    from seeded_inputs import VARLEN_PACKED as W
 
-    H, D = 32, 128
-    lens = [512 * k for k in VARLEN_LENGTHS]
+    H, D = W["H"], W["D"]
+    lens = [W["unit"] * k for k in W["k"]]
     cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32, device="cuda")
     T, mx = sum(lens), max(lens)
     g = torch.Generator(device="cuda")

@@ -70,3 +70,8 @@ WORKLOADS = {
         wid=5, name="causal_fwdbwd_32k", dtype="bf16", B=2, H_q=32, H_kv=32,
         S_q=32768, S_k=32768, D=128, causal=True, n_chunks=16, balanced=True),
 }
+
+# Packed variable-length batch: causal sequences of unit * k tokens for each k
+# in the order given (every k in 1..16 once), H heads of dimension D.
+VARLEN_PACKED = {"wid": 6, "name": "varlen_packed_70k", "unit": 512,
+                 "k": (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10), "H": 32, "D": 128}

@@ -25,7 +25,7 @@ import torch
 import oracle
 from exact_blockwise_attention_attn_amd import binding as B
 from exact_blockwise_attention_attn_amd import shard
-from seeded_inputs import WORKLOADS, bf16_bits_to_f32, normal_bf16, normal_f32
+from seeded_inputs import VARLEN_PACKED, WORKLOADS, bf16_bits_to_f32, normal_bf16, normal_f32
 from tests.gpu_util import check, log, to_np
 
 pytestmark = pytest.mark.gpu
@@ -161,15 +161,12 @@ def test_fp32_s256_4chunks():
             check(f"{name} (bound {bound or tol})", got, ref, bound or tol)
 
 
-VARLEN_K = (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10)  # sequence lengths / 512, as benchmarked
-
-
 def test_varlen_packed_70k():
     """The packed variable-length workload at its benchmarked size: 16 causal sequences of
     512 k tokens (k = 1..16), H = 32, d = 128.  Every sequence and head: row 0 equals v_0 and
     the two gradient sum rules; two (sequence, head) pairs in full against the oracle."""
-    H, D, wid = 32, 128, 6
-    lens = [512 * k for k in VARLEN_K]
+    H, D, wid = VARLEN_PACKED["H"], VARLEN_PACKED["D"], VARLEN_PACKED["wid"]
+    lens = [VARLEN_PACKED["unit"] * k for k in VARLEN_PACKED["k"]]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T, mx = int(cu[-1]), max(lens)
     log(f"varlen_packed_70k: {len(lens)} sequences, {T} tokens")
