@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "fp32_small", "varlen", "copy"], default=None,
+    ap.add_argument("--only", choices=["main", "shard_fwd", "shard_bwd", "decode", "fp32_small", "varlen", "tree", "copy"], default=None,
                     help="run a single workload (for profiling); 'copy' runs a plain 1 GiB device copy that "
                          "calibrates the HBM traffic counters")
     return ap.parse_args()
@@ -267,6 +267,54 @@ def bench_varlen(args, stream):
             "fwd_tflops": f_fwd / tf / 1e9, "bwd_tflops": f_bwd / tb / 1e9}
 
 
+def bench_tree_decode(args, stream):
+    """Tree-structured decode (64 queries under one 32K-token root, 8 children of 4K, 8 leaves of 512 each)
+    against split-KV decode of the same queries over their materialised per-query caches."""
+    import torch
+
+    from exact_blockwise_attention_attn_amd import binding
+    from seeded_inputs import TREE_DECODE as T
+    from seeded_inputs import tree_nodes
+
+    nodes = tree_nodes(T)
+    nq = T["children"] * T["leaves"]
+    L = T["root"] + T["children"] * (T["child_len"] + T["leaves"] * T["leaf_len"])
+    Hq, Hkv, D = T["H_q"], T["H_kv"], T["D"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    q = randn_bf16((nq, Hq, D), g)
+    kc, vc = randn_bf16((L, Hkv, D), g), randn_bf16((L, Hkv, D), g)
+    ks, kl, qb, qe = zip(*nodes)
+    o = torch.empty((nq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((nq, Hq), dtype=torch.float32, device="cuda")
+    need = binding.attn_decode_tree_workspace_size(q, kc, kv_start=ks, kv_len=kl, q_begin=qb, q_end=qe)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def tree():
+        binding.attn_decode_tree(q, kc, vc, o, lse, ws, kv_start=ks, kv_len=kl, q_begin=qb, q_end=qe, stream=stream)
+
+    # The same queries over materialised caches: each query's path keys copied out (not timed).
+    path = T["root"] + T["child_len"] + T["leaf_len"]
+    rows = []
+    for i in range(nq):
+        rows.append(torch.cat([torch.arange(s, s + n) for s, n, b, e in nodes if b <= i < e]))
+    idx = torch.stack(rows).cuda()
+    kp, vp = kc[idx], vc[idx]  # [nq, path, Hkv, D]
+    o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+    ns = 16
+    ws2 = torch.empty(binding.attn_decode_workspace_size(nq, Hq, D, ns), dtype=torch.uint8, device="cuda")
+
+    def flat():
+        binding.attn_decode_splitkv(q, kp, vp, o2, l2, ws2, n_splits=ns, stream=stream)
+
+    (tt, tf), _ = time_calls([tree, flat], max(10, args.steps), 3, stream)
+    uniq = 2.0 * L * Hkv * D * 2
+    flat_bytes = 2.0 * nq * path * Hkv * D * 2
+    return {"workload": "tree_decode_64q", "queries": nq, "nodes": len(nodes), "tree_ms": tt,
+            "unique_kv_bytes": uniq, "unique_gbs": uniq / tt / 1e6, "frac_hbm_unique": uniq / tt / 1e6 / HBM_PEAK_GBS,
+            "flat_splitkv_ms": tf, "flat_kv_bytes": flat_bytes, "speedup_vs_flat": tf / tt}
+
+
 def bench_decode(args, stream):
     import torch
 
@@ -345,6 +393,9 @@ def main():
     if args.only == "varlen":
         print(json.dumps(bench_varlen(args, stream)), flush=True)
         return
+    if args.only == "tree":
+        print(json.dumps(bench_tree_decode(args, stream)), flush=True)
+        return
     if args.only == "copy":
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -368,6 +419,8 @@ def main():
         torch.cuda.empty_cache()
         secondary["fp32_s256_4chunks"] = bench_fp32_small(args, stream)
         secondary["varlen_packed_70k"] = bench_varlen(args, stream)
+        torch.cuda.empty_cache()
+        secondary["tree_decode_64q"] = bench_tree_decode(args, stream)
         torch.cuda.empty_cache()
     cpu = None if (args.no_cpu_baseline or args.only) else cpu_baseline()
     bwd_achieved = m["bwd_tflops"]

@@ -144,6 +144,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodeTreeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32),
+        ("n_queries", c_i32), ("heads_q", c_i32), ("heads_kv", c_i32), ("head_dim", c_i32),
+        ("n_nodes", c_i32), ("cache_len", c_i64),
+        ("q", c_vp), ("q_stride", I64x2),
+        ("k_cache", c_vp), ("k_stride", I64x2),
+        ("v_cache", c_vp), ("v_stride", I64x2),
+        ("kv_start", ctypes.POINTER(c_i64)), ("kv_len", ctypes.POINTER(c_i32)),
+        ("q_begin", ctypes.POINTER(c_i32)), ("q_end", ctypes.POINTER(c_i32)),
+        ("scale", c_f32),
+        ("o", c_vp), ("o_stride", I64x2),
+        ("lse", c_vp),
+        ("workspace", c_vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 EXPORTED = [
     "attn_fwd_partial",
     "attn_fwd_chunks",
@@ -151,6 +168,8 @@ EXPORTED = [
     "attn_bwd",
     "attn_bwd_chunks",
     "attn_decode_splitkv",
+    "attn_decode_tree",
+    "attn_decode_tree_workspace_size",
     "attn_bwd_workspace_size",
     "attn_decode_workspace_size",
     "attn_status_string",
@@ -189,7 +208,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                            ("attn_merge_lse", [ctypes.POINTER(MergeArgs), c_vp]),
                            ("attn_bwd", [ctypes.POINTER(BwdArgs), c_vp]),
                            ("attn_bwd_chunks", [ctypes.POINTER(BwdChunksArgs), c_vp]),
-                           ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp])):
+                           ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp]),
+                           ("attn_decode_tree", [ctypes.POINTER(DecodeTreeArgs), c_vp])):
             fn = getattr(lib, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
@@ -197,6 +217,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_decode_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
         lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+        lib.attn_decode_tree_workspace_size.argtypes = [ctypes.POINTER(DecodeTreeArgs)]
+        lib.attn_decode_tree_workspace_size.restype = ctypes.c_size_t
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -259,6 +281,46 @@ def attn_bwd_workspace_size(batch: int, heads_q: int, seqlen_q: int) -> int:
 
 def attn_decode_workspace_size(batch: int, heads_q: int, head_dim: int, n_splits: int) -> int:
     return load().attn_decode_workspace_size(batch, heads_q, head_dim, n_splits)
+
+
+def _tree_args(q, k_cache, v_cache, o, lse, workspace, kv_start, kv_len, q_begin, q_end, scale):
+    n = len(kv_start)
+    assert len(kv_len) == n and len(q_begin) == n and len(q_end) == n
+    a = DecodeTreeArgs()
+    a.struct_size = ctypes.sizeof(DecodeTreeArgs)
+    a.n_queries, a.heads_q, a.head_dim = q.shape
+    a.heads_kv = k_cache.shape[1]
+    a.n_nodes = n
+    a.cache_len = k_cache.shape[0]
+    a.q, a.q_stride = _ptr(q), I64x2(q.stride(0), q.stride(1))
+    a.k_cache, a.k_stride = _ptr(k_cache), I64x2(k_cache.stride(0), k_cache.stride(1))
+    if v_cache is not None:
+        a.v_cache, a.v_stride = _ptr(v_cache), I64x2(v_cache.stride(0), v_cache.stride(1))
+    a.kv_start = (c_i64 * max(n, 1))(*[int(x) for x in kv_start])
+    a.kv_len = (c_i32 * max(n, 1))(*[int(x) for x in kv_len])
+    a.q_begin = (c_i32 * max(n, 1))(*[int(x) for x in q_begin])
+    a.q_end = (c_i32 * max(n, 1))(*[int(x) for x in q_end])
+    a.scale = float(scale)
+    if o is not None:
+        a.o, a.o_stride = _ptr(o), I64x2(o.stride(0), o.stride(1))
+    a.lse = _ptr(lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def attn_decode_tree_workspace_size(q, k_cache, *, kv_start, kv_len, q_begin, q_end) -> int:
+    """Workspace bytes attn_decode_tree needs for this tree (0 if the node lists are invalid)."""
+    a = _tree_args(q, k_cache, None, None, None, None, kv_start, kv_len, q_begin, q_end, 0.0)
+    return load().attn_decode_tree_workspace_size(ctypes.byref(a))
+
+
+def attn_decode_tree(q, k_cache, v_cache, o, lse, workspace, *, kv_start, kv_len, q_begin, q_end, scale=0.0,
+                     stream=None) -> None:
+    """q [n_q, Hq, D], packed caches [L, Hkv, D] bf16, node lists (host ints) -> o [n_q, Hq, D], lse [n_q, Hq]."""
+    assert q.stride(2) == 1 and k_cache.stride(2) == 1 and v_cache.stride(2) == 1 and o.stride(2) == 1
+    a = _tree_args(q, k_cache, v_cache, o, lse, workspace, kv_start, kv_len, q_begin, q_end, scale)
+    _check(load().attn_decode_tree(ctypes.byref(a), _stream(stream)))
 
 
 def attn_fwd_partial(q, k, v, o, lse, *, q_pos0=0, k_pos0=0, causal=False, scale=0.0,

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/attn.h"
@@ -495,6 +496,143 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   // Without queries the dK/dV kernel writes zeros for every chunk and no dQ pass runs.
   e = attn::launch_bwd_chunks_bf16(p, ct, a->head_dim, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunks launch");
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Nodes of a decode tree are cut into segments of at most `seg` keys (each a
+// table entry with the node's query range), so a long shared prefix is
+// streamed by many workgroups.  seg starts at kTreeSeg and doubles until the
+// segments fit the table.  Returns false (with the error set) on invalid nodes.
+constexpr int64_t kTreeSeg = 2048;
+bool tree_table(const attn_decode_tree_args* a, attn::TreeTable* tt, int64_t* entries, int* code) {
+  *tt = attn::TreeTable{};
+  *entries = 0;
+  if (a->n_nodes < 0 || a->n_nodes > ATTN_MAX_TREE_NODES) {
+    *code = fail(ATTN_ERR_INVALID_ARG, "n_nodes must be in [0, %d]", ATTN_MAX_TREE_NODES);
+    return false;
+  }
+  if (a->n_nodes > 0 && (!a->kv_start || !a->kv_len || !a->q_begin || !a->q_end)) {
+    *code = fail(ATTN_ERR_INVALID_ARG, "node arrays must not be NULL");
+    return false;
+  }
+  for (int n = 0; n < a->n_nodes; ++n) {
+    if (a->kv_len[n] < 0 || a->kv_start[n] < 0 || a->kv_start[n] + a->kv_len[n] > a->cache_len) {
+      *code = fail(ATTN_ERR_INVALID_ARG, "node %d: keys [%lld, %lld) outside the cache of %lld", n,
+                   (long long)a->kv_start[n], (long long)a->kv_start[n] + a->kv_len[n], (long long)a->cache_len);
+      return false;
+    }
+    if (a->q_begin[n] < 0 || a->q_end[n] < a->q_begin[n] || a->q_end[n] > a->n_queries) {
+      *code = fail(ATTN_ERR_INVALID_ARG, "node %d: queries [%d, %d) outside [0, %d)", n, a->q_begin[n], a->q_end[n],
+                   a->n_queries);
+      return false;
+    }
+  }
+  int64_t seg = kTreeSeg;
+  for (;;) {
+    int64_t pieces = 0;
+    for (int n = 0; n < a->n_nodes; ++n) pieces += std::max<int64_t>(1, (a->kv_len[n] + seg - 1) / seg);
+    if (pieces <= attn::kMaxTreeNodes) break;
+    seg *= 2;
+  }
+  for (int n = 0; n < a->n_nodes; ++n) {
+    const int64_t len = a->kv_len[n];
+    const int64_t np = std::max<int64_t>(1, (len + seg - 1) / seg);
+    for (int64_t j = 0; j < np; ++j) {
+      const int e = tt->n++;
+      tt->kv_start[e] = a->kv_start[n] + j * seg;
+      tt->kv_len[e] = (int)std::min(seg, len - j * seg);
+      tt->q_begin[e] = a->q_begin[n];
+      tt->q_end[e] = a->q_end[n];
+      tt->e0[e] = (int)*entries;
+      *entries += a->q_end[n] - a->q_begin[n];
+      tt->max_q = std::max(tt->max_q, a->q_end[n] - a->q_begin[n]);
+    }
+  }
+  if (*entries > 0x7fffffffLL / std::max(1, a->heads_q)) {
+    *code = fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    return false;
+  }
+  return true;
+}
+
+size_t tree_workspace_bytes(int64_t entries, int heads_q, int head_dim) {
+  const size_t rows = (size_t)entries * heads_q;
+  return ((rows * head_dim * 4 + 255) & ~(size_t)255) + ((rows * 4 + 255) & ~(size_t)255);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_tree_workspace_size(const attn_decode_tree_args* a) {
+  if (!a || a->struct_size < sizeof(attn_decode_tree_args) || a->heads_q < 1 ||
+      (a->head_dim != 64 && a->head_dim != 128))
+    return 0;
+  attn::TreeTable tt;
+  int64_t entries;
+  int code;
+  const std::string saved = g_last_error;
+  const bool okay = tree_table(a, &tt, &entries, &code);
+  g_last_error = saved;  // a size query leaves the last error as it was
+  return okay ? tree_workspace_bytes(entries, a->heads_q, a->head_dim) : 0;
+}
+
+int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
+  if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
+  if (a->struct_size < sizeof(attn_decode_tree_args))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_decode_tree_args));
+  if (a->n_queries < 0) return fail(ATTN_ERR_INVALID_ARG, "n_queries must be >= 0");
+  TRY(check_dims(1, a->heads_q, a->heads_kv, 1, 0, a->head_dim));
+  if (a->cache_len < 0) return fail(ATTN_ERR_INVALID_ARG, "cache_len must be >= 0");
+  float scale;
+  TRY(check_scale(a->scale, a->head_dim, &scale));
+  attn::TreeTable tt;
+  int64_t entries;
+  int code;
+  if (!tree_table(a, &tt, &entries, &code)) return code;
+  if (a->n_queries == 0) return ok();
+  TRY(check_view("q", a->q, a->q_stride, 2, ATTN_DTYPE_BF16, true));
+  TRY(check_view("k_cache", a->k_cache, a->k_stride, 2, ATTN_DTYPE_BF16, a->cache_len > 0));
+  TRY(check_view("v_cache", a->v_cache, a->v_stride, 2, ATTN_DTYPE_BF16, a->cache_len > 0));
+  TRY(check_view("o", a->o, a->o_stride, 2, ATTN_DTYPE_BF16, true));
+  if (!a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (!aligned16(a->lse)) return fail(ATTN_ERR_UNSUPPORTED, "lse is not 16-byte aligned");
+  const size_t need = tree_workspace_bytes(entries, a->heads_q, a->head_dim);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)a->workspace & 255u))
+    return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  // The per-segment pass is the forward over (the node's queries) x (the segment's
+  // keys), non-causal, writing fp32 partials [entries, heads_q, head_dim] and their
+  // LSE [entries, heads_q].
+  const size_t rows = (size_t)entries * a->heads_q;
+  attn::FwdParams p{};
+  p.q = attn::View{a->q, 0, a->q_stride[0], a->q_stride[1]};
+  p.k = attn::View{a->k_cache, 0, a->k_stride[0], a->k_stride[1]};
+  p.v = attn::View{a->v_cache, 0, a->v_stride[0], a->v_stride[1]};
+  p.o = attn::MView{a->workspace, 0, (int64_t)a->heads_q * a->head_dim, a->head_dim};
+  p.o_final = attn::MView{nullptr, 0, 0, 0};
+  p.lse = (float*)((char*)a->workspace + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
+  p.lse_sb = 0;
+  p.lse_sh = 1;
+  p.lse_ss = a->heads_q;
+  p.B = 1;
+  p.Hq = a->heads_q;
+  p.Hkv = a->heads_kv;
+  p.group = a->heads_q / a->heads_kv;
+  p.causal = 0;
+  p.o_f32 = 1;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_tree_decode(p, tt, a->n_queries, a->o, a->o_stride[0], a->o_stride[1], a->lse,
+                                          a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode_tree launch");
   return ok();
 }
 

@@ -111,6 +111,19 @@ struct BwdChunkTable {
   int n_units;
 };
 
+// Tree-structured decode: node n holds keys kv_start[n] .. + kv_len[n] - 1 of
+// the packed cache and is attended by queries q_begin[n] .. q_end[n] - 1; its
+// partial results go to workspace entries e0[n] .. e0[n] + (q_end - q_begin) - 1.
+constexpr int kMaxTreeNodes = 256;
+struct TreeTable {
+  int64_t kv_start[kMaxTreeNodes];
+  int kv_len[kMaxTreeNodes];
+  int q_begin[kMaxTreeNodes], q_end[kMaxTreeNodes];
+  int e0[kMaxTreeNodes];
+  int n;
+  int max_q;  // most queries of any node
+};
+
 struct DecodeParams {
   const uint16_t* q;
   int64_t q_sb, q_sh;
@@ -151,5 +164,11 @@ hipError_t launch_bwd_chunks_bf16(const BwdParams& p, const BwdChunkTable& ct, i
 hipError_t launch_bwd_f32(const BwdParams& p, int D, int run_dq, hipStream_t s);
 // Decode: split partials into the workspace, then the per-(b, h) tree merge.
 hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s);
+// Tree decode: p describes the queries (q, Hq, Hkv, group, scale), the packed
+// cache (k, v with their token and head strides), the fp32 partials (o as
+// [entries, Hq, D], lse as [entries, Hq]) and is the forward parameter block
+// of the per-node pass; the merge writes out_o [n_q, Hq, D] bf16 and out_lse.
+hipError_t launch_tree_decode(const FwdParams& p, const TreeTable& t, int n_q, void* out_o, int64_t out_o_sq,
+                              int64_t out_o_sh, float* out_lse, int D, hipStream_t s);
 
 }  // namespace attn

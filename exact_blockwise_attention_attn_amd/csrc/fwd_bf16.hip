@@ -319,6 +319,60 @@ __global__ __launch_bounds__(NT, 2) void fwd_varlen_kernel(FwdParams p) {
   }
 }
 
+// ------------------------------------------------------ tree decode -------
+//
+// Tree-structured decoding (DeFT under the Tree Attention page's related
+// papers): the queries below a node of a prefix tree share that node's keys.
+// Pass 1 reads each node's keys once per query head for all of its queries
+// (workgroup = node, head, tile of 128 of its queries), through the same tile
+// code as the forward, and writes a partial (O, LSE) per (node, query).
+// Pass 2 merges each query's partials in node order.
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void tree_fwd_kernel(FwdParams p, TreeTable tt) {
+  __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
+  __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
+  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hq, p.n_units);
+  const int n = w.b, h = w.h, unit = w.unit;
+  const int hk = h / p.group;
+  FwdParams s = p;
+  s.Sq = tt.q_end[n] - tt.q_begin[n];
+  s.Sk = tt.kv_len[n];
+  s.n_qtiles = (s.Sq + BM - 1) / BM;
+  if (unit >= s.n_qtiles) return;
+  s.o.ptr = (float*)p.o.ptr + (int64_t)tt.e0[n] * p.o.ss;
+  s.lse = p.lse + (int64_t)tt.e0[n] * p.lse_ss;
+  const u16* qb = (const u16*)p.q.ptr + (int64_t)tt.q_begin[n] * p.q.ss + (int64_t)h * p.q.sh;
+  const u16* kb = (const u16*)p.k.ptr + tt.kv_start[n] * p.k.ss + (int64_t)hk * p.k.sh;
+  const u16* vb = (const u16*)p.v.ptr + tt.kv_start[n] * p.v.ss + (int64_t)hk * p.v.sh;
+  fwd_tile<D>(s, k0s, v0s, k1s, v1s, unit, 0, h, qb, kb, vb);
+}
+
+// One workgroup per (query, head), one thread per feature: the partials of
+// the nodes whose query range holds the query, merged in node order.
+template <int D>
+__global__ __launch_bounds__(D) void tree_merge_kernel(const float* po, const float* pl, int Hq, TreeTable tt,
+                                                       u16* out_o, int64_t o_sq, int64_t o_sh, float* out_lse) {
+  const int i = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
+  float L = neg_inf(), O = 0.f;
+  for (int n = 0; n < tt.n; ++n) {
+    if (i < tt.q_begin[n] || i >= tt.q_end[n]) continue;
+    const int64_t e = (int64_t)tt.e0[n] + (i - tt.q_begin[n]);
+    const float lb = pl[e * Hq + h], ob = po[(e * Hq + h) * D + d];
+    float wa, wb, Ln;
+    merge_weights(L, lb, wa, wb, Ln);
+    float r = 0.f;
+    if (wa != 0.f) r += wa * O;
+    if (wb != 0.f) r += wb * ob;
+    O = r;
+    L = Ln;
+  }
+  out_o[(int64_t)i * o_sq + (int64_t)h * o_sh + d] = f32_to_bf16(O);
+  if (d == 0) out_lse[(int64_t)i * Hq + h] = L;
+}
+
 // ------------------------------------------------------ fused chunk table --
 //
 // The same tile step over the keys of several chunks, in chunk order, in one
@@ -487,6 +541,30 @@ hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
     hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);
   else
     hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_decode(const FwdParams& p0, const TreeTable& tt, int n_q, void* out_o, int64_t out_o_sq,
+                              int64_t out_o_sh, float* out_lse, int D, hipStream_t s) {
+  FwdParams p = p0;
+  p.n_units = (tt.max_q + BM - 1) / BM;
+  const int64_t grid = (int64_t)tt.n * p.Hq * p.n_units;
+  if (grid > 0) {
+    if (D == 128)
+      hipLaunchKernelGGL(tree_fwd_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, tt);
+    else
+      hipLaunchKernelGGL(tree_fwd_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, tt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t gm = (int64_t)n_q * p.Hq;
+  if (gm == 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL(tree_merge_kernel<128>, dim3((unsigned)gm), dim3(128), 0, s, (const float*)p.o.ptr, p.lse,
+                       p.Hq, tt, (u16*)out_o, out_o_sq, out_o_sh, out_lse);
+  else
+    hipLaunchKernelGGL(tree_merge_kernel<64>, dim3((unsigned)gm), dim3(64), 0, s, (const float*)p.o.ptr, p.lse, p.Hq,
+                       tt, (u16*)out_o, out_o_sq, out_o_sh, out_lse);
   return hipGetLastError();
 }
 

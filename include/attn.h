@@ -65,7 +65,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -399,6 +399,61 @@ typedef struct attn_decode_args {
 ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
 
 /* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
+#define ATTN_MAX_TREE_NODES 256
+
+/*
+ * attn_decode_tree: one decode query per leaf of a prefix tree whose nodes own
+ * segments of a packed KV cache (tree-structured decoding: DeFT, under the
+ * Tree Attention page's related papers).  Queries are numbered so that the
+ * queries below any node are contiguous (leaves in depth-first order): node n
+ * owns keys kv_start[n] .. kv_start[n] + kv_len[n] - 1 of the cache and is on
+ * the path of queries q_begin[n] .. q_end[n] - 1.  Query i attends, with no
+ * mask, every key of every node whose query range holds i; query head h reads
+ * key/value head h / (heads_q / heads_kv).  Each node's keys are read once per
+ * query head for all of its queries; the per-node partial results of a query
+ * are then merged in node order (list a node after its ancestors to merge root
+ * first).  A query that no node covers gets O = 0, LSE = -inf.
+ *
+ * q [n_queries, heads_q, head_dim] bf16 (strides q_stride = {query, head});
+ * k_cache, v_cache [cache_len, heads_kv, head_dim] bf16 (strides {token, head});
+ * o [n_queries, heads_q, head_dim] bf16 (strides o_stride); lse [n_queries, heads_q]
+ * fp32 contiguous.  kv_start, kv_len, q_begin and q_end are HOST arrays of
+ * n_nodes entries (0 <= n_nodes <= ATTN_MAX_TREE_NODES).  The workspace (device
+ * memory of at least attn_decode_tree_workspace_size(args) bytes, 256-byte
+ * aligned) receives the per-node partials and is overwritten.  Nodes with many
+ * keys are processed as segments of up to 2048 keys (more when the segments of
+ * all nodes would not fit ATTN_MAX_TREE_NODES table entries), each merged like
+ * a node of its own.
+ */
+typedef struct attn_decode_tree_args {
+  uint32_t struct_size;
+  int32_t n_queries, heads_q, heads_kv, head_dim;
+  int32_t n_nodes;
+  int64_t cache_len;
+  const void* q;
+  int64_t q_stride[2];
+  const void* k_cache;
+  int64_t k_stride[2];
+  const void* v_cache;
+  int64_t v_stride[2];
+  const int64_t* kv_start; /* host arrays of n_nodes entries */
+  const int32_t* kv_len;
+  const int32_t* q_begin;
+  const int32_t* q_end;
+  float scale;
+  void* o;
+  int64_t o_stride[2];
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} attn_decode_tree_args;
+
+ATTN_API int attn_decode_tree(const attn_decode_tree_args* args, void* stream);
+
+/* Workspace bytes attn_decode_tree needs for these arguments (the node arrays, heads_q and
+ * head_dim are read); 0 if they are invalid. */
+ATTN_API size_t attn_decode_tree_workspace_size(const attn_decode_tree_args* args);
+
 ATTN_API size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q);
 
 /* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes). */

@@ -23,4 +23,4 @@ from .gen import (  # noqa: F401
     normal_f32,
     round_to_bf16,
 )
-from .configs import VARLEN_PACKED, WORKLOADS, Workload  # noqa: F401
+from .configs import TREE_DECODE, VARLEN_PACKED, WORKLOADS, Workload, tree_nodes  # noqa: F401

@@ -75,3 +75,22 @@ WORKLOADS = {
 # in the order given (every k in 1..16 once), H heads of dimension D.
 VARLEN_PACKED = {"wid": 6, "name": "varlen_packed_70k", "unit": 512,
                  "k": (7, 2, 12, 16, 1, 9, 4, 14, 6, 11, 3, 15, 8, 13, 5, 10), "H": 32, "D": 128}
+
+# Tree-structured decode: a root segment shared by every query, `children`
+# child segments, each with `leaves` leaf segments; one query per leaf (in
+# depth-first order), GQA with H_q query heads over H_kv key/value heads.
+TREE_DECODE = {"wid": 7, "name": "tree_decode_64q", "root": 32768, "children": 8, "child_len": 4096, "leaves": 8,
+               "leaf_len": 512, "H_q": 32, "H_kv": 8, "D": 128}
+
+
+def tree_nodes(t):
+    """(kv_start, kv_len, q_begin, q_end) of every node of a TREE_DECODE-style tree, root first."""
+    nodes = [(0, t["root"], 0, t["children"] * t["leaves"])]
+    base = t["root"]
+    for c in range(t["children"]):
+        nodes.append((base + c * t["child_len"], t["child_len"], c * t["leaves"], (c + 1) * t["leaves"]))
+    base += t["children"] * t["child_len"]
+    for i in range(t["children"] * t["leaves"]):
+        nodes.append((base + i * t["leaf_len"], t["leaf_len"], i, i + 1))
+    return nodes
+

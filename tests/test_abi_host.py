@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -63,6 +63,9 @@ int main(void) {
   P(attn_fwd_args, flags); P(attn_fwd_args, o_final_stride); P(attn_fwd_args, q_pos0);
   P(attn_fwd_args, cu_seqlens_q); P(attn_fwd_args, cu_seqlens_k);
   P(attn_bwd_args, cu_seqlens_q); P(attn_bwd_args, cu_seqlens_k);
+  printf("tree %zu\n", sizeof(attn_decode_tree_args));
+  P(attn_decode_tree_args, cache_len); P(attn_decode_tree_args, kv_start); P(attn_decode_tree_args, q_end);
+  P(attn_decode_tree_args, scale); P(attn_decode_tree_args, o_stride); P(attn_decode_tree_args, workspace_bytes);
   P(attn_merge_args, mode); P(attn_merge_args, lse_out);
   P(attn_bwd_args, flags); P(attn_bwd_args, dv_stride); P(attn_bwd_args, dq_acc);
   P(attn_bwd_args, workspace); P(attn_bwd_args, workspace_bytes);
@@ -82,9 +85,10 @@ int main(void) {
     assert int(got["decode"]) == ctypes.sizeof(B.DecodeArgs)
     assert int(got["chunks"]) == ctypes.sizeof(B.FwdChunksArgs)
     assert int(got["bwdchunks"]) == ctypes.sizeof(B.BwdChunksArgs)
+    assert int(got["tree"]) == ctypes.sizeof(B.DecodeTreeArgs)
     cls = {"attn_fwd_args": B.FwdArgs, "attn_merge_args": B.MergeArgs, "attn_bwd_args": B.BwdArgs,
            "attn_decode_args": B.DecodeArgs, "attn_fwd_chunks_args": B.FwdChunksArgs,
-           "attn_bwd_chunks_args": B.BwdChunksArgs}
+           "attn_bwd_chunks_args": B.BwdChunksArgs, "attn_decode_tree_args": B.DecodeTreeArgs}
     for key, val in got.items():
         if "." in key:
             t, f = key.split(".")
@@ -92,7 +96,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -372,6 +376,68 @@ def test_bwd_chunks_nothing_to_do(lib):
     # No query rows and no chunk: nothing is launched and no pointer is dereferenced.
     a = bwd_chunks_args(lens=(), seqlen_q=0, q=None, o=None, dout=None, lse=None, dq_acc=None, workspace=None)
     assert lib.attn_bwd_chunks(ctypes.byref(a), None) == B.ATTN_OK
+
+
+def tree_args(nodes=((0, 100, 0, 3), (100, 50, 1, 3)), **kw):
+    """nodes: (kv_start, kv_len, q_begin, q_end) each."""
+    a = B.DecodeTreeArgs()
+    a.struct_size = ctypes.sizeof(B.DecodeTreeArgs)
+    a.n_queries, a.heads_q, a.heads_kv, a.head_dim = 3, 8, 2, 128
+    a.cache_len = 200
+    a.q = a.k_cache = a.v_cache = a.o = a.lse = a.workspace = FAKE
+    a.q_stride = a.o_stride = B.I64x2(8 * 128, 128)
+    a.k_stride = a.v_stride = B.I64x2(2 * 128, 128)
+    n = len(nodes)
+    a.n_nodes = n
+    a._keep = ((ctypes.c_int64 * max(n, 1))(*[x[0] for x in nodes]), (ctypes.c_int32 * max(n, 1))(*[x[1] for x in nodes]),
+               (ctypes.c_int32 * max(n, 1))(*[x[2] for x in nodes]), (ctypes.c_int32 * max(n, 1))(*[x[3] for x in nodes]))
+    a.kv_start, a.kv_len, a.q_begin, a.q_end = a._keep
+    a.workspace_bytes = 1 << 20
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+TREE_BAD = [
+    (dict(n_nodes=257), B.ATTN_ERR_INVALID_ARG, "n_nodes"),
+    (dict(cache_len=120), B.ATTN_ERR_INVALID_ARG, "node 1: keys [100, 150) outside the cache of 120"),
+    (dict(n_queries=2), B.ATTN_ERR_INVALID_ARG, "node 0: queries [0, 3) outside [0, 2)"),
+    (dict(workspace_bytes=100), B.ATTN_ERR_WORKSPACE, "workspace of"),
+    (dict(head_dim=80), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
+    (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse is NULL"),
+    (dict(kv_len=None), B.ATTN_ERR_INVALID_ARG, "node arrays"),
+]
+
+
+@pytest.mark.parametrize("kw,code,msg", TREE_BAD, ids=[m for _, _, m in TREE_BAD])
+def test_decode_tree_rejects(lib, kw, code, msg):
+    a = tree_args(**kw)
+    assert lib.attn_decode_tree(ctypes.byref(a), None) == code
+    assert msg in lib.attn_last_error().decode()
+
+
+def test_decode_tree_workspace_size(lib):
+    # Two nodes of 100 and 50 keys (one segment each) over 3 and 2 queries: 5 entries x 8 heads x 128
+    # fp32 partial rows, then their LSE, each part rounded up to 256 bytes.
+    assert lib.attn_decode_tree_workspace_size(ctypes.byref(tree_args())) == 5 * 8 * 128 * 4 + 256
+    # A node of 5000 keys is cut into segments of 2048 keys: 3 entries per query it covers.
+    a = tree_args(nodes=((0, 5000, 0, 2),), cache_len=5000)
+    assert lib.attn_decode_tree_workspace_size(ctypes.byref(a)) == 6 * 8 * 128 * 4 + 256
+    # Invalid node lists give 0 and leave the last error alone.
+    lib.attn_decode_tree(None, None)
+    before = lib.attn_last_error()
+    assert lib.attn_decode_tree_workspace_size(ctypes.byref(tree_args(cache_len=10))) == 0
+    assert lib.attn_last_error() == before
+    a = tree_args(workspace_bytes=lib.attn_decode_tree_workspace_size(ctypes.byref(tree_args())) - 1)
+    assert lib.attn_decode_tree(ctypes.byref(a), None) == B.ATTN_ERR_WORKSPACE
+
+
+def test_decode_tree_segments_fit_the_table(lib):
+    # 200 nodes of 8192 keys would be 800 segments of 2048: the segment length doubles until the
+    # segments fit the 256-entry table (here 8192 keys: one segment per node, 200 entries).
+    nodes = tuple((0, 8192, 0, 1) for _ in range(200))
+    a = tree_args(nodes=nodes, cache_len=8192, n_queries=1)
+    assert lib.attn_decode_tree_workspace_size(ctypes.byref(a)) == 200 * 8 * 128 * 4 + 256 * ((200 * 8 * 4 + 255) // 256)
 
 
 def decode_args(**kw):

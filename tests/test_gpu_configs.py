@@ -25,7 +25,7 @@ import torch
 import oracle
 from exact_blockwise_attention_attn_amd import binding as B
 from exact_blockwise_attention_attn_amd import shard
-from seeded_inputs import VARLEN_PACKED, WORKLOADS, bf16_bits_to_f32, normal_bf16, normal_f32
+from seeded_inputs import TREE_DECODE, VARLEN_PACKED, WORKLOADS, bf16_bits_to_f32, normal_bf16, normal_f32, tree_nodes
 from tests.gpu_util import check, log, to_np
 
 pytestmark = pytest.mark.gpu
@@ -206,6 +206,43 @@ def test_varlen_packed_70k():
             err = _rel_fro(got, ref)
             log(f"    {name} relative Frobenius error {err:.3e}")
             assert err < 2e-2
+
+
+def test_tree_decode_64q():
+    """The tree decode workload at its benchmarked size: 64 queries under a 32K-token root, 8 children
+    of 4K, 8 leaves of 512 each, GQA 32/8.  Every query against split-KV decode of its materialised
+    path; sampled (query, head) pairs against the oracle over the path's keys."""
+    T = TREE_DECODE
+    nodes = tree_nodes(T)
+    nq = T["children"] * T["leaves"]
+    L = T["root"] + T["children"] * (T["child_len"] + T["leaves"] * T["leaf_len"])
+    Hq, Hkv, D = T["H_q"], T["H_kv"], T["D"]
+    log(f"tree_decode_64q: {nq} queries, {len(nodes)} nodes, {L} cached tokens")
+    qb_ = normal_bf16(T["wid"], 0, 1, (nq, Hq, D))[0]
+    kb_ = normal_bf16(T["wid"], 1, 1, (L, Hkv, D), threads=16)[0]
+    vb_ = normal_bf16(T["wid"], 2, 1, (L, Hkv, D), threads=16)[0]
+    q, kc, vc = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda() for b in (qb_, kb_, vb_))
+    ks, kl, qs, qe = zip(*nodes)
+    ws = torch.empty(B.attn_decode_tree_workspace_size(q, kc, kv_start=ks, kv_len=kl, q_begin=qs, q_end=qe),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((nq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((nq, Hq), dtype=torch.float32, device="cuda")
+    B.attn_decode_tree(q, kc, vc, o, lse, ws, kv_start=ks, kv_len=kl, q_begin=qs, q_end=qe)
+    paths = [np.concatenate([np.arange(s, s + n) for s, n, b, e in nodes if b <= i < e]) for i in range(nq)]
+    idx = torch.from_numpy(np.stack(paths)).cuda()
+    o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+    ws2 = torch.empty(B.attn_decode_workspace_size(nq, Hq, D, 16), dtype=torch.uint8, device="cuda")
+    B.attn_decode_splitkv(q, kc[idx], vc[idx], o2, l2, ws2, n_splits=16)
+    torch.cuda.synchronize()
+    check("O vs split-KV decode of the paths, all queries", o, to_np(o2), 1e-2)
+    check("LSE vs split-KV decode of the paths, all queries", lse, to_np(l2), 1e-3)
+    G = Hq // Hkv
+    scale = 1 / math.sqrt(D)
+    for i, h in ((0, 0), (37, 17), (63, 31)):
+        r = paths[i]
+        O_ref, L_ref = oracle.attention_head(_f64(qb_[i:i + 1, h]), _f64(kb_[r, h // G]), _f64(vb_[r, h // G]), scale)
+        check(f"query {i} head {h} O", o[i, h], O_ref[0], 1e-2)
+        check(f"query {i} head {h} LSE", lse[i, h], L_ref[0], 1e-3)
 
 
 def _sum_rule_quiet(grads, target):

@@ -431,6 +431,67 @@ def test_varlen_fwd_bwd(case):
         check(f"seq {s} dV", dv[b0:b1], dv_r[0], G_TOL, scale_by_max=True)
 
 
+# (n_queries, Hq, Hkv, D, cache_len, nodes as (kv_start, kv_len, q_begin, q_end), root first)
+TREE_CASES = [
+    # root, two inner nodes, five leaves (one with no keys)
+    (5, 8, 2, 128, 1700, ((0, 1000, 0, 5), (1000, 300, 0, 3), (1300, 10, 3, 5), (1310, 90, 0, 1), (1400, 1, 1, 2),
+                          (1401, 0, 2, 3), (1401, 99, 3, 4), (1500, 200, 4, 5))),
+    # a root shared by 300 queries (several query tiles per node) and three uneven branches
+    (300, 4, 4, 64, 6500, ((0, 5000, 0, 300), (5000, 500, 0, 100), (5500, 500, 100, 250), (6000, 500, 250, 300))),
+    # a query no node covers
+    (3, 2, 1, 128, 64, ((0, 64, 0, 2),)),
+]
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=[f"tree{i}" for i in range(len(TREE_CASES))])
+def test_decode_tree(case):
+    """Tree-structured decode against the oracle over each query's path (the concatenated keys
+    of the nodes that cover it); the first tree also against split-KV decode of the
+    materialised per-query caches."""
+    nq, Hq, Hkv, D, L, nodes = case
+    log(f"tree decode {nq} queries, {len(nodes)} nodes")
+    q, qh = seq_tensor(114, 0, 1, nq, Hq, D, "bf16")
+    kc, kh = seq_tensor(114, 1, 1, L, Hkv, D, "bf16")
+    vc, vh = seq_tensor(114, 2, 1, L, Hkv, D, "bf16")
+    q, qh, kc, kh, vc, vh = q[0], qh[0], kc[0], kh[0], vc[0], vh[0]
+    scale = 1 / math.sqrt(D)
+    ks, kl, qb, qe = zip(*nodes)
+    need = B.attn_decode_tree_workspace_size(q, kc, kv_start=ks, kv_len=kl, q_begin=qb, q_end=qe)
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    o = torch.full((nq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((nq, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_decode_tree(q, kc, vc, o, lse, ws, kv_start=ks, kv_len=kl, q_begin=qb, q_end=qe)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    O_ref = np.zeros((nq, Hq, D))
+    L_ref = np.full((nq, Hq), -np.inf)
+    paths = []
+    for i in range(nq):
+        rows = np.concatenate([np.arange(s, s + n) for s, n, b, e in nodes if b <= i < e] + [np.zeros(0, int)])
+        paths.append(rows)
+        for h in range(Hq):
+            O_ref[i, h], L_ref[i, h] = (x[0] for x in oracle.attention_head(qh[i:i + 1, h], kh[rows, h // G],
+                                                                            vh[rows, h // G], scale))
+    check("O", o, O_ref, O_TOL, scale_by_max=True)
+    check("LSE", lse, L_ref, L_TOL)
+    if case is TREE_CASES[0]:
+        P = max(len(r) for r in paths)
+        kp = torch.zeros((nq, P, Hkv, D), dtype=torch.bfloat16, device="cuda")
+        vp = torch.zeros_like(kp)
+        for i, r in enumerate(paths):
+            idx = torch.from_numpy(r).cuda()
+            kp[i, :len(r)] = kc[idx]
+            vp[i, :len(r)] = vc[idx]
+        lens = torch.tensor([len(r) for r in paths], dtype=torch.int32, device="cuda")
+        o2 = torch.empty_like(o)
+        l2 = torch.empty_like(lse)
+        ws2 = torch.empty(B.attn_decode_workspace_size(nq, Hq, D, 4), dtype=torch.uint8, device="cuda")
+        B.attn_decode_splitkv(q, kp, vp, o2, l2, ws2, n_splits=4, seqlens=lens)
+        torch.cuda.synchronize()
+        check("O vs split-KV decode of the paths", o, to_np(o2), O_TOL, scale_by_max=True)
+        check("LSE vs split-KV decode of the paths", lse, to_np(l2), L_TOL)
+
+
 def test_bwd_deterministic():
     log("bwd determinism")
     (q, k, v), _ = _inputs(107, 1, 300, 300, 2, 2, 128, "bf16")
