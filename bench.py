@@ -333,10 +333,21 @@ def bench_decode(args, stream):
     def dec():
         binding.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=NS, stream=stream)
 
-    (t,), _ = time_calls([dec], max(10, args.steps), 3, stream)
+    # The same cache with uneven lengths (8K k tokens for k = 1..16, shuffled): whether fixed splits
+    # per sequence keep the HBM rate when the work per sequence differs 16-fold.
+    lens = [8192 * k for k in (5, 12, 1, 16, 9, 3, 14, 7, 11, 2, 15, 6, 10, 4, 13, 8)]
+    seqlens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+
+    def dec_uneven():
+        binding.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=NS, seqlens=seqlens, stream=stream)
+
+    (t, tu), _ = time_calls([dec, dec_uneven], max(10, args.steps), 3, stream)
     kv_bytes = 2.0 * B * L * HKV * D * 2
     gbs = kv_bytes / t / 1e6
-    return {"workload": "decode_gqa_128k", "ms": t, "kv_bytes": kv_bytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    u_bytes = 2.0 * sum(lens) * HKV * D * 2
+    return {"workload": "decode_gqa_128k", "ms": t, "kv_bytes": kv_bytes, "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "uneven_lengths": {"ms": tu, "kv_bytes": u_bytes, "gbs": u_bytes / tu / 1e6,
+                               "frac_hbm": u_bytes / tu / 1e6 / HBM_PEAK_GBS}}
 
 
 def cpu_baseline():
