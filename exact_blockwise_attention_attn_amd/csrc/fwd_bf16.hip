@@ -186,7 +186,11 @@ __device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x16* oacc
   if (lg == 0) *lse_ptr = L;
 }
 
-template <int D>
+// One tile of 128 rows against keys [0, Sk).  Normally row i is query i of head
+// h.  With PACK (non-causal only) the rows are the queries of a whole GQA group:
+// row r is query r / group of head h + r % group, so the group's heads share
+// every key and value tile, and p.Sq counts rows (queries x group).
+template <int D, bool PACK = false>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s, u16* k1s, u16* v1s, int qt, int b,
                                          int h, const u16* qb, const u16* kb, const u16* vb) {
   constexpr int NS = D / 16;
@@ -197,13 +201,18 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   const int q0 = qt * BM;
   const int qi = q0 + wave * 32 + lr;
   const bool qok = qi < p.Sq;
+  int q_row = qi, h_row = h;  // query and head of this lane's row
+  if constexpr (PACK) {
+    q_row = qi / p.group;
+    h_row = h + (qi - q_row * p.group);
+  }
 
   // Keys [0, kv_end) are visible to some query of this tile; keys [0, full_end)
   // to all of them.  Causal visibility: key j is visible to query i iff j <= delta + i.
   const int q_last = min(q0 + BM, p.Sq) - 1;
   int kv_end = p.Sk, full_end = p.Sk;
   int64_t lim64 = (int64_t)p.Sk - 1;
-  if (p.causal) {
+  if (!PACK && p.causal) {
     kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta + q_last + 1, p.Sk));
     full_end = (int)max<int64_t>(0, min<int64_t>(p.delta + q0 + 1, p.Sk));
     lim64 = min<int64_t>(p.delta + qi, lim64);
@@ -221,7 +230,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
 
   bf16x8 qf[NS];
   {
-    const u16* qrow = qb + (int64_t)qi * p.q.ss + lg * 8;
+    const u16* qrow = qb + (int64_t)q_row * p.q.ss + (int64_t)(h_row - h) * p.q.sh + lg * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qf[s] = qok ? as_bf16x8(*(const u32x4*)(qrow + s * 16)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -236,20 +245,25 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   rf.init(lane);
   tf.init(lane);
 
+  // With PACK, a wavefront whose rows all lie past the end only helps with the
+  // loads and barriers (a node with few queries fills part of a tile).
+  const bool live = !PACK || q0 + wave * 32 < p.Sq;
   for (int t = 0; t < n_tiles; t += 2) {
     wait_loads();
     __syncthreads();
     if (t + 1 < n_tiles) issue(k1s, v1s, (t + 1) * BN);
-    tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf, lane);
+    if (live)
+      tile_step<D>(k0s, v0s, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf, lane);
     if (t + 1 >= n_tiles) break;
     wait_loads();
     __syncthreads();
     if (t + 2 < n_tiles) issue(k0s, v0s, (t + 2) * BN);
-    tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, rf, tf, lane);
+    if (live)
+      tile_step<D>(k1s, v1s, qf, oacc, st, (t + 1) * BN, (t + 1) * BN + BN > full_end, lim64, sl2, rf, tf, lane);
   }
   __syncthreads();  // the next call of this function reuses the buffers
 
-  fwd_store<D>(p, oacc, st, qi, qok, b, h, lg);
+  fwd_store<D>(p, oacc, st, q_row, qok, b, h_row, lg);
 }
 
 template <int D>
@@ -323,10 +337,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_varlen_kernel(FwdParams p) {
 //
 // Tree-structured decoding (DeFT under the Tree Attention page's related
 // papers): the queries below a node of a prefix tree share that node's keys.
-// Pass 1 reads each node's keys once per query head for all of its queries
-// (workgroup = node, head, tile of 128 of its queries), through the same tile
-// code as the forward, and writes a partial (O, LSE) per (node, query).
-// Pass 2 merges each query's partials in node order.
+// Pass 1 reads each node's keys once per key/value head for all of its queries
+// and all query heads of the GQA group (workgroup = node, key/value head, tile
+// of 128 rows of (query, head in group)), through the same tile code as the
+// forward, and writes a partial (O, LSE) per (node, query, head).  Pass 2
+// merges each query's partials in node order.
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void tree_fwd_kernel(FwdParams p, TreeTable tt) {
@@ -334,43 +349,66 @@ __global__ __launch_bounds__(NT, 2) void tree_fwd_kernel(FwdParams p, TreeTable 
   __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
-  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hq, p.n_units);
-  const int n = w.b, h = w.h, unit = w.unit;
-  const int hk = h / p.group;
+  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hkv, p.n_units);
+  const int n = w.b, hk = w.h, unit = w.unit;
+  const int h0 = hk * p.group;
   FwdParams s = p;
-  s.Sq = tt.q_end[n] - tt.q_begin[n];
+  s.Sq = (tt.q_end[n] - tt.q_begin[n]) * p.group;  // rows: (query, head in group)
   s.Sk = tt.kv_len[n];
   s.n_qtiles = (s.Sq + BM - 1) / BM;
   if (unit >= s.n_qtiles) return;
   s.o.ptr = (float*)p.o.ptr + (int64_t)tt.e0[n] * p.o.ss;
   s.lse = p.lse + (int64_t)tt.e0[n] * p.lse_ss;
-  const u16* qb = (const u16*)p.q.ptr + (int64_t)tt.q_begin[n] * p.q.ss + (int64_t)h * p.q.sh;
+  const u16* qb = (const u16*)p.q.ptr + (int64_t)tt.q_begin[n] * p.q.ss + (int64_t)h0 * p.q.sh;
   const u16* kb = (const u16*)p.k.ptr + tt.kv_start[n] * p.k.ss + (int64_t)hk * p.k.sh;
   const u16* vb = (const u16*)p.v.ptr + tt.kv_start[n] * p.v.ss + (int64_t)hk * p.v.sh;
-  fwd_tile<D>(s, k0s, v0s, k1s, v1s, unit, 0, h, qb, kb, vb);
+  fwd_tile<D, true>(s, k0s, v0s, k1s, v1s, unit, 0, h0, qb, kb, vb);
 }
 
-// One workgroup per (query, head), one thread per feature: the partials of
-// the nodes whose query range holds the query, merged in node order.
+// One workgroup per (query, head), one thread per feature.  The first
+// wavefront lists the query's partials in node order (an ordered compaction of
+// the nodes whose range holds the query), then the partials are combined in
+// one LSE-weighted sum stabilised by their largest LSE: every load of the sum
+// is independent of the others, unlike a chain of pairwise merges, and the
+// result is the same up to rounding (the merge is associative).
 template <int D>
 __global__ __launch_bounds__(D) void tree_merge_kernel(const float* po, const float* pl, int Hq, TreeTable tt,
                                                        u16* out_o, int64_t o_sq, int64_t o_sh, float* out_lse) {
-  const int i = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
-  float L = neg_inf(), O = 0.f;
-  for (int n = 0; n < tt.n; ++n) {
-    if (i < tt.q_begin[n] || i >= tt.q_end[n]) continue;
-    const int64_t e = (int64_t)tt.e0[n] + (i - tt.q_begin[n]);
-    const float lb = pl[e * Hq + h], ob = po[(e * Hq + h) * D + d];
-    float wa, wb, Ln;
-    merge_weights(L, lb, wa, wb, Ln);
-    float r = 0.f;
-    if (wa != 0.f) r += wa * O;
-    if (wb != 0.f) r += wb * ob;
-    O = r;
-    L = Ln;
+  __shared__ int ent[kMaxTreeNodes];  // partial rows of this query, in node order
+  __shared__ float lv[kMaxTreeNodes];  // their LSE
+  __shared__ int n_ent;
+  const int i = blockIdx.x / Hq, h = blockIdx.x % Hq, t = threadIdx.x;
+  if (t < 64) {
+    int k = 0;
+    for (int n0 = 0; n0 < tt.n; n0 += 64) {
+      const int n = n0 + t;
+      const int nc = min(n, tt.n - 1);
+      const int qb = tt.q_begin[nc], qe = tt.q_end[nc], e = tt.e0[nc] + (i - qb);
+      const bool hit = (n < tt.n) & (i >= qb) & (i < qe);
+      const unsigned long long m = __ballot(hit);
+      if (hit) ent[k + __popcll(m & ((1ull << t) - 1ull))] = e;
+      k += __popcll(m);
+    }
+    if (t == 0) n_ent = k;
   }
-  out_o[(int64_t)i * o_sq + (int64_t)h * o_sh + d] = f32_to_bf16(O);
-  if (d == 0) out_lse[(int64_t)i * Hq + h] = L;
+  __syncthreads();
+  const int K = n_ent;
+  for (int k = t; k < K; k += D) lv[k] = pl[(int64_t)ent[k] * Hq + h];
+  __syncthreads();
+  float M = neg_inf();
+  for (int k = 0; k < K; ++k) M = fmaxf(M, lv[k]);
+  float S = 0.f, O = 0.f;
+  if (M != neg_inf()) {
+#pragma unroll 8
+    for (int k = 0; k < K; ++k) {
+      const float w = expf(lv[k] - M);  // 0 for an empty partial
+      S += w;
+      O = fmaf(w, po[((int64_t)ent[k] * Hq + h) * D + t], O);
+    }
+  }
+  const bool any = S > 0.f;
+  out_o[(int64_t)i * o_sq + (int64_t)h * o_sh + t] = f32_to_bf16(any ? O / S : 0.f);
+  if (t == 0) out_lse[(int64_t)i * Hq + h] = any ? M + logf(S) : neg_inf();
 }
 
 // ------------------------------------------------------ fused chunk table --
@@ -547,8 +585,8 @@ hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
 hipError_t launch_tree_decode(const FwdParams& p0, const TreeTable& tt, int n_q, void* out_o, int64_t out_o_sq,
                               int64_t out_o_sh, float* out_lse, int D, hipStream_t s) {
   FwdParams p = p0;
-  p.n_units = (tt.max_q + BM - 1) / BM;
-  const int64_t grid = (int64_t)tt.n * p.Hq * p.n_units;
+  p.n_units = (int)(((int64_t)tt.max_q * p.group + BM - 1) / BM);
+  const int64_t grid = (int64_t)tt.n * p.Hkv * p.n_units;
   if (grid > 0) {
     if (D == 128)
       hipLaunchKernelGGL(tree_fwd_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, tt);

@@ -432,6 +432,23 @@ def test_varlen_fwd_bwd(case):
 
 
 # (n_queries, Hq, Hkv, D, cache_len, nodes as (kv_start, kv_len, q_begin, q_end), root first)
+def _chain_tree():
+    """20 queries under a chain of 70 short nodes, a node with no keys, one leaf per query and a
+    2100-key node (two segments) over queries 5..14."""
+    nodes, s = [], 0
+    for j in range(70):
+        n = 16 + j % 5
+        nodes.append((s, n, 0, 20))
+        s += n
+    nodes.append((s, 0, 0, 20))
+    for i in range(20):
+        nodes.append((s, 33, i, i + 1))
+        s += 33
+    nodes.append((s, 2100, 5, 15))
+    s += 2100
+    return (20, 16, 2, 128, s, tuple(nodes))
+
+
 TREE_CASES = [
     # root, two inner nodes, five leaves (one with no keys)
     (5, 8, 2, 128, 1700, ((0, 1000, 0, 5), (1000, 300, 0, 3), (1300, 10, 3, 5), (1310, 90, 0, 1), (1400, 1, 1, 2),
@@ -440,6 +457,9 @@ TREE_CASES = [
     (300, 4, 4, 64, 6500, ((0, 5000, 0, 300), (5000, 500, 0, 100), (5500, 500, 100, 250), (6000, 500, 250, 300))),
     # a query no node covers
     (3, 2, 1, 128, 64, ((0, 64, 0, 2),)),
+    # GQA group of 8 (a packed tile of 20 queries x 8 heads, leaves with 8 live rows); 93 table
+    # segments, more than 64 of them on every query's path
+    _chain_tree(),
 ]
 
 
