@@ -410,9 +410,10 @@ ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
  * the path of queries q_begin[n] .. q_end[n] - 1.  Query i attends, with no
  * mask, every key of every node whose query range holds i; query head h reads
  * key/value head h / (heads_q / heads_kv).  Each node's keys are read once per
- * query head for all of its queries; the per-node partial results of a query
- * are then merged in node order (list a node after its ancestors to merge root
- * first).  A query that no node covers gets O = 0, LSE = -inf.
+ * key/value head for all of its queries and all query heads of the group; the
+ * per-node partial results of a query are then combined by one LSE-weighted
+ * sum (the same result as merging them in node order, up to rounding).  A
+ * query that no node covers gets O = 0, LSE = -inf.
  *
  * q [n_queries, heads_q, head_dim] bf16 (strides q_stride = {query, head});
  * k_cache, v_cache [cache_len, heads_kv, head_dim] bf16 (strides {token, head});
