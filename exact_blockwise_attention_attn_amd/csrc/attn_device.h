@@ -58,6 +58,18 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Value held by lane l ^ 32 (the other half of the wavefront).
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
 
+// Sum over each aligned group of 16 lanes (a DPP row), the result in every lane
+// of the group: swaps within quads, then rotations of the row by 4 and 8 lanes.
+// Vector-ALU moves only (no LDS crossbar round trip).  Every lane of the row
+// must be active.
+__device__ __forceinline__ float sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lanes 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lanes 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror 4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror 8
+  return x;
+}
+
 // Position of key k (within a tile) in the MFMA k-slot order used for operands
 // that come straight out of an MFMA accumulator: slot (g, s) of a 16-key slab
 // holds key 8*(s/4) + 4*g + s%4, so the 8 keys a lane contributes are

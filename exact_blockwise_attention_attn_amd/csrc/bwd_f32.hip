@@ -86,14 +86,8 @@ constexpr int FROWS = 16;          // rows per workgroup
 constexpr int FNT = TPR * FROWS;   // threads per workgroup
 constexpr int FTK = 32;            // rows per staged tile
 
-// Sum over the 16 lanes of this thread's row group.
-__device__ __forceinline__ float row_sum(float x) {
-  x += __shfl_xor(x, 8, TPR);
-  x += __shfl_xor(x, 4, TPR);
-  x += __shfl_xor(x, 2, TPR);
-  x += __shfl_xor(x, 1, TPR);
-  return x;
-}
+// Sum over the 16 lanes of this thread's row group (TPR = 16 lanes, one DPP row).
+__device__ __forceinline__ float row_sum(float x) { return sum16(x); }
 
 template <int D>
 __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
@@ -139,6 +133,7 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
     __syncthreads();
     // Every lane runs every step (the row sums exchange data across lanes);
     // pairs a row does not see get P = 0.
+#pragma unroll 16
     for (int j = 0; j < FTK; ++j) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
@@ -219,6 +214,7 @@ __global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
         ds_[tid] = (i < p.Sq) ? dltb[i] : 0.f;
       }
       __syncthreads();
+#pragma unroll 8
       for (int rr = 0; rr < FTK; ++rr) {
         float s = 0.f, dp = 0.f;
 #pragma unroll

@@ -17,14 +17,8 @@ constexpr int BM = 16;          // queries per workgroup
 constexpr int NT = TPR * BM;    // threads per workgroup
 constexpr int TK = 32;          // keys per tile
 
-// Sum over the 16 lanes of this thread's row group.
-__device__ __forceinline__ float row_sum(float x) {
-  x += __shfl_xor(x, 8, TPR);
-  x += __shfl_xor(x, 4, TPR);
-  x += __shfl_xor(x, 2, TPR);
-  x += __shfl_xor(x, 1, TPR);
-  return x;
-}
+// Sum over the 16 lanes of this thread's row group (TPR = 16 lanes, one DPP row).
+__device__ __forceinline__ float row_sum(float x) { return sum16(x); }
 
 template <int D>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {

@@ -460,6 +460,8 @@ TREE_CASES = [
     # GQA group of 8 (a packed tile of 20 queries x 8 heads, leaves with 8 live rows); 93 table
     # segments, more than 64 of them on every query's path
     _chain_tree(),
+    # d = 64 with GQA 4: 70 queries x 4 heads = 280 packed rows under the root (three tiles)
+    (70, 8, 2, 64, 3000, ((0, 2500, 0, 70), (2500, 300, 0, 35), (2800, 200, 35, 70))),
 ]
 
 
