@@ -484,16 +484,35 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
   const bool kfast = TileSrc<D, 4>::fits(p.k.ss), vfast = TileSrc<D, 4>::fits(p.v.ss);
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
-  auto issue = [&](int c, int tile, int slot) {
-    const u16* kb = (const u16*)ct.k[c] + (int64_t)b * ct.kb[c] + (int64_t)hk * p.k.sh;
-    const u16* vb = (const u16*)ct.v[c] + (int64_t)b * ct.vb[c] + (int64_t)hk * p.v.sh;
-    ksrc.issue(k_s + slot * SZ, kb, p.k.ss, tile * BN, ct.len[c], kfast, wave, lane);
-    vsrc.issue(v_s + slot * SZ, vb, p.v.ss, tile * BN, ct.len[c], vfast, wave, lane);
+  // What the steps need of a chunk, read from the table once per chunk (the
+  // table lives in kernel-argument memory: a read per step would put a scalar
+  // load's latency into every step).
+  struct Chunk {
+    const u16* kb;
+    const u16* vb;
+    int len, kv_end, full_end;
+    int64_t lim64;  // this lane's last visible key of the chunk
+  };
+  auto chunk_of = [&](int cc) {
+    Chunk k;
+    k.kb = (const u16*)ct.k[cc] + (int64_t)b * ct.kb[cc] + (int64_t)hk * p.k.sh;
+    k.vb = (const u16*)ct.v[cc] + (int64_t)b * ct.vb[cc] + (int64_t)hk * p.v.sh;
+    k.len = ct.len[cc];
+    chunk_range(cc, k.kv_end, k.full_end);
+    k.lim64 = (int64_t)k.len - 1;
+    if (p.causal) k.lim64 = min<int64_t>(ct.q_pos0 - ct.pos0[cc] + qi, k.lim64);
+    return k;
+  };
+  auto issue = [&](const Chunk& k, int tile, int slot) {
+    ksrc.issue(k_s + slot * SZ, k.kb, p.k.ss, tile * BN, k.len, kfast, wave, lane);
+    vsrc.issue(v_s + slot * SZ, k.vb, p.v.ss, tile * BN, k.len, vfast, wave, lane);
   };
 
   int c = first_from(0), t = 0;
+  Chunk cur{};
   if (c < ct.n) {
-    issue(c, 0, 0);
+    cur = chunk_of(c);
+    issue(cur, 0, 0);
     wait_vm<0>();
     lds_barrier();
   }
@@ -501,23 +520,22 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
   // step's slot is a compile-time constant folded into its LDS read offsets.
   auto step = [&](auto slot_c) {
     constexpr int SLOT = decltype(slot_c)::value;
-    int kv_end, full_end;
-    chunk_range(c, kv_end, full_end);
     // Next tile in sequence: the rest of this chunk, then the next chunk with visible keys.
     int nc = c, nt = t + 1;
-    if (nt * BN >= kv_end) {
+    Chunk nxt = cur;
+    if (nt * BN >= cur.kv_end) {
       nc = first_from(c + 1);
       nt = 0;
+      if (nc < ct.n) nxt = chunk_of(nc);
     }
-    if (nc < ct.n) issue(nc, nt, SLOT ^ 1);
-    int64_t lim64 = (int64_t)ct.len[c] - 1;  // this lane's last visible key of chunk c
-    if (p.causal) lim64 = min<int64_t>(ct.q_pos0 - ct.pos0[c] + qi, lim64);
-    tile_step<D>(k_s + SLOT * SZ, v_s + SLOT * SZ, qf, oacc, st, t * BN, t * BN + BN > full_end, lim64, sl2, rf, tf,
-                 lane);
+    if (nc < ct.n) issue(nxt, nt, SLOT ^ 1);
+    tile_step<D>(k_s + SLOT * SZ, v_s + SLOT * SZ, qf, oacc, st, t * BN, t * BN + BN > cur.full_end, cur.lim64, sl2,
+                 rf, tf, lane);
     wait_vm<0>();  // the next tile, the only load in flight
     lds_barrier();
     c = nc;
     t = nt;
+    cur = nxt;
   };
   while (c < ct.n) {
     step(std::integral_constant<int, 0>{});
