@@ -19,9 +19,9 @@
 //     ALUs.
 // The four wavefronts' partials are merged in LDS and written to the workspace.
 //
-// Tree kernel: one workgroup per (batch, query head); a binary-carry stack
-// realises the adjacent-pair tree over the splits, whose power-of-two chunks
-// are reduced in parallel (see decode_tree_kernel).
+// Tree kernel: one workgroup per (batch, query head); the adjacent-pair tree
+// over the split LSEs is built level by level in LDS and fixes each split's
+// weight in the root (see decode_tree_kernel).
 #include <type_traits>
 
 #include "attn_device.h"
@@ -35,7 +35,6 @@ constexpr int NW = 4;      // wavefronts
 constexpr int KW = 16;     // keys per tile
 constexpr int DEPTH = 4;   // tiles in flight per wavefront
 constexpr int QPW = 4;     // query heads per workgroup
-constexpr int kMaxLevels = 11;
 
 template <int D>
 struct KvTile {
@@ -216,105 +215,70 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
   }
 }
 
-__device__ __forceinline__ void merge_scalar(float& La, float& Oa, float Lb, float Ob) {
-  float wa, wb, L;
-  merge_weights(La, Lb, wa, wb, L);
-  float r = 0.f;
-  if (wa != 0.f) r += wa * Oa;
-  if (wb != 0.f) r += wb * Ob;
-  Oa = r;
-  La = L;
-}
-
-// Binary-carry stack for the adjacent-pair tree: push partials in order; a
-// push merges equal-size subtrees as soon as both exist.
-struct TreeStack {
-  float sl[kMaxLevels], so[kMaxLevels];
-  unsigned pending = 0;
-  __device__ __forceinline__ void push(float xl, float xo) {
-#pragma unroll
-    for (int k = 0; k < kMaxLevels; ++k) {
-      if (pending & (1u << k)) {
-        merge_scalar(sl[k], so[k], xl, xo);
-        xl = sl[k];
-        xo = so[k];
-        pending &= ~(1u << k);
-      } else {
-        sl[k] = xl;
-        so[k] = xo;
-        pending |= 1u << k;
-        return;
-      }
-    }
-  }
-  // Combine what is left, smaller subtrees first: the tree's root.
-  __device__ __forceinline__ void root(float& L, float& O) const {
-    L = neg_inf();
-    O = 0.f;
-    bool have = false;
-#pragma unroll
-    for (int k = 0; k < kMaxLevels; ++k) {
-      if (pending & (1u << k)) {
-        if (!have) {
-          L = sl[k];
-          O = so[k];
-          have = true;
-        } else {
-          float l2 = sl[k], o2 = so[k];
-          merge_scalar(l2, o2, L, O);
-          L = l2;
-          O = o2;
-        }
-      }
-    }
-  }
-};
-
-// One workgroup per (batch, query head) with TREE_NT threads: NC = TREE_NT / D
-// groups of D threads (one per feature).  Group c reduces splits
-// [c * cs, (c + 1) * cs) with cs a power of two, giving the root of that
-// subtree; group 0 then pushes the NC roots in order.  Because every chunk but
-// the last is a complete subtree, this is the same adjacent-pair tree as
-// pushing all splits one by one, with a much shorter dependency chain.
-constexpr int TREE_NT = 1024;
+// Tree kernel: one workgroup per (batch, query head).  The adjacent-pair tree
+// is built over the split LSEs level by level in LDS: at each level node k of
+// the next level merges nodes 2k and 2k+1 (an odd last node is carried up
+// unchanged), and each node keeps the weight e^{L_node - L_parent} it gets in
+// its parent.  A split's weight in the root is the product of the weights on
+// its path, so the root's O is the sum of the split partials with those
+// weights: the same tree, with the O additions done in one pass whose loads
+// are all independent (a chain of pairwise merges in registers would wait on
+// each load in turn).  Rows whose splits are all empty get O = 0, LSE = -inf.
+constexpr int TREE_NT = 256;
+constexpr int kMaxNodes = 2 * 1024;  // nodes of all levels for up to 1024 splits
 
 template <int D>
 __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) {
-  constexpr int NC = TREE_NT / D;
-  __shared__ float rl[NC], ro[NC][D];
-  const int d = threadIdx.x % D, c = threadIdx.x / D;
+  constexpr int NC = TREE_NT / D;  // groups of D threads, one thread per feature
+  __shared__ float lv[kMaxNodes];  // node LSEs, level 0 (the splits) first
+  __shared__ float wv[kMaxNodes];  // weight of each node in its parent
+  __shared__ float wl[kMaxNodes / 2];  // weight of each split in the root
+  __shared__ float red[NC][D];
+  const int tid = threadIdx.x, d = tid % D, c = tid / D;
   const int h = blockIdx.x % prm.Hq, b = blockIdx.x / prm.Hq;
-  const int64_t base = ((int64_t)b * prm.Hq + h) * prm.n_splits;
-  int cs = 1;
-  while (cs * NC < prm.n_splits) cs *= 2;
-  const int i_beg = min(c * cs, prm.n_splits), i_end = min(i_beg + cs, prm.n_splits);
-  TreeStack st;
-  // Fetch 16 partials at a time (independent loads whose latencies overlap).
-  constexpr int CH = 16;
-  for (int i0 = i_beg; i0 < i_end; i0 += CH) {
-    float cl[CH], co[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int i = min(i0 + j, i_end - 1);
-      cl[j] = prm.part_lse[base + i];
-      co[j] = prm.part_o[(base + i) * D + d];
+  const int n = prm.n_splits;
+  const int64_t base = ((int64_t)b * prm.Hq + h) * n;
+  for (int i = tid; i < n; i += TREE_NT) lv[i] = prm.part_lse[base + i];
+  __syncthreads();
+  int off = 0, m = n;  // this level's nodes are lv[off .. off + m)
+  while (m > 1) {
+    const int mp = (m + 1) / 2;
+    for (int k = tid; k < mp; k += TREE_NT) {
+      if (2 * k + 1 < m) {
+        float wa, wb, L;
+        merge_weights(lv[off + 2 * k], lv[off + 2 * k + 1], wa, wb, L);
+        wv[off + 2 * k] = wa;
+        wv[off + 2 * k + 1] = wb;
+        lv[off + m + k] = L;
+      } else {
+        wv[off + 2 * k] = 1.f;
+        lv[off + m + k] = lv[off + 2 * k];
+      }
     }
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (i0 + j < i_end) st.push(cl[j], co[j]);
+    __syncthreads();
+    off += m;
+    m = mp;
   }
-  float L, O;
-  st.root(L, O);
-  if (d == 0) rl[c] = L;
-  ro[c][d] = O;
+  const float L_root = lv[off];
+  for (int i = tid; i < n; i += TREE_NT) {
+    float w = 1.f;
+    for (int j = i, o = 0, mm = n; mm > 1; o += mm, j >>= 1, mm = (mm + 1) / 2) w *= wv[o + j];
+    wl[i] = w;
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll 4
+  for (int i = c; i < n; i += NC) {
+    const float w = wl[i];
+    if (w != 0.f) acc = fmaf(w, prm.part_o[(base + i) * D + d], acc);
+  }
+  red[c][d] = acc;
   __syncthreads();
   if (c != 0) return;
-  TreeStack top;
-  for (int k = 0; k < NC; ++k)
-    if (k * cs < prm.n_splits) top.push(rl[k], ro[k][d]);
-  top.root(L, O);
-  prm.o[(int64_t)b * prm.o_sb + (int64_t)h * prm.o_sh + d] = f32_to_bf16(O);
-  if (d == 0) prm.lse[(int64_t)b * prm.Hq + h] = L;
+#pragma unroll
+  for (int k = 1; k < NC; ++k) acc += red[k][d];
+  prm.o[(int64_t)b * prm.o_sb + (int64_t)h * prm.o_sh + d] = f32_to_bf16(L_root == neg_inf() ? 0.f : acc);
+  if (d == 0) prm.lse[(int64_t)b * prm.Hq + h] = L_root;
 }
 
 }  // namespace
