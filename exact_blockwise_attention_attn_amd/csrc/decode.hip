@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
 // weights: the same tree, with the O additions done in one pass whose loads
 // are all independent (a chain of pairwise merges in registers would wait on
 // each load in turn).  Rows whose splits are all empty get O = 0, LSE = -inf.
-constexpr int TREE_NT = 256;
+constexpr int TREE_NT = 512;
 constexpr int kMaxNodes = 2 * 1024;  // nodes of all levels for up to 1024 splits
 
 template <int D>
@@ -266,12 +266,20 @@ __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) 
     wl[i] = w;
   }
   __syncthreads();
+  // Sixteen loads in flight per thread; an empty split's partial is 0 with
+  // weight 0, so no branch is needed.
+  constexpr int U = 16;
+  const float* po = prm.part_o + base * D + d;
   float acc = 0.f;
-#pragma unroll 4
-  for (int i = c; i < n; i += NC) {
-    const float w = wl[i];
-    if (w != 0.f) acc = fmaf(w, prm.part_o[(base + i) * D + d], acc);
+  int i = c;
+  for (; i + (U - 1) * NC < n; i += U * NC) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = po[(int64_t)(i + k * NC) * D];
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc = fmaf(wl[i + k * NC], v[k], acc);
   }
+  for (; i < n; i += NC) acc = fmaf(wl[i], po[(int64_t)i * D], acc);
   red[c][d] = acc;
   __syncthreads();
   if (c != 0) return;

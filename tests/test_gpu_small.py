@@ -539,6 +539,13 @@ DECODE_CASES = [
     # (a last tile of one key), and 64 splits over many (batch, head) items.
     (4, 8, 8, 4133, 128, 64, [0, 1, 2000, 4133]),
     (2, 16, 4, 8192, 64, 128, [8192, 777]),
+    # Deep merge trees: the most splits the boundary takes (10 levels, most of
+    # them empty), more splits than keys, and split counts that carry an odd
+    # node up at several levels.
+    (2, 8, 2, 1500, 128, 1024, [1500, 3]),
+    (1, 4, 1, 37, 64, 100, None),
+    (2, 4, 2, 999, 128, 1000, None),
+    (1, 8, 2, 700, 128, 5, [700]),
 ]
 
 
