@@ -36,10 +36,13 @@ constexpr int KW = 16;     // keys per tile
 constexpr int DEPTH = 4;   // tiles in flight per wavefront
 constexpr int QPW = 4;     // query heads per workgroup
 
-// Cache bytes are read exactly once per call: the loads carry the non-temporal
-// hint, so they stream past the caches instead of displacing lines.
+// Cache bytes are read exactly once per call.  V rows are read whole (16 lanes
+// x 16 B cover a 256-byte row) with the non-temporal hint, so they stream past
+// the caches.  K rows are read 64 bytes per instruction (the operand layout of
+// the score MFMA), two instructions per 128-byte line; under the streaming hint
+// about 9% of those lines were fetched twice, so K loads stay ordinary.
 template <class T>
-__device__ __forceinline__ T cache_load(const T* p) {
+__device__ __forceinline__ T stream_load(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
@@ -97,11 +100,11 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
     const int kkey = min(key0 + l16, n_keys - 1);
     const u16* kp = kbase + (int64_t)kkey * prm.k_sl;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) t.k[kk] = cache_load((const u32x4*)(kp + (4 * kk + g) * 8));
+    for (int kk = 0; kk < NKK; ++kk) t.k[kk] = *(const u32x4*)(kp + (4 * kk + g) * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int vkey = min(key0 + 4 * j + g, n_keys - 1);
-      t.v[j] = cache_load((const typename KvTile<D>::VT*)(vbase + (int64_t)vkey * prm.v_sl + FPV * l16));
+      t.v[j] = stream_load((const typename KvTile<D>::VT*)(vbase + (int64_t)vkey * prm.v_sl + FPV * l16));
     }
   };
 
