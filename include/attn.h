@@ -371,7 +371,10 @@ ATTN_API int attn_bwd_chunks(const attn_bwd_chunks_args* args, void* stream);
  * [0, cache_len]) or cache_len when seqlens is NULL; no causal mask applies.
  * The keys are cut into n_splits contiguous splits of ceil(cache_len / n_splits)
  * keys; each split yields a partial (O, LSE) in the workspace and the partials of
- * each (b, h) are reduced by a binary tree of adjacent pairs.
+ * each (b, h) are reduced by a binary tree of adjacent pairs (an odd node is
+ * carried up a level): the tree is built over the split LSEs, and O is the sum
+ * of the split partials weighted by their weights in the tree's root, which is
+ * the tree's result up to the order of the additions.
  * Writes o [batch, heads_q, head_dim] bf16 (strides o_stride = {batch, head}) and
  * lse [batch, heads_q] fp32.  The workspace (device memory of at least
  * attn_decode_workspace_size(...) bytes, 256-byte aligned) is overwritten.
