@@ -276,6 +276,25 @@ def test_decode_gqa_128k():
     log(f"  16 (b, kv head) pairs: max|err| O {err_o:.3e}, LSE {err_l:.3e}")
     assert err_o <= 1e-2 and err_l <= 1e-3
 
+    # The uneven-length call the benchmark also times: sequence b holds 8192 k
+    # keys, k a permutation of 1..16, so most of its 64 splits are empty.
+    lens = [8192 * k for k in (5, 12, 1, 16, 9, 3, 14, 7, 11, 2, 15, 6, 10, 4, 13, 8)]
+    log("decode_gqa_128k: uneven lengths, 64 splits + tree merge")
+    B.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=w.n_chunks,
+                          seqlens=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o_np, l_np = to_np(o), to_np(lse)
+    err_o = err_l = 0.0
+    for b in range(w.B):
+        g = (5 * b + 1) % w.H_kv
+        heads = list(range(g * G, g * G + G))
+        n = lens[b]
+        O_ref, L_ref = oracle.attention_head(_f64(qbits[b, heads]), _f64(kb[b, :n, g]), _f64(vb[b, :n, g]), w.scale)
+        err_o = max(err_o, np.abs(o_np[b, heads] - O_ref).max())
+        err_l = max(err_l, np.abs(l_np[b, heads] - L_ref).max())
+    log(f"  uneven lengths, 16 (b, kv head) pairs: max|err| O {err_o:.3e}, LSE {err_l:.3e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+
 
 def test_causal_fwdbwd_32k():
     w = WORKLOADS["causal_fwdbwd_32k"]
