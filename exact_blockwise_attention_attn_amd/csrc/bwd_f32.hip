@@ -81,20 +81,31 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
 // over the row's 16 lanes, and each thread updates its own features.  Tiles of
 // the other side's rows are staged in LDS and read by all rows.
 
-constexpr int TPR = 16;            // threads per row
-constexpr int FROWS = 16;          // rows per workgroup
-constexpr int FNT = TPR * FROWS;   // threads per workgroup
-constexpr int FTK = 32;            // rows per staged tile
+// Small problems give few workgroups, so each workgroup also splits the
+// dimension it walks over groups of threads (keys for dQ, queries for dK/dV);
+// the groups' partial sums are added in LDS in a fixed order at the end
+// (deterministic; no atomics).
+constexpr int TPR = 16;                 // threads per row
+constexpr int FROWS = 16;               // query rows per dQ workgroup
+constexpr int QSPL = 4;                 // dQ: groups splitting the keys
+constexpr int FTK = 32;                 // dQ: key rows per staged tile
+constexpr int QGT = TPR * FROWS;        // dQ: threads per group
+constexpr int QNT = QGT * QSPL;         // dQ: threads per workgroup
+constexpr int KROWS = 8;                // key rows per dK/dV workgroup
+constexpr int KSPL = 8;                 // dK/dV: groups splitting the queries
+constexpr int KTK = 16;                 // dK/dV: query rows per staged tile
+constexpr int KGT = TPR * KROWS;        // dK/dV: threads per group
+constexpr int KNT = KGT * KSPL;         // dK/dV: threads per workgroup
 
 // Sum over the 16 lanes of this thread's row group (TPR = 16 lanes, one DPP row).
 __device__ __forceinline__ float row_sum(float x) { return sum16(x); }
 
 template <int D>
-__global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(QNT) void dq_f32_kernel(BwdParams p) {
   constexpr int F = D / TPR;
-  __shared__ __attribute__((aligned(16))) float ks[FTK][D];
-  __shared__ __attribute__((aligned(16))) float vs[FTK][D];
-  const int tid = threadIdx.x, r = tid / TPR, c = tid % TPR, f0 = c * F;
+  __shared__ __attribute__((aligned(16))) float ks[QSPL][FTK][D];
+  __shared__ __attribute__((aligned(16))) float vs[QSPL][FTK][D];
+  const int tid = threadIdx.x, g = tid / QGT, lt = tid % QGT, r = lt / TPR, c = lt % TPR, f0 = c * F;
   const int qt = blockIdx.x % p.n_qtiles;
   const int bh = blockIdx.x / p.n_qtiles;
   const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
@@ -121,14 +132,17 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
     kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta_pos + q_last + 1, p.Sk));
     lim = min<int64_t>(p.delta_pos + qi, lim);
   }
-  for (int key0 = 0; key0 < kv_end; key0 += FTK) {
+  // Group g takes key tiles g, g + QSPL, ...; every group runs the same count.
+  const int n_iter = ((kv_end + FTK - 1) / FTK + QSPL - 1) / QSPL;
+  for (int it = 0; it < n_iter; ++it) {
+    const int key0 = (it * QSPL + g) * FTK;
     __syncthreads();
-    for (int e = tid; e < FTK * D; e += FNT) {
+    for (int e = lt; e < FTK * D; e += QGT) {
       const int rr = e / D, cc = e % D;
       const int key = key0 + rr;
       const bool ok = key < p.Sk;
-      ks[rr][cc] = ok ? kb[(int64_t)key * p.k.ss + cc] : 0.f;
-      vs[rr][cc] = ok ? vb[(int64_t)key * p.v.ss + cc] : 0.f;
+      ks[g][rr][cc] = ok ? kb[(int64_t)key * p.k.ss + cc] : 0.f;
+      vs[g][rr][cc] = ok ? vb[(int64_t)key * p.v.ss + cc] : 0.f;
     }
     __syncthreads();
     // Every lane runs every step (the row sums exchange data across lanes);
@@ -138,8 +152,8 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        s = fmaf(q[f], ks[j][f0 + f], s);
-        dp = fmaf(dO[f], vs[j][f0 + f], dp);
+        s = fmaf(q[f], ks[g][j][f0 + f], s);
+        dp = fmaf(dO[f], vs[g][j][f0 + f], dp);
       }
       s = row_sum(s);
       dp = row_sum(dp);
@@ -147,10 +161,23 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
       const float pj = vis ? expf(s * p.scale - lse) : 0.f;
       const float ds = pj * (dp - dlt);
 #pragma unroll
-      for (int f = 0; f < F; ++f) dq[f] = fmaf(ds, ks[j][f0 + f], dq[f]);
+      for (int f = 0; f < F; ++f) dq[f] = fmaf(ds, ks[g][j][f0 + f], dq[f]);
     }
   }
-  if (!qok) return;
+  // Add the groups' partials in group order.
+  __syncthreads();
+  float* red = &ks[0][0][0];  // [QSPL][FROWS][D]
+#pragma unroll
+  for (int f = 0; f < F; ++f) red[(g * FROWS + r) * D + f0 + f] = dq[f];
+  __syncthreads();
+  if (g != 0 || !qok) return;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    float t = red[r * D + f0 + f];
+#pragma unroll
+    for (int k = 1; k < QSPL; ++k) t += red[(k * FROWS + r) * D + f0 + f];
+    dq[f] = t;
+  }
   float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D + f0;
   float* dqp = p.finalize_dq
                    ? (float*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh + f0
@@ -167,17 +194,17 @@ __global__ __launch_bounds__(FNT) void dq_f32_kernel(BwdParams p) {
 // ---------------------------------------------------------- fp32 dK/dV ----
 
 template <int D>
-__global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(KNT) void dkdv_f32_kernel(BwdParams p) {
   constexpr int F = D / TPR;
-  __shared__ __attribute__((aligned(16))) float qs[FTK][D];
-  __shared__ __attribute__((aligned(16))) float dos[FTK][D];
-  __shared__ float ls[FTK];
-  __shared__ float ds_[FTK];
-  const int tid = threadIdx.x, r = tid / TPR, c = tid % TPR, f0 = c * F;
+  __shared__ __attribute__((aligned(16))) float qs[KSPL][KTK][D];
+  __shared__ __attribute__((aligned(16))) float dos[KSPL][KTK][D];
+  __shared__ float ls[KSPL][KTK];
+  __shared__ float ds_[KSPL][KTK];
+  const int tid = threadIdx.x, g = tid / KGT, lt = tid % KGT, r = lt / TPR, c = lt % TPR, f0 = c * F;
   const int kt = blockIdx.x % p.n_ktiles;
   const int bh = blockIdx.x / p.n_ktiles;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  const int kj = kt * FROWS + r;
+  const int kj = kt * KROWS + r;
   const bool kok = kj < p.Sk;
   const float* kb = (const float*)p.k.ptr + (int64_t)b * p.k.sb + (int64_t)hk * p.k.sh;
   const float* vb = (const float*)p.v.ptr + (int64_t)b * p.v.sb + (int64_t)hk * p.v.sh;
@@ -191,58 +218,77 @@ __global__ __launch_bounds__(FNT) void dkdv_f32_kernel(BwdParams p) {
   }
   const int64_t need = (int64_t)kj - p.delta_pos;  // causal: query index must be >= need
   int i_start = 0;
-  if (p.causal) i_start = (int)min<int64_t>(p.Sq, max<int64_t>(0, (int64_t)kt * FROWS - p.delta_pos));
-  i_start = (i_start / FTK) * FTK;
+  if (p.causal) i_start = (int)min<int64_t>(p.Sq, max<int64_t>(0, (int64_t)kt * KROWS - p.delta_pos));
+  i_start = (i_start / KTK) * KTK;
+  // Group g takes query tiles g, g + KSPL, ... from i_start; every group runs the same count.
+  const int n_iter = ((p.Sq - i_start + KTK - 1) / KTK + KSPL - 1) / KSPL;
   for (int hh = 0; hh < p.group; ++hh) {
     const int h = hk * p.group + hh;
     const float* qb = (const float*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const float* dob = (const float*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
     const float* lseb = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
     const float* dltb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad;
-    for (int i0 = i_start; i0 < p.Sq; i0 += FTK) {
+    for (int it = 0; it < n_iter; ++it) {
+      const int i0 = i_start + (it * KSPL + g) * KTK;
       __syncthreads();
-      for (int e = tid; e < FTK * D; e += FNT) {
+      for (int e = lt; e < KTK * D; e += KGT) {
         const int rr = e / D, cc = e % D;
         const int i = i0 + rr;
         const bool ok = i < p.Sq;
-        qs[rr][cc] = ok ? qb[(int64_t)i * p.q.ss + cc] : 0.f;
-        dos[rr][cc] = ok ? dob[(int64_t)i * p.dout.ss + cc] : 0.f;
+        qs[g][rr][cc] = ok ? qb[(int64_t)i * p.q.ss + cc] : 0.f;
+        dos[g][rr][cc] = ok ? dob[(int64_t)i * p.dout.ss + cc] : 0.f;
       }
-      if (tid < FTK) {
-        const int i = i0 + tid;
-        ls[tid] = (i < p.Sq) ? lseb[(int64_t)i * p.lse_ss] : neg_inf();
-        ds_[tid] = (i < p.Sq) ? dltb[i] : 0.f;
+      if (lt < KTK) {
+        const int i = i0 + lt;
+        ls[g][lt] = (i < p.Sq) ? lseb[(int64_t)i * p.lse_ss] : neg_inf();
+        ds_[g][lt] = (i < p.Sq) ? dltb[i] : 0.f;
       }
       __syncthreads();
-#pragma unroll 8
-      for (int rr = 0; rr < FTK; ++rr) {
+#pragma unroll 2
+      for (int rr = 0; rr < KTK; ++rr) {
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int f = 0; f < F; ++f) {
-          s = fmaf(k[f], qs[rr][f0 + f], s);
-          dp = fmaf(v[f], dos[rr][f0 + f], dp);
+          s = fmaf(k[f], qs[g][rr][f0 + f], s);
+          dp = fmaf(v[f], dos[g][rr][f0 + f], dp);
         }
         s = row_sum(s);
         dp = row_sum(dp);
-        const float lse = ls[rr];
+        const float lse = ls[g][rr];
         const bool vis = kok && lse != neg_inf() && !(p.causal && (int64_t)(i0 + rr) < need);
         const float pj = vis ? expf(s * p.scale - lse) : 0.f;
-        const float ds = pj * (dp - ds_[rr]);
+        const float ds = pj * (dp - ds_[g][rr]);
 #pragma unroll
         for (int f = 0; f < F; ++f) {
-          dv[f] = fmaf(pj, dos[rr][f0 + f], dv[f]);
-          dk[f] = fmaf(ds, qs[rr][f0 + f], dk[f]);
+          dv[f] = fmaf(pj, dos[g][rr][f0 + f], dv[f]);
+          dk[f] = fmaf(ds, qs[g][rr][f0 + f], dk[f]);
         }
       }
     }
   }
-  if (!kok) return;
+  // Add the groups' partials in group order.
+  __syncthreads();
+  float* redk = &qs[0][0][0];   // [KSPL][KROWS][D]
+  float* redv = &dos[0][0][0];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    redk[(g * KROWS + r) * D + f0 + f] = dk[f];
+    redv[(g * KROWS + r) * D + f0 + f] = dv[f];
+  }
+  __syncthreads();
+  if (g != 0 || !kok) return;
   float* dkp = (float*)p.dk.ptr + (int64_t)b * p.dk.sb + (int64_t)kj * p.dk.ss + (int64_t)hk * p.dk.sh + f0;
   float* dvp = (float*)p.dv.ptr + (int64_t)b * p.dv.sb + (int64_t)kj * p.dv.ss + (int64_t)hk * p.dv.sh + f0;
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    dkp[f] = dk[f] * p.scale;
-    dvp[f] = dv[f];
+    float tk = redk[r * D + f0 + f], tv = redv[r * D + f0 + f];
+#pragma unroll
+    for (int k2 = 1; k2 < KSPL; ++k2) {
+      tk += redk[(k2 * KROWS + r) * D + f0 + f];
+      tv += redv[(k2 * KROWS + r) * D + f0 + f];
+    }
+    dkp[f] = tk * p.scale;
+    dvp[f] = tv;
   }
 }
 
@@ -264,19 +310,19 @@ hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_
 
 hipError_t launch_bwd_f32(const BwdParams& p0, int D, int run_dq, hipStream_t s) {
   BwdParams p = p0;
-  p.n_ktiles = (p.Sk + FROWS - 1) / FROWS;
+  p.n_ktiles = (p.Sk + KROWS - 1) / KROWS;
   p.n_qtiles = (p.Sq + FROWS - 1) / FROWS;
   const int64_t gk = (int64_t)p.B * p.Hkv * p.n_ktiles;
   if (gk > 0) {
-    if (D == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3((unsigned)gk), dim3(FNT), 0, s, p);
-    else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3((unsigned)gk), dim3(FNT), 0, s, p);
+    if (D == 128) hipLaunchKernelGGL(dkdv_f32_kernel<128>, dim3((unsigned)gk), dim3(KNT), 0, s, p);
+    else hipLaunchKernelGGL(dkdv_f32_kernel<64>, dim3((unsigned)gk), dim3(KNT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t gq = (int64_t)p.B * p.Hq * p.n_qtiles;
   if (run_dq && gq > 0) {
-    if (D == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)gq), dim3(FNT), 0, s, p);
-    else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)gq), dim3(FNT), 0, s, p);
+    if (D == 128) hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((unsigned)gq), dim3(QNT), 0, s, p);
+    else hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((unsigned)gq), dim3(QNT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -6,6 +6,11 @@
 // the row's lanes.  Key and value tiles of 32 rows are staged in LDS.
 // The online softmax is applied once per tile.  Same semantics, flags and
 // epilogue as the bf16 kernel.
+//
+// Small problems give few workgroups, so a workgroup splits its keys over
+// KSPL groups of threads: group g takes key tiles g, g + KSPL, ..., keeps its
+// own running (max, sum, O), and the groups' results are merged in LDS in a
+// fixed order at the end (deterministic; no atomics).
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -14,7 +19,9 @@ namespace {
 
 constexpr int TPR = 16;         // threads per query row
 constexpr int BM = 16;          // queries per workgroup
-constexpr int NT = TPR * BM;    // threads per workgroup
+constexpr int KSPL = 2;         // groups splitting the keys
+constexpr int GT = TPR * BM;    // threads per group
+constexpr int NT = GT * KSPL;   // threads per workgroup
 constexpr int TK = 32;          // keys per tile
 
 // Sum over the 16 lanes of this thread's row group (TPR = 16 lanes, one DPP row).
@@ -23,9 +30,10 @@ __device__ __forceinline__ float row_sum(float x) { return sum16(x); }
 template <int D>
 __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   constexpr int F = D / TPR;  // features per thread
-  __shared__ __attribute__((aligned(16))) float ks[TK][D];
-  __shared__ __attribute__((aligned(16))) float vs[TK][D];
-  const int tid = threadIdx.x, r = tid / TPR, c = tid % TPR, f0 = c * F;
+  __shared__ __attribute__((aligned(16))) float ks[KSPL][TK][D];
+  __shared__ __attribute__((aligned(16))) float vs[KSPL][TK][D];
+  __shared__ float m_s[KSPL][BM], l_s[KSPL][BM];
+  const int tid = threadIdx.x, g = tid / GT, lt = tid % GT, r = lt / TPR, c = lt % TPR, f0 = c * F;
   const int unit = blockIdx.x % p.n_units;
   const int bh = blockIdx.x / p.n_units;
   const int h = bh % p.Hq, b = bh / p.Hq, hk = h / p.group;
@@ -51,16 +59,18 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     kv_end = (int)max<int64_t>(0, min<int64_t>(p.delta + q_last + 1, p.Sk));
     lim = min<int64_t>(p.delta + qi, lim);
   }
-  // Every lane of a row holds the row's running maximum and sum.
+  // Every lane of a row holds the row's running maximum and sum (of its group's keys).
   float m_run = neg_inf(), l_run = 0.f;
-  for (int key0 = 0; key0 < kv_end; key0 += TK) {
+  const int n_iter = ((kv_end + TK - 1) / TK + KSPL - 1) / KSPL;  // the same count for every group
+  for (int it = 0; it < n_iter; ++it) {
+    const int key0 = (it * KSPL + g) * TK;
     __syncthreads();
-    for (int e = tid; e < TK * D; e += NT) {
+    for (int e = lt; e < TK * D; e += GT) {
       const int rr = e / D, cc = e % D;
       const int key = key0 + rr;
       const bool ok = key < p.Sk;
-      ks[rr][cc] = ok ? kb[(int64_t)key * p.k.ss + cc] : 0.f;
-      vs[rr][cc] = ok ? vb[(int64_t)key * p.v.ss + cc] : 0.f;
+      ks[g][rr][cc] = ok ? kb[(int64_t)key * p.k.ss + cc] : 0.f;
+      vs[g][rr][cc] = ok ? vb[(int64_t)key * p.v.ss + cc] : 0.f;
     }
     __syncthreads();
     float s[TK];
@@ -69,7 +79,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
     for (int j = 0; j < TK; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int f = 0; f < F; ++f) dot = fmaf(q[f], ks[j][f0 + f], dot);
+      for (int f = 0; f < F; ++f) dot = fmaf(q[f], ks[g][j][f0 + f], dot);
       dot = row_sum(dot);
       s[j] = (key0 + j <= lim) ? dot * p.scale : neg_inf();
       mt = fmaxf(mt, s[j]);
@@ -85,10 +95,37 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
       const float pj = expf(s[j] - m_use);
       l_run += pj;
 #pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] = fmaf(pj, vs[j][f0 + f], acc[f]);
+      for (int f = 0; f < F; ++f) acc[f] = fmaf(pj, vs[g][j][f0 + f], acc[f]);
     }
     m_run = m_new;
   }
+  // Merge the groups' partial results (group order), then the epilogue in group 0.
+  __syncthreads();
+  float* accs = &ks[0][0][0];  // [KSPL][BM][D]
+  if (c == 0) {
+    m_s[g][r] = m_run;
+    l_s[g][r] = l_run;
+  }
+#pragma unroll
+  for (int f = 0; f < F; ++f) accs[(g * BM + r) * D + f0 + f] = acc[f];
+  __syncthreads();
+  if (g != 0) return;
+  float M = neg_inf();
+#pragma unroll
+  for (int k = 0; k < KSPL; ++k) M = fmaxf(M, m_s[k][r]);
+  l_run = 0.f;
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+  if (M != neg_inf()) {
+#pragma unroll
+    for (int k = 0; k < KSPL; ++k) {
+      const float w = expf(m_s[k][r] - M);  // 0 for a group that saw no key
+      l_run = fmaf(w, l_s[k][r], l_run);
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[f] = fmaf(w, accs[(k * BM + r) * D + f0 + f], acc[f]);
+    }
+  }
+  m_run = M;
   if (!qok) return;
   const float lse_this = (m_run == neg_inf()) ? neg_inf() : m_run + logf(l_run);
   const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
