@@ -39,8 +39,9 @@ constexpr int QPW = 4;     // query heads per workgroup
 // Cache bytes are read exactly once per call.  V rows are read whole (16 lanes
 // x 16 B cover a 256-byte row) with the non-temporal hint, so they stream past
 // the caches.  K rows are read 64 bytes per instruction (the operand layout of
-// the score MFMA), two instructions per 128-byte line; under the streaming hint
-// about 9% of those lines were fetched twice, so K loads stay ordinary.
+// the score MFMA), two instructions per 128-byte line; with the streaming hint
+// on K as well, a call fetched 9% more bytes than the cache holds (lines
+// fetched twice) and ran slower, so K loads stay ordinary.
 template <class T>
 __device__ __forceinline__ T stream_load(const T* p) {
   return __builtin_nontemporal_load(p);
