@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
 // (deterministic; no atomics).
 constexpr int TPR = 16;                 // threads per row
 constexpr int FROWS = 16;               // query rows per dQ workgroup
-constexpr int QSPL = 4;                 // dQ: groups splitting the keys
+constexpr int QSPL = 2;                 // dQ: groups splitting the keys
 constexpr int FTK = 32;                 // dQ: key rows per staged tile
 constexpr int QGT = TPR * FROWS;        // dQ: threads per group
 constexpr int QNT = QGT * QSPL;         // dQ: threads per workgroup
