@@ -361,6 +361,51 @@ def pin_decode(impl):
         _close(O[b, 0], vc[b, :lens[b], 0].mean(axis=0), 1e-13, 1e-15, "decode mean")
 
 
+def pin_gqa_backward(impl):
+    """The batched backward with grouped heads: dK/dV of a key/value head sum the
+    contributions of every query head of its group, and query head h reads key/value
+    head h // (H_q / H_kv).  Checked against PyTorch autograd through SDPA with
+    enable_gqa (fp64, CPU), and against the scalar brute force run per query head on
+    its own key/value head and summed by hand over each group."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(23)
+    for (B, sq, sk, Hq, Hkv, d, causal, qp) in [(2, 9, 13, 6, 2, 4, True, 5), (1, 7, 7, 4, 4, 3, False, 0),
+                                                 (1, 6, 10, 8, 2, 4, True, 2)]:
+        q, k, v = _rand(rng, B, sq, Hq, d), _rand(rng, B, sk, Hkv, d), _rand(rng, B, sk, Hkv, d)
+        do = _rand(rng, B, sq, Hq, d)
+        c = 0.6
+        O, L = impl.attention(q, k, v, c, causal, qp, 0)
+        got = impl.attention_backward(q, k, v, O, do, L, c, causal, qp, 0)
+        # Autograd through SDPA, heads-major layout [B, H, S, d].
+        tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3).copy(), requires_grad=True) for x in (q, k, v))
+        mask = torch.ones(sq, sk, dtype=torch.bool)
+        if causal:
+            mask = torch.arange(sk)[None, :] <= (qp + torch.arange(sq))[:, None]
+        out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=c, enable_gqa=True)
+        out.backward(torch.from_numpy(do.transpose(0, 2, 1, 3).copy()))
+        for name, a, t in zip("qkv", got, (tq, tk, tv)):
+            _close(a, t.grad.numpy().transpose(0, 2, 1, 3), 1e-11, 1e-13, f"GQA d{name} vs autograd {Hq, Hkv}")
+        # Scalar brute force per query head, summed over each group by hand.
+        G = Hq // Hkv
+        ref = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G
+                bq, bk, bv = brute.backward(q[b, :, h].tolist(), k[b, :, g].tolist(), v[b, :, g].tolist(),
+                                            do[b, :, h].tolist(), c, causal, qp, 0)
+                ref[0][b, :, h] = bq
+                ref[1][b, :, g] += np.array(bk)
+                ref[2][b, :, g] += np.array(bv)
+        for name, a, r in zip("qkv", got, ref):
+            _close(a, r, 1e-11, 1e-13, f"GQA d{name} vs brute per head {Hq, Hkv}")
+        # A subset of query heads gives exactly their share: the other heads' dQ stays 0.
+        sub = impl.attention_backward(q, k, v, O, do, L, c, causal, qp, 0, heads=[0, Hq - 1])
+        _close(sub[0][:, :, [0, Hq - 1]], got[0][:, :, [0, Hq - 1]], 1e-15, 0, "GQA head subset dQ")
+        assert np.all(sub[0][:, :, 1:Hq - 1] == 0), "GQA head subset leaves other heads"
+
+
 ALL_PINS = [
     pin_brute_forward,
     pin_golden_two_keys,
@@ -375,4 +420,5 @@ ALL_PINS = [
     pin_sum_rules,
     pin_energy_gradient,
     pin_decode,
+    pin_gqa_backward,
 ]

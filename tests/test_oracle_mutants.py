@@ -40,6 +40,9 @@ MUTANTS = [
      "P = np.where(live[:, None], np.exp(s - lse_safe[:, None]), 0.0)", None),
     ("delta from dO only", "D = np.sum(do * o, axis=1)", "D = np.sum(do, axis=1)", None),
     ("GQA interleaved mapping", "return h // (H_q // H_kv)", "return h % H_kv", None),
+    ("GQA backward overwrites dK", "dk[b, :, g] += bk", "dk[b, :, g] = bk", None),
+    ("GQA backward overwrites dV", "dv[b, :, g] += bv", "dv[b, :, g] = bv", None),
+    ("GQA backward interleaved mapping", "g = _kv_head(h, H_q, H_kv)", "g = h % H_kv", 1),
     ("decode ignores seqlens", "n = L if seqlens is None else int(seqlens[b])", "n = L", None),
 ]
 
