@@ -75,6 +75,44 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+def resource_usage(sources=None) -> dict:
+    """Per-kernel register, scratch and LDS use as the compiler reports it.
+
+    Compiles each source (default: all) to a throw-away object with the
+    library's flags plus -Rpass-analysis=kernel-resource-usage and returns
+    {mangled kernel name: {"VGPRs": .., "AGPRs": .., "ScratchSize": .., "VGPRs Spill": ..,
+    "SGPRs Spill": .., "Occupancy": .., "LDS Size": ..}}.  The in-tree library is
+    not touched.
+    """
+    import re
+    import tempfile
+
+    out = {}
+    with tempfile.TemporaryDirectory() as tmp:
+        def one(src):
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                   "-o", obj]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr[-4000:]}")
+            return res.stdout + res.stderr
+
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+            texts = list(ex.map(one, sources or SOURCES))
+    for text in texts:
+        cur = None
+        for line in text.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = out.setdefault(m.group(1), {})
+                continue
+            m = re.search(r"remark: ([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = int(m.group(2))
+    return out
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--verbose", action="store_true", help="print kernel register/LDS usage")

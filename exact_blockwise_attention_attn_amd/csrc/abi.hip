@@ -53,6 +53,25 @@ int check_view(const char* name, const void* p, const int64_t* st, int n_st, uin
   return ATTN_OK;
 }
 
+// Key and value tiles are fetched as a wave-uniform row base plus a 32-bit
+// per-lane offset spanning 64 rows, so a key/value sequence stride may not
+// exceed 2^24 elements (a row stride of 32 MiB; [B, S, H, d] layouts have H * d).
+constexpr int64_t kMaxSeqStride = int64_t{1} << 24;
+int check_seq_stride(const char* name, int64_t ss, bool needed) {
+  if (needed && ss > kMaxSeqStride)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s sequence stride %lld exceeds 2^24 elements", name, (long long)ss);
+  return ATTN_OK;
+}
+
+// Every launch of a call must fit the 2^32 - 1 work-items a grid dimension
+// allows; checked for all of a call's launches before the first is enqueued.
+int check_items(int64_t items, const char* what) {
+  if (items > (int64_t)0xffffffffLL)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: problem too large for one launch (%lld work-items > 2^32 - 1)", what,
+                (long long)items);
+  return ATTN_OK;
+}
+
 int check_scale(float in, int head_dim, float* out) {
   if (in == 0.0f) {
     *out = 1.0f / sqrtf((float)head_dim);
@@ -137,6 +156,8 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
   TRY(check_view("k", a->k, a->k_stride, 3, a->dtype, has_q && has_k));
   TRY(check_view("v", a->v, a->v_stride, 3, a->dtype, has_q && has_k));
+  TRY(check_seq_stride("k", a->k_stride[1], has_q && has_k));
+  TRY(check_seq_stride("v", a->v_stride[1], has_q && has_k));
   TRY(check_view("o", a->o, a->o_stride, 3, a->o_dtype, has_q));
   if (has_q && !a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
   if (has_q && !aligned16(a->lse)) return fail(ATTN_ERR_UNSUPPORTED, "lse is not 16-byte aligned");
@@ -176,6 +197,8 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   const bool invisible = !varlen && (a->seqlen_k == 0 || (p.causal && p.delta + (a->seqlen_q - 1) < 0));
   if (invisible && accumulate && !a->o_final) return ok();
 
+  TRY(check_items(a->dtype == ATTN_DTYPE_BF16 ? attn::items_fwd_bf16(p) : attn::items_fwd_f32(p),
+                  "attn_fwd_partial"));
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = a->dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(p, a->head_dim, s)
                                              : attn::launch_fwd_f32(p, a->head_dim, s);
@@ -208,6 +231,8 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   if (a->o_final) TRY(check_view("o_final", a->o_final, a->o_final_stride, 3, ATTN_DTYPE_BF16, has_q));
   if (a->n_chunks > 0 && (!a->k_chunks || !a->v_chunks || !a->chunk_len || !a->chunk_pos0))
     return fail(ATTN_ERR_INVALID_ARG, "chunk arrays must not be NULL");
+  TRY(check_seq_stride("k_chunks", a->k_stride[1], has_q && a->n_chunks > 0));
+  TRY(check_seq_stride("v_chunks", a->v_stride[1], has_q && a->n_chunks > 0));
   attn::ChunkTable ct{};
   ct.q_pos0 = a->q_pos0;
   for (int c = 0; c < a->n_chunks; ++c) {
@@ -257,6 +282,7 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   p.balanced = (a->flags & ATTN_FWD_BALANCED) != 0;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  TRY(check_items(attn::items_fwd_bf16(p), "attn_fwd_chunks"));
   hipError_t e = attn::launch_fwd_chunks_bf16(p, ct, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunks launch");
   return ok();
@@ -301,6 +327,7 @@ int attn_merge_lse(const attn_merge_args* a, void* stream) {
   p.S = a->seqlen;
   p.H = a->heads;
   p.tree = a->mode == ATTN_MERGE_TREE;
+  TRY(check_items(attn::items_merge(p, a->head_dim), "attn_merge_lse"));
   hipError_t e = attn::launch_merge(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_merge_lse launch");
   return ok();
@@ -324,6 +351,8 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   TRY(check_view("q", a->q, a->q_stride, 3, a->dtype, has_q));
   TRY(check_view("k", a->k, a->k_stride, 3, a->dtype, has_k));
   TRY(check_view("v", a->v, a->v_stride, 3, a->dtype, has_k));
+  TRY(check_seq_stride("k", a->k_stride[1], has_q && has_k));
+  TRY(check_seq_stride("v", a->v_stride[1], has_q && has_k));
   TRY(check_view("o", a->o, a->o_stride, 3, a->dtype, has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)));
   TRY(check_view("dout", a->dout, a->do_stride, 3, a->dtype, has_q));
   TRY(check_view("dk", a->dk, a->dk_stride, 3, a->dtype, has_k));
@@ -375,9 +404,11 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  hipStream_t s = (hipStream_t)stream;
   const int D = a->head_dim;
   const int bf16 = a->dtype == ATTN_DTYPE_BF16;
+  TRY(check_items(attn::items_bwd_prepare(p, D), "attn_bwd"));
+  TRY(check_items(bf16 ? attn::items_bwd_bf16(p) : attn::items_bwd_f32(p), "attn_bwd"));
+  hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)) {
     e = attn::launch_bwd_prepare(p, D, bf16, s);
@@ -422,6 +453,8 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   if (a->n_chunks > 0 && (!a->k_chunks || !a->v_chunks || !a->dk_chunks || !a->dv_chunks || !a->chunk_len ||
                           !a->chunk_pos0))
     return fail(ATTN_ERR_INVALID_ARG, "chunk arrays must not be NULL");
+  TRY(check_seq_stride("k_chunks", a->k_stride[1], a->seqlen_q > 0 && a->n_chunks > 0));
+  TRY(check_seq_stride("v_chunks", a->v_stride[1], a->seqlen_q > 0 && a->n_chunks > 0));
   attn::BwdChunkTable ct{};
   ct.kv.q_pos0 = a->q_pos0;
   int64_t key_tiles = 0;
@@ -487,6 +520,8 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
 
+  TRY(check_items(attn::items_bwd_prepare(p, a->head_dim), "attn_bwd_chunks"));
+  TRY(check_items(attn::items_bwd_chunks_bf16(p, ct), "attn_bwd_chunks"));
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (has_q && (a->flags & ATTN_BWD_COMPUTE_DELTA)) {
@@ -598,6 +633,8 @@ int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
   TRY(check_view("q", a->q, a->q_stride, 2, ATTN_DTYPE_BF16, true));
   TRY(check_view("k_cache", a->k_cache, a->k_stride, 2, ATTN_DTYPE_BF16, a->cache_len > 0));
   TRY(check_view("v_cache", a->v_cache, a->v_stride, 2, ATTN_DTYPE_BF16, a->cache_len > 0));
+  TRY(check_seq_stride("k_cache", a->k_stride[0], a->cache_len > 0));
+  TRY(check_seq_stride("v_cache", a->v_stride[0], a->cache_len > 0));
   TRY(check_view("o", a->o, a->o_stride, 2, ATTN_DTYPE_BF16, true));
   if (!a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(a->lse)) return fail(ATTN_ERR_UNSUPPORTED, "lse is not 16-byte aligned");
@@ -630,6 +667,7 @@ int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
   p.o_f32 = 1;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  TRY(check_items(attn::items_tree_decode(p, tt, a->n_queries, a->head_dim), "attn_decode_tree"));
   hipError_t e = attn::launch_tree_decode(p, tt, a->n_queries, a->o, a->o_stride[0], a->o_stride[1], a->lse,
                                           a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode_tree launch");
@@ -703,6 +741,7 @@ int attn_decode_splitkv(const attn_decode_args* a, void* stream) {
   p.o_sb = a->o_stride[0];
   p.o_sh = a->o_stride[1];
   p.lse = a->lse;
+  TRY(check_items(attn::items_decode(p), "attn_decode_splitkv"));
   hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode_splitkv launch");
   return ok();

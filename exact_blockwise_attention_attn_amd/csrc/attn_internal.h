@@ -145,6 +145,20 @@ struct DecodeParams {
 };
 
 // Launchers (return the launch status).  D is the head dimension.
+// Largest number of work-items (workgroups x threads per workgroup) any one
+// launch of the matching launcher would use, from the launcher's own grid
+// formulas; a launch is limited to 2^32 - 1 work-items per grid dimension, and
+// the host checks every launch of a call before enqueueing the first.
+int64_t items_fwd_bf16(const FwdParams& p);
+int64_t items_fwd_f32(const FwdParams& p);
+int64_t items_merge(const MergeParams& p, int D);
+int64_t items_bwd_prepare(const BwdParams& p, int D);
+int64_t items_bwd_bf16(const BwdParams& p);
+int64_t items_bwd_chunks_bf16(const BwdParams& p, const BwdChunkTable& ct);
+int64_t items_bwd_f32(const BwdParams& p);
+int64_t items_decode(const DecodeParams& p);
+int64_t items_tree_decode(const FwdParams& p, const TreeTable& tt, int n_q, int D);
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
 // Fused forward over a chunk table (bf16): one launch, the running (O, LSE) of

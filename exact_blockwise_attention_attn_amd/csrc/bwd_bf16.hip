@@ -322,7 +322,15 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
 // Early keys are seen by the most queries, so they come first.
 template <int D, bool PW>
 __device__ __forceinline__ void dkdv_unit(const BwdParams& p, u16* q_s, u16* d_s, float (*st_s)[256],
-                                          u32x4 (*pex)[2][4][64], int wave, int lane, int unit, int b, int hk) {
+                                          u32x4 (*pex)[2][4][64], int wave, int unit, int b, int hk) {
+  // The two roles run in one kernel behind a wave-uniform branch, and the
+  // compiler places the second role's code after the first's.  The lane index
+  // comes from an opaque copy of the thread index made inside each role, so
+  // no per-lane value of the second role is computed ahead of the branch,
+  // where it would stay live through the first role.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   RowFrag<D> rf;
   TrFrag<D> tf;
   rf.init(lane);
@@ -341,13 +349,13 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];  // [pair][step parity][slab][lane]
   // The wavefront index is uniform across the wavefront; say so, so that the
   // role branch below is a scalar branch.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int unit = lin % p.n_units_k;
   const int bh = lin / p.n_units_k;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
-  if (wave < 4) dkdv_unit<D, true>(p, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
-  else dkdv_unit<D, false>(p, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
+  if (wave < 4) dkdv_unit<D, true>(p, q_s, d_s, st_s, pex_s, wave, unit, b, hk);
+  else dkdv_unit<D, false>(p, q_s, d_s, st_s, pex_s, wave, unit, b, hk);
 }
 
 // The same over the chunks of a table: work unit u of the whole grid belongs
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_chunks_kernel(BwdParams p, BwdChu
   __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) float st_s[3][256];
   __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int gunit = lin % ct.n_units;
   const int bh = lin / ct.n_units;
@@ -379,8 +387,8 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_chunks_kernel(BwdParams p, BwdChu
   pc.delta_pos = ct.kv.q_pos0 - ct.kv.pos0[c];
   pc.n_ktiles = (pc.Sk + KBN - 1) / KBN;
   const int unit = gunit - ct.unit0[c];
-  if (wave < 4) dkdv_unit<D, true>(pc, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
-  else dkdv_unit<D, false>(pc, q_s, d_s, st_s, pex_s, wave, lane, unit, b, hk);
+  if (wave < 4) dkdv_unit<D, true>(pc, q_s, d_s, st_s, pex_s, wave, unit, b, hk);
+  else dkdv_unit<D, false>(pc, q_s, d_s, st_s, pex_s, wave, unit, b, hk);
 }
 
 // --------------------------------------------------------------------- dQ --
@@ -405,6 +413,20 @@ struct KeySeg {
   int Sk;
   int64_t delta_pos;
 };
+
+// Lane index within the wavefront, from the count of lanes below this one
+// (two vector instructions).  Volatile, so the compiler recomputes it where it
+// is written instead of hoisting it and keeping a register live meanwhile.
+__device__ __forceinline__ int lane_id() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
+// x clamped to [0, n], for wave-uniform x.  Written as compares and selects:
+// as a 64-bit min/max the compiler forms it with double-precision vector
+// operations, whose operands then sit in vector registers.
+__device__ __forceinline__ int clamp_len(int64_t x, int n) { return x <= 0 ? 0 : (x >= n ? n : (int)x); }
 
 template <int D, class Seg>
 __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int unit, int n_seg, Seg seg) {
@@ -455,7 +477,6 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   TileSrc<D, 8> ksrc, vsrc;
-  const bool kfast = TileSrc<D, 8>::fits(p.k.ss), vfast = TileSrc<D, 8>::fits(p.v.ss);
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
   using I0 = std::integral_constant<int, 0>;
@@ -471,14 +492,17 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
     int kv_end = sg.Sk, full_end = sg.Sk;
     int64_t lim64 = (int64_t)sg.Sk - 1;  // last key of the segment this lane's query sees
     if (p.causal) {
-      kv_end = (int)max<int64_t>(0, min<int64_t>(sg.delta_pos + q_last + 1, sg.Sk));
-      full_end = (int)max<int64_t>(0, min<int64_t>(sg.delta_pos + q0 + 1, sg.Sk));
-      lim64 = min<int64_t>(sg.delta_pos + qi, lim64);
+      kv_end = clamp_len(sg.delta_pos + q_last + 1, sg.Sk);
+      full_end = clamp_len(sg.delta_pos + q0 + 1, sg.Sk);
+      // The query index is recomputed here from the lane index rather than
+      // kept live across all segments.
+      const int qi_s = q0 + pair * 32 + (lane_id() & 31);
+      lim64 = min<int64_t>(sg.delta_pos + qi_s, lim64);
     }
     const int n = (kv_end + QBN - 1) / QBN;
     auto issue = [&](int tile, int slot) {
-      ksrc.issue(k_s + slot * SZ, sg.kb, p.k.ss, tile * QBN, sg.Sk, kfast, wave, lane);
-      vsrc.issue(v_s + slot * SZ, sg.vb, p.v.ss, tile * QBN, sg.Sk, vfast, wave, lane);
+      ksrc.issue(k_s + slot * SZ, sg.kb, p.k.ss, tile * QBN, sg.Sk, wave, lane);
+      vsrc.issue(v_s + slot * SZ, sg.vb, p.v.ss, tile * QBN, sg.Sk, wave, lane);
     };
     if (n > 0) {
       issue(0, 0);
@@ -506,7 +530,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
         // Operand j: key rows (even j) or value rows (odd j) of slab j/2, read
         // AH ahead of the MFMA that uses them; the hard scheduling boundaries
         // hold each read in its slot.
-        constexpr int NJ = 2 * NS, AH = DQ_AHEAD;
+        constexpr int NJ = 2 * NS, AH = decltype(masked_c)::value ? 2 : DQ_AHEAD;
         bf16x8 f[NJ];
 #pragma unroll
         for (int j = 0; j < AH; ++j) f[j] = rf.get((j & 1) ? vt : kt, kh, j >> 1);
@@ -538,7 +562,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
       const bf16x8 sb[2] = {slab8(sc, 0), slab8(sc, 8)};
       __builtin_amdgcn_s_setprio(1);
       {
-        constexpr int NJ = 2 * NDB, AH = DQ_AHEAD_T;
+        constexpr int NJ = 2 * NDB, AH = decltype(masked_c)::value ? 2 : DQ_AHEAD_T;
         bf16x8 f[NJ];
 #pragma unroll
         for (int j = 0; j < AH; ++j) f[j] = tf.get(kt, kh * 2 + j / NDB, j % NDB);
@@ -574,29 +598,32 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
   }
 
   // Add the pair's two partials: the key-half-1 wavefront hands its dQ^T to
-  // its partner through LDS (the tile ring is free now).
-  float* red = (float*)tiles + pair * (NDB * 16 * 64);
+  // its partner through LDS (the tile ring is free now).  The lane index is
+  // recomputed here rather than kept live across the loop.
+  const int lane_e = lane_id();
+  float* red = (float*)tiles + pair * (NDB * 16 * 64) + lane_e * 4;
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; i += 4)
-        *(f32x4*)(red + (db * 16 + i) * 64 + lane * 4) = f32x4{acc[db][i], acc[db][i + 1], acc[db][i + 2], acc[db][i + 3]};
+        *(f32x4*)(red + (db * 16 + i) * 64) = f32x4{acc[db][i], acc[db][i + 1], acc[db][i + 2], acc[db][i + 3]};
   }
   lds_barrier();
-  if (kh == 1 || !qok) return;
+  const int qi_e = q0 + pair * 32 + (lane_e & 31);
+  if (kh == 1 || qi_e >= p.Sq) return;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
-      const f32x4 o = *(const f32x4*)(red + (db * 16 + i) * 64 + lane * 4);
+      const f32x4 o = *(const f32x4*)(red + (db * 16 + i) * 64);
       acc[db][i] += o[0];
       acc[db][i + 1] += o[1];
       acc[db][i + 2] += o[2];
       acc[db][i + 3] += o[3];
     }
-  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi) * p.Hq + h) * D;
-  u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi * p.dq.ss + (int64_t)h * p.dq.sh
+  float* accp = p.dq_acc + (((int64_t)b * p.Sq + qi_e) * p.Hq + h) * D;
+  u16* dqp = p.finalize_dq ? (u16*)p.dq.ptr + (int64_t)b * p.dq.sb + (int64_t)qi_e * p.dq.ss + (int64_t)h * p.dq.sh
                            : nullptr;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -664,14 +691,14 @@ __global__ __launch_bounds__(DKV_NT) void dkdv_varlen_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) float st_s[3][256];
   __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hkv, p.n_units_k);
   const int unit = w.unit, hk = w.h, b = w.b;
   BwdParams s = varlen_seq(p, b, D);
   s.n_ktiles = (s.Sk + KBN - 1) / KBN;
   if (unit >= (p.balanced ? (s.n_ktiles + 1) / 2 : s.n_ktiles)) return;
-  if (wave < 4) dkdv_unit<D, true>(s, q_s, d_s, st_s, pex_s, wave, lane, unit, 0, hk);
-  else dkdv_unit<D, false>(s, q_s, d_s, st_s, pex_s, wave, lane, unit, 0, hk);
+  if (wave < 4) dkdv_unit<D, true>(s, q_s, d_s, st_s, pex_s, wave, unit, 0, hk);
+  else dkdv_unit<D, false>(s, q_s, d_s, st_s, pex_s, wave, unit, 0, hk);
 }
 
 template <int D>
@@ -688,6 +715,23 @@ __global__ __launch_bounds__(DQ_NT) void dq_varlen_kernel(BwdParams p) {
 }
 
 }  // namespace
+
+int64_t items_bwd_bf16(const BwdParams& p) {
+  const int64_t n_ktiles = (p.Sk + KBN - 1) / KBN;
+  const int64_t gk = (int64_t)p.B * p.Hkv * (p.balanced ? (n_ktiles + 1) / 2 : n_ktiles);
+  const int64_t gq = (int64_t)p.B * p.Hq * ((p.Sq + QBM - 1) / QBM);
+  return std::max(gk * DKV_NT, gq * DQ_NT);
+}
+
+int64_t items_bwd_chunks_bf16(const BwdParams& p, const BwdChunkTable& ct) {
+  int64_t units = 0;
+  for (int c = 0; c < ct.kv.n; ++c) {
+    const int64_t nk = (ct.kv.len[c] + KBN - 1) / KBN;
+    units += p.balanced ? (nk + 1) / 2 : nk;
+  }
+  const int64_t gq = (int64_t)p.B * p.Hq * ((p.Sq + QBM - 1) / QBM);
+  return std::max((int64_t)p.B * p.Hkv * units * DKV_NT, gq * DQ_NT);
+}
 
 hipError_t launch_bwd_bf16(const BwdParams& p0, int D, int run_dq, hipStream_t s) {
   BwdParams p = p0;

@@ -294,6 +294,17 @@ __global__ __launch_bounds__(KNT) void dkdv_f32_kernel(BwdParams p) {
 
 }  // namespace
 
+int64_t items_bwd_prepare(const BwdParams& p, int D) {
+  const int64_t threads = (int64_t)p.B * p.Hq * p.Sq_pad * (D / 8);
+  return (threads + 255) / 256 * 256;
+}
+
+int64_t items_bwd_f32(const BwdParams& p) {
+  const int64_t gk = (int64_t)p.B * p.Hkv * ((p.Sk + KROWS - 1) / KROWS);
+  const int64_t gq = (int64_t)p.B * p.Hq * ((p.Sq + FROWS - 1) / FROWS);
+  return std::max(gk * KNT, gq * QNT);
+}
+
 hipError_t launch_bwd_prepare(const BwdParams& p, int D, int is_bf16, hipStream_t s) {
   const int64_t threads = (int64_t)p.B * p.Hq * p.Sq_pad * (D / 8);
   if (threads == 0) return hipSuccess;

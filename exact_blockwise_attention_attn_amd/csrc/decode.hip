@@ -302,6 +302,11 @@ __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) 
 
 }  // namespace
 
+int64_t items_decode(const DecodeParams& p) {
+  const int64_t n_qblk = (p.group + QPW - 1) / QPW;
+  return std::max((int64_t)p.B * p.Hkv * n_qblk * p.n_splits * NT, (int64_t)p.B * p.Hq * TREE_NT);
+}
+
 hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s) {
   const int n_qblk = (p.group + QPW - 1) / QPW;
   const int64_t grid = (int64_t)p.B * p.Hkv * n_qblk * p.n_splits;

@@ -219,12 +219,11 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
   TileSrc<D, 4> ksrc, vsrc;
-  const bool kfast = TileSrc<D, 4>::fits(p.k.ss), vfast = TileSrc<D, 4>::fits(p.v.ss);
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
   auto issue = [&](u16* ks, u16* vs, int key0) {
-    ksrc.issue(ks, kb, p.k.ss, key0, p.Sk, kfast, wave, lane);
-    vsrc.issue(vs, vb, p.v.ss, key0, p.Sk, vfast, wave, lane);
+    ksrc.issue(ks, kb, p.k.ss, key0, p.Sk, wave, lane);
+    vsrc.issue(vs, vb, p.v.ss, key0, p.Sk, wave, lane);
   };
   if (n_tiles > 0) issue(k0s, v0s, 0);
 
@@ -481,7 +480,6 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
   tf.init(lane);
 
   TileSrc<D, 4> ksrc, vsrc;
-  const bool kfast = TileSrc<D, 4>::fits(p.k.ss), vfast = TileSrc<D, 4>::fits(p.v.ss);
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
   // What the steps need of a chunk, read from the table once per chunk (the
@@ -504,8 +502,8 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
     return k;
   };
   auto issue = [&](const Chunk& k, int tile, int slot) {
-    ksrc.issue(k_s + slot * SZ, k.kb, p.k.ss, tile * BN, k.len, kfast, wave, lane);
-    vsrc.issue(v_s + slot * SZ, k.vb, p.v.ss, tile * BN, k.len, vfast, wave, lane);
+    ksrc.issue(k_s + slot * SZ, k.kb, p.k.ss, tile * BN, k.len, wave, lane);
+    vsrc.issue(v_s + slot * SZ, k.vb, p.v.ss, tile * BN, k.len, wave, lane);
   };
 
   int c = first_from(0), t = 0;
@@ -566,6 +564,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_chunks_kernel(FwdParams p, ChunkTab
 }
 
 }  // namespace
+
+int64_t items_fwd_bf16(const FwdParams& p) {
+  const int64_t n_qtiles = (p.Sq + BM - 1) / BM;
+  const int64_t n_units = p.balanced ? (n_qtiles + 1) / 2 : n_qtiles;
+  return (int64_t)p.B * p.Hq * n_units * NT;
+}
+
+int64_t items_tree_decode(const FwdParams& p, const TreeTable& tt, int n_q, int D) {
+  const int64_t n_units = ((int64_t)tt.max_q * p.group + BM - 1) / BM;
+  return std::max<int64_t>((int64_t)tt.n * p.Hkv * n_units * NT, (int64_t)n_q * p.Hq * D);
+}
 
 hipError_t launch_fwd_chunks_bf16(const FwdParams& p0, const ChunkTable& ct, int D, hipStream_t s) {
   FwdParams p = p0;

@@ -153,6 +153,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
 
 }  // namespace
 
+int64_t items_fwd_f32(const FwdParams& p) { return (int64_t)p.B * p.Hq * ((p.Sq + BM - 1) / BM) * NT; }
+
 hipError_t launch_fwd_f32(const FwdParams& p0, int D, hipStream_t s) {
   FwdParams p = p0;
   p.n_qtiles = (p.Sq + BM - 1) / BM;

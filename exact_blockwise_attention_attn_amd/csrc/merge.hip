@@ -98,6 +98,11 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p) {
 
 }  // namespace
 
+int64_t items_merge(const MergeParams& p, int D) {
+  const int64_t threads = (int64_t)p.B * p.S * p.H * (D / 4);
+  return (threads + NT - 1) / NT * NT;
+}
+
 hipError_t launch_merge(const MergeParams& p, int D, hipStream_t s) {
   const int64_t threads = (int64_t)p.B * p.S * p.H * (D / 4);
   if (threads == 0) return hipSuccess;

@@ -100,37 +100,50 @@ __device__ __forceinline__ void dma16_untracked_s(const void* sbase, unsigned vo
                : "memory", "m0", "scc");
 }
 
-// Per-lane byte offsets of the 64-row tile copy (the pattern issue_swtile
-// follows), computed once, so that each later load is the tile's first row
-// (wave-uniform) plus this lane's offset.  Usable while the tile's last byte
-// lies within 4 GiB of its first row (the offsets are 32-bit), which fits()
-// tells; tiles that run past the last row fall back to issue_swtile, which
-// clamps rows.
+// Per-lane byte offset of the 64-row tile copy (the pattern issue_swtile
+// follows), computed once, so that each later load is a wave-uniform base plus
+// this lane's offset.  A wavefront's i-th load covers the rows of its first
+// load plus 64 * NW * i / CH, a multiple of 16, and the chunk swizzle depends
+// only on the row modulo 16, so every load of the wavefront shares one lane
+// offset and the row step goes into the scalar base.  A tile that runs past
+// the last row clamps each lane's row to it and recomputes the offset on the
+// spot (no per-lane pointers stay live).  The offset is 32-bit, so the row
+// stride ss must lie in [0, 2^24] elements (64 rows then span under 2 GiB);
+// the host rejects larger key/value sequence strides.
 template <int D, int NW>
 struct TileSrc {
-  static constexpr int N = SwTile<D>::RUNS / NW;  // loads per wavefront per tile
-  unsigned off[N];
-  __device__ __forceinline__ static bool fits(int64_t ss) { return ss >= 0 && ss <= (int64_t{1} << 24); }
+  static constexpr int N = SwTile<D>::RUNS / NW;             // loads per wavefront per tile
+  static constexpr int ROW_STEP = NW * 64 / SwTile<D>::CH;  // rows between a wavefront's loads
+  static_assert(ROW_STEP % 16 == 0, "the swizzle must repeat between a wavefront's loads");
+  unsigned off;
   __device__ __forceinline__ void init(int64_t ss, int wave, int lane) {
     using T = SwTile<D>;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int slot = (wave + i * NW) * 64 + lane;
-      const int r = slot / T::CH;
-      off[i] = (unsigned)(((int64_t)r * ss + ((slot % T::CH) ^ swz<D>(r)) * 8) * 2);
-    }
+    const int slot = wave * 64 + lane;
+    const int r = slot / T::CH;
+    off = (unsigned)(((int64_t)r * ss + ((slot % T::CH) ^ swz<D>(r)) * 8) * 2);
   }
-  // Copy rows [row0, row0 + 64) of g (row stride ss) into lds, untracked.
-  // fast: fits(ss) held when the offsets were made.
-  __device__ __forceinline__ void issue(u16* lds, const u16* g, int64_t ss, int row0, int nrows, bool fast, int wave,
+  // Copy rows [row0, row0 + 64) of g (row stride ss) into lds, untracked; rows
+  // at or past nrows load row nrows - 1 (row0 < nrows).
+  __device__ __forceinline__ void issue(u16* lds, const u16* g, int64_t ss, int row0, int nrows, int wave,
                                         int lane) const {
-    if (fast && row0 + 64 <= nrows) {
-      const u16* base = g + (int64_t)row0 * ss;
+    using T = SwTile<D>;
+    const u16* base = g + (int64_t)row0 * ss;
+    if (row0 + 64 <= nrows) {
 #pragma unroll
       for (int i = 0; i < N; ++i)
-        dma16_untracked_s(base, off[i], (lds_void*)(lds + i * NW * 512), (unsigned)wave * 1024u);
+        dma16_untracked_s(base + (int64_t)(i * ROW_STEP) * ss, off, (lds_void*)(lds + i * NW * 512),
+                          (unsigned)wave * 1024u);
     } else {
-      issue_swtile<D, NW, true>(lds, g, ss, row0, nrows, wave, lane);
+      const int last = nrows - 1 - row0;  // last valid row of the tile, >= 0
+      const int slot = wave * 64 + lane;
+      const int r0 = slot / T::CH;
+      const int cpos = ((slot % T::CH) ^ swz<D>(r0)) * 8;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int r = min(r0 + i * ROW_STEP, last);
+        dma16_untracked_s(base, (unsigned)(r * (int)ss + cpos) * 2u, (lds_void*)(lds + i * NW * 512),
+                          (unsigned)wave * 1024u);
+      }
     }
   }
 };

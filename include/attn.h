@@ -34,6 +34,10 @@
  *     LSE vectors are contiguous fp32 [batch, heads, seq].
  *   - All pointers are device pointers unless stated otherwise, 16-byte
  *     aligned, and element strides must keep every row start 16-byte aligned.
+ *     Strides are never negative.  The sequence stride of keys and values (and
+ *     of the decode-tree caches) is at most 2^24 elements: tiles of 64 rows are
+ *     addressed as one row base plus a 32-bit offset per lane; a larger stride
+ *     returns ATTN_ERR_UNSUPPORTED.
  *     The caller owns every buffer; the library never allocates, frees or
  *     retains a pointer past the call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -41,7 +45,10 @@
  *     Device-side faults surface at the caller's next synchronisation.
  *   - Every argument is checked on the host before anything is enqueued; on
  *     error the call returns a nonzero status, enqueues nothing, leaves every
- *     output untouched and records a message for attn_last_error().
+ *     output untouched and records a message for attn_last_error().  This
+ *     includes the size of every kernel launch the call would make: a problem
+ *     that needs more than 2^32 - 1 work-items in one launch returns
+ *     ATTN_ERR_UNSUPPORTED before the first launch.
  *   - Argument structs start with struct_size = sizeof(the struct).
  *   - head_dim must be 64 or 128.  Scale 0 means 1/sqrt(head_dim); otherwise it
  *     must be finite and positive.
@@ -401,7 +408,7 @@ typedef struct attn_decode_args {
 
 ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
 
-/* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
+/* Most nodes a decode tree may have (attn_decode_tree below). */
 #define ATTN_MAX_TREE_NODES 256
 
 /*
@@ -458,6 +465,7 @@ ATTN_API int attn_decode_tree(const attn_decode_tree_args* args, void* stream);
  * head_dim are read); 0 if they are invalid. */
 ATTN_API size_t attn_decode_tree_workspace_size(const attn_decode_tree_args* args);
 
+/* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
 ATTN_API size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q);
 
 /* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes). */

@@ -147,6 +147,13 @@ FWD_BAD = [
     (dict(flags=1 << 5), B.ATTN_ERR_INVALID_ARG, "flag"),
     (dict(flags=B.ATTN_FWD_ACCUMULATE, o_dtype=B.ATTN_DTYPE_BF16), B.ATTN_ERR_INVALID_ARG, "ACCUMULATE"),
     (dict(o_final=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "o_final"),
+    (dict(k_stride=B.I64x3(0, (1 << 24) + 64, 128)), B.ATTN_ERR_UNSUPPORTED, "k sequence stride"),
+    (dict(v_stride=B.I64x3(0, (1 << 24) + 64, 128)), B.ATTN_ERR_UNSUPPORTED, "v sequence stride"),
+    # 1024 heads x 2^21 queries: 2^25 64-row units, but 2^24 workgroups of 256 threads = 2^32 work-items.
+    (dict(heads_q=1024, heads_kv=1024, seqlen_q=1 << 21, seqlen_k=1,
+          q_stride=B.I64x3(0, 1024 * 128, 128), o_stride=B.I64x3(0, 1024 * 128, 128),
+          k_stride=B.I64x3(0, 1024 * 128, 128), v_stride=B.I64x3(0, 1024 * 128, 128)),
+     B.ATTN_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
@@ -188,6 +195,9 @@ MERGE_BAD = [
     (dict(lse_out=None), B.ATTN_ERR_INVALID_ARG, "NULL"),
     (dict(o_part_stride=0), B.ATTN_ERR_INVALID_ARG, "part strides"),
     (dict(o_out_dtype=9), B.ATTN_ERR_UNSUPPORTED, "o_out_dtype"),
+    # One thread per 4 features: 2^20 rows x 1024 heads x 32 threads = 2^35 work-items.
+    (dict(n_parts=1, seqlen=1 << 20, heads=1024, head_dim=128, o_stride=B.I64x3(0, 1024 * 128, 128),
+          o_out_stride=B.I64x3(0, 1024 * 128, 128)), B.ATTN_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
@@ -226,6 +236,12 @@ BWD_BAD = [
     (dict(o=None, flags=B.ATTN_BWD_COMPUTE_DELTA), B.ATTN_ERR_INVALID_ARG, "o is NULL"),
     (dict(head_dim=256), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(scale=float("inf")), B.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(k_stride=B.I64x3(0, (1 << 24) + 64, 64)), B.ATTN_ERR_UNSUPPORTED, "k sequence stride"),
+    # dK/dV: 2 x 2^24 keys -> 2^17 128-key workgroups x 512 threads = 2^26 per head, x 64 heads = 2^32.
+    (dict(heads_q=64, heads_kv=64, seqlen_q=64, seqlen_k=1 << 24, workspace_bytes=1 << 20,
+          k_stride=B.I64x3(0, 64 * 64, 64), v_stride=B.I64x3(0, 64 * 64, 64), dk_stride=B.I64x3(0, 64 * 64, 64),
+          dv_stride=B.I64x3(0, 64 * 64, 64)),
+     B.ATTN_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
@@ -265,6 +281,7 @@ CHUNKS_BAD = [
     (dict(k_stride=B.I64x3(64 * 2 * 64, 2 * 64, 3)), B.ATTN_ERR_UNSUPPORTED, "k_chunks[0] stride"),
     (dict(head_dim=96), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(chunk_k_bstride=(ctypes.c_int64 * 2)(5, 5)), B.ATTN_ERR_UNSUPPORTED, "k_chunks[0] stride[0]"),
+    (dict(v_stride=B.I64x3(0, (1 << 24) + 64, 64)), B.ATTN_ERR_UNSUPPORTED, "v_chunks sequence stride"),
 ]
 
 
@@ -351,6 +368,7 @@ BWD_CHUNKS_BAD = [
     (dict(dv_chunks=None), B.ATTN_ERR_INVALID_ARG, "chunk arrays"),
     (dict(dk_stride=B.I64x3(64 * 2 * 64, 2 * 64, 3)), B.ATTN_ERR_UNSUPPORTED, "dk_chunks[0] stride"),
     (dict(chunk_dv_bstride=(ctypes.c_int64 * 2)(6, 6)), B.ATTN_ERR_UNSUPPORTED, "dv_chunks[0] stride[0]"),
+    (dict(k_stride=B.I64x3(0, (1 << 24) + 64, 64)), B.ATTN_ERR_UNSUPPORTED, "k_chunks sequence stride"),
     (dict(head_dim=96), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
 ]
 
@@ -406,6 +424,7 @@ TREE_BAD = [
     (dict(head_dim=80), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse is NULL"),
     (dict(kv_len=None), B.ATTN_ERR_INVALID_ARG, "node arrays"),
+    (dict(k_stride=B.I64x2((1 << 24) + 64, 128)), B.ATTN_ERR_UNSUPPORTED, "k_cache sequence stride"),
 ]
 
 
@@ -464,6 +483,8 @@ DECODE_BAD = [
     (dict(seqlens=FAKE + 2), B.ATTN_ERR_UNSUPPORTED, "seqlens"),
     (dict(k_stride=B.I64x3(1000 * 2 * 128, 2 * 128 + 1, 128)), B.ATTN_ERR_UNSUPPORTED, "alignment"),
     (dict(lse=None), B.ATTN_ERR_INVALID_ARG, "lse"),
+    # 2^14 sequences x 2 key/value heads x 1024 splits = 2^25 workgroups of 256 threads.
+    (dict(batch=1 << 14, n_splits=1024, workspace_bytes=1 << 40), B.ATTN_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
