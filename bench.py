@@ -15,8 +15,11 @@ Prints one JSON line.  Besides the contract fields it carries:
   kernels       per-call timings (forward call, backward call);
   secondary     the other workloads: the 128K sequence shard forward over 32
                 chunks, its backward, and split-KV GQA decode (GB/s of K/V);
-  cpu_baseline  the fp64 oracle on a bounded sample (one head, a 12288-token
-                causal prefix, forward + backward) on the host's cores.
+  cpu_baseline  the fp64 oracle, unmodified, on bounded samples of each workload
+                on the host's cores (value: one full (batch, head) of the
+                causal 32K workload, forward + backward), with the host's
+                core count, CPU model and BLAS, and per-workload times with
+                labelled linear extrapolations to the full sizes.
 Inputs are seeded synthetic N(0,1) values generated on the device and rounded
 to bf16; they are resident in HBM before timing starts.
 """
@@ -39,7 +42,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # runs of its kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
 # copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md): 14.36 GB read + 3.19 GB written.  Set to
 # None whenever these kernels change, until they are measured again.
-BWD_CALL_HBM_BYTES = 17552944992
+BWD_CALL_HBM_BYTES = None
 HBM_PEAK_GBS = 8000.0
 
 
@@ -350,30 +353,116 @@ def bench_decode(args, stream):
                                "frac_hbm": u_bytes / tu / 1e6 / HBM_PEAK_GBS}}
 
 
-def cpu_baseline():
-    """The fp64 oracle on a bounded sample: one (b, h), causal prefix of 12288 tokens, fwd + bwd."""
-    import numpy as np
-
-    import oracle
-    from seeded_inputs import bf16_bits_to_f32, normal_bf16
-
+def _host_facts():
+    facts = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": []}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    facts["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+        facts["blas"] = [{"api": i.get("internal_api"), "version": i.get("version"), "threads": i.get("num_threads")}
+                         for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
-    S, D = 12288, 128
-    x = [bf16_bits_to_f32(normal_bf16(5, t, 1, (S, 1, D))[0, :, 0]).astype(np.float64) for t in range(4)]
+        pass
+    return facts
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, timed on bounded samples of each workload on the host's cores.
+
+    Inputs are seeded N(0,1) rounded to bf16 (fp32 for the fp32 workload), the
+    shapes and positions of each workload's sample; generation is not timed.
+    Full-size times are linear extrapolations from the sample (per head, per
+    sampled row, or per (batch, key/value head)) and are labelled as such.
+    """
+    import numpy as np
+
+    import oracle
+    from seeded_inputs import bf16_bits_to_f32, normal_f32
+    from seeded_inputs.gen import normal_bf16_bits
+
+    facts = _host_facts()
+    threads = max([b["threads"] or 0 for b in facts["blas"]] or [0]) or facts["affinity_cores"]
+    gen = lambda wid, t, s, d: bf16_bits_to_f32(normal_bf16_bits(wid, t, 0, (s, 1, d))[:, 0]).astype(np.float64)  # noqa: E731
+    configs = {}
+
+    def timed(f):
+        t0 = time.perf_counter()
+        r = f()
+        return r, time.perf_counter() - t0
+
+    # Causal self-attention, 32K (the headline workload): one (batch, head) in full, fwd + bwd.
+    S, D = 32768, 128
+    q, k, v, do = (gen(5, t, S, D) for t in range(4))
     c = 1 / math.sqrt(D)
-    t0 = time.perf_counter()
-    O, L = oracle.attention_head(x[0], x[1], x[2], c, True)
-    oracle.attention_backward_head(x[0], x[1], x[2], O, x[3], L, c, True)
-    dt = time.perf_counter() - t0
-    flops = 3.5 * causal_flops(1, 1, S, D)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one (batch, head), causal prefix of {S} tokens, d={D}, forward + backward, fp64 NumPy; "
-                      f"{dt:.1f} s for {flops / 1e9:.1f} GFLOP (same FLOP convention)"}
+    (O, L), tf = timed(lambda: oracle.attention_head(q, k, v, c, True))
+    _, tb = timed(lambda: oracle.attention_backward_head(q, k, v, O, do, L, c, True))
+    per_head = 3.5 * causal_flops(1, 1, S, D)
+    configs["causal_fwdbwd_32k"] = {
+        "sample": "one (batch, head) of 64, S=32768, forward + backward", "fwd_s": round(tf, 2), "bwd_s": round(tb, 2),
+        "tflops": per_head / (tf + tb) / 1e12, "full_s_extrapolated": round(64 * (tf + tb), 1)}
+    del q, k, v, do, O, L
+
+    # 128K shard forward: 256 sampled query rows of one head (rows 0-127 and 3968-4095 at positions
+    # 65536 + i) against the keys up to the shard's last position; backward: one head in full.
+    SQ, QP = 4096, 65536
+    last = QP + SQ
+    q, do = gen(2, 0, SQ, D), gen(2, 3, SQ, D)
+    k, v = gen(2, 1, last, D), gen(2, 2, last, D)
+    rows = np.r_[0:128, SQ - 128:SQ]
+    t_rows = 0.0
+    for a in (0, SQ - 128):
+        _, t = timed(lambda: oracle.attention_head(q[a:a + 128], k, v, c, True, QP + a, 0))
+        t_rows += t
+    shard_flops = 4.0 * SQ * 131072 * D * 32 / 2
+    full_fwd = t_rows / len(rows) * SQ * 32
+    configs["shard_fwd_128k"] = {"sample": "256 query rows of one head of 32", "sample_s": round(t_rows, 2),
+                                 "full_s_extrapolated": round(full_fwd, 1),
+                                 "tflops_extrapolated": shard_flops / full_fwd / 1e12}
+    (O, L), _ = timed(lambda: oracle.attention_head(q, k, v, c, True, QP, 0))
+    _, tb = timed(lambda: oracle.attention_backward_head(q, k, v, O, do, L, c, True, QP, 0))
+    configs["shard_bwd_128k"] = {"sample": "one head of 32 in full (backward from the saved O and LSE)",
+                                 "sample_s": round(tb, 2), "full_s_extrapolated": round(32 * tb, 1),
+                                 "tflops_extrapolated": 2.5 * shard_flops / (32 * tb) / 1e12}
+    del q, k, v, do, O, L
+
+    # Split-KV decode with GQA: one (sequence, key/value head) slice: 4 query heads over 131072 keys.
+    L4 = 131072
+    qd = bf16_bits_to_f32(normal_bf16_bits(4, 0, 0, (1, 4, D))).astype(np.float64)
+    kd, vd = gen(4, 1, L4, D)[None, :, None], gen(4, 2, L4, D)[None, :, None]
+    _, t = timed(lambda: oracle.decode(qd, kd, vd, c))
+    kv_bytes = 2.0 * 16 * L4 * 8 * D * 2
+    configs["decode_gqa_128k"] = {"sample": "one (sequence, key/value head) of 16 x 8", "sample_s": round(t, 3),
+                                  "full_s_extrapolated": round(128 * t, 2),
+                                  "gbs_extrapolated": kv_bytes / (128 * t) / 1e9}
+
+    # fp32 workload in full: 4 chunk partials merged, then the backward per chunk from the merged result.
+    S1, D1 = 256, 64
+    x = [normal_f32(1, t, 0, (S1, 1, D1))[:, 0].astype(np.float64) for t in range(4)]
+    c1 = 1 / math.sqrt(D1)
+
+    def fp32_all():
+        parts = [oracle.attention_head(x[0], x[1][a:a + 64], x[2][a:a + 64], c1, False) for a in range(0, S1, 64)]
+        Om, Lm = oracle.merge(parts)
+        for a in range(0, S1, 64):
+            oracle.attention_backward_head(x[0], x[1][a:a + 64], x[2][a:a + 64], Om, x[3], Lm, c1, False)
+
+    _, t = timed(fp32_all)
+    configs["fp32_s256_4chunks"] = {"sample": "the whole workload", "s": round(t, 4)}
+
+    head = configs["causal_fwdbwd_32k"]
+    return {"value": head["tflops"], "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one (batch, head) of the causal 32K workload (S=32768, d=128), forward + backward, fp64 NumPy: "
+                      f"{head['fwd_s'] + head['bwd_s']:.1f} s for {per_head / 1e12:.3f} TFLOP (same FLOP convention); "
+                      f"the full 64 (batch, head) pairs would take {head['full_s_extrapolated']:.0f} s (linear "
+                      f"extrapolation)",
+            "host": facts, "configs": configs}
 
 
 def main():
