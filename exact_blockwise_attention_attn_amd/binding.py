@@ -168,6 +168,7 @@ EXPORTED = [
     "attn_bwd",
     "attn_bwd_chunks",
     "attn_decode_splitkv",
+    "attn_decode_splitkv_noalloc",
     "attn_decode_tree",
     "attn_decode_tree_workspace_size",
     "attn_bwd_workspace_size",
@@ -209,6 +210,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                            ("attn_bwd", [ctypes.POINTER(BwdArgs), c_vp]),
                            ("attn_bwd_chunks", [ctypes.POINTER(BwdChunksArgs), c_vp]),
                            ("attn_decode_splitkv", [ctypes.POINTER(DecodeArgs), c_vp]),
+                           ("attn_decode_splitkv_noalloc", [ctypes.POINTER(DecodeArgs), c_vp]),
                            ("attn_decode_tree", [ctypes.POINTER(DecodeTreeArgs), c_vp])):
             fn = getattr(lib, name)
             fn.argtypes = argt
@@ -544,9 +546,7 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, cu_seqlens
     _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
 
 
-def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seqlens=None, scale=0.0,
-                        stream=None) -> None:
-    """q [B,Hq,D] bf16, caches [B,L,Hkv,D] bf16 -> o [B,Hq,D] bf16, lse [B,Hq] fp32."""
+def _decode_args(q, k_cache, v_cache, o, lse, workspace, n_splits, seqlens, scale):
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
     a.batch, a.heads_q, a.head_dim = q.shape
@@ -563,4 +563,18 @@ def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seq
     a.lse = _ptr(lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, o, lse, workspace, *, n_splits, seqlens=None, scale=0.0,
+                        stream=None) -> None:
+    """q [B,Hq,D] bf16, caches [B,L,Hkv,D] bf16 -> o [B,Hq,D] bf16, lse [B,Hq] fp32."""
+    a = _decode_args(q, k_cache, v_cache, o, lse, workspace, n_splits, seqlens, scale)
     _check(load().attn_decode_splitkv(ctypes.byref(a), _stream(stream)))
+
+
+def attn_decode_splitkv_noalloc(q, k_cache, v_cache, o, lse, *, n_splits, seqlens=None, scale=0.0,
+                                stream=None) -> None:
+    """As attn_decode_splitkv, with the split partials in the library's fixed per-device scratch (no workspace)."""
+    a = _decode_args(q, k_cache, v_cache, o, lse, None, n_splits, seqlens, scale)
+    _check(load().attn_decode_splitkv_noalloc(ctypes.byref(a), _stream(stream)))

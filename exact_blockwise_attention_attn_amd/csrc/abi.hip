@@ -687,7 +687,9 @@ size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_d
   return o_bytes + ((rows * 4 + 255) & ~(size_t)255);
 }
 
-int attn_decode_splitkv(const attn_decode_args* a, void* stream) {
+// Split-KV decode with the partials in the caller's workspace, or (noalloc) in
+// the library's fixed per-device scratch.
+static int decode_splitkv(const attn_decode_args* a, void* stream, bool noalloc) {
   if (!a) return fail(ATTN_ERR_INVALID_ARG, "args is NULL");
   if (a->struct_size < sizeof(attn_decode_args))
     return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_decode_args));
@@ -703,10 +705,18 @@ int attn_decode_splitkv(const attn_decode_args* a, void* stream) {
   if (!a->lse) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
   if (a->seqlens && ((uintptr_t)a->seqlens & 3u)) return fail(ATTN_ERR_UNSUPPORTED, "seqlens is misaligned");
   const size_t need = attn_decode_workspace_size(a->batch, a->heads_q, a->head_dim, a->n_splits);
-  if (!a->workspace || a->workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                a->workspace ? a->workspace_bytes : (size_t)0);
-  if ((uintptr_t)a->workspace & 255u) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (need > attn::kNoAllocScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "attn_decode_splitkv_noalloc: the split partials need %zu bytes, more than its fixed scratch of "
+                  "%zu bytes (batch x heads_q x n_splits x (head_dim + 1) x 4 bytes, each part 256-byte aligned)",
+                  need, attn::kNoAllocScratchBytes);
+  } else {
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if ((uintptr_t)a->workspace & 255u) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   const int group = a->heads_q / a->heads_kv;
   const int64_t grid = (int64_t)a->batch * a->heads_kv * ((group + 3) / 4) * a->n_splits;
   if (grid > 0x7fffffffLL || (int64_t)a->batch * a->heads_q > 0x7fffffffLL)
@@ -734,17 +744,27 @@ int attn_decode_splitkv(const attn_decode_args* a, void* stream) {
   p.split_len = (a->cache_len + a->n_splits - 1) / a->n_splits;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const size_t rows = (size_t)a->batch * a->heads_q * a->n_splits;
-  p.part_o = (float*)a->workspace;
-  p.part_lse = (float*)((char*)a->workspace + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
   p.o = (uint16_t*)a->o;
   p.o_sb = a->o_stride[0];
   p.o_sh = a->o_stride[1];
   p.lse = a->lse;
-  TRY(check_items(attn::items_decode(p), "attn_decode_splitkv"));
+  TRY(check_items(attn::items_decode(p), noalloc ? "attn_decode_splitkv_noalloc" : "attn_decode_splitkv"));
+  // Validation is complete; the scratch lookup is the first HIP call.
+  void* ws = a->workspace;
+  if (noalloc) {
+    hipError_t e = attn::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_splitkv_noalloc scratch lookup");
+  }
+  const size_t rows = (size_t)a->batch * a->heads_q * a->n_splits;
+  p.part_o = (float*)ws;
+  p.part_lse = (float*)((char*)ws + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
   hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "attn_decode_splitkv launch");
+  if (e != hipSuccess) return hip_fail(e, noalloc ? "attn_decode_splitkv_noalloc launch" : "attn_decode_splitkv launch");
   return ok();
 }
+
+int attn_decode_splitkv(const attn_decode_args* a, void* stream) { return decode_splitkv(a, stream, false); }
+
+int attn_decode_splitkv_noalloc(const attn_decode_args* a, void* stream) { return decode_splitkv(a, stream, true); }
 
 }  // extern "C"

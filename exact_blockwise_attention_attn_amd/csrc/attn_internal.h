@@ -178,6 +178,12 @@ hipError_t launch_bwd_chunks_bf16(const BwdParams& p, const BwdChunkTable& ct, i
 hipError_t launch_bwd_f32(const BwdParams& p, int D, int run_dq, hipStream_t s);
 // Decode: split partials into the workspace, then the per-(b, h) tree merge.
 hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s);
+
+// Fixed scratch of attn_decode_splitkv_noalloc (the split partials), one per
+// device; noalloc_scratch gives its device address on the current device
+// (looked up once per device).  It allocates nothing.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+hipError_t noalloc_scratch(void** ptr);
 // Tree decode: p describes the queries (q, Hq, Hkv, group, scale), the packed
 // cache (k, v with their token and head strides), the fp32 partials (o as
 // [entries, Hq, D], lse as [entries, Hq]) and is the forward parameter block

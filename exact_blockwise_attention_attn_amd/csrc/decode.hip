@@ -22,6 +22,7 @@
 // Tree kernel: one workgroup per (batch, query head); the adjacent-pair tree
 // over the split LSEs is built level by level in LDS and fixes each split's
 // weight in the root (see decode_tree_kernel).
+#include <mutex>
 #include <type_traits>
 
 #include "attn_device.h"
@@ -301,6 +302,33 @@ __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) 
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode entry point: the split partials live
+// here instead of in a caller's workspace.  One copy per device, held until the
+// process ends.  Host code must not pass the array's name to a kernel (on the
+// host it is a stand-in, not a device address): its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int64_t items_decode(const DecodeParams& p) {
   const int64_t n_qblk = (p.group + QPW - 1) / QPW;

@@ -72,7 +72,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -407,6 +407,29 @@ typedef struct attn_decode_args {
 } attn_decode_args;
 
 ATTN_API int attn_decode_splitkv(const attn_decode_args* args, void* stream);
+
+/*
+ * attn_decode_splitkv_noalloc: attn_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, same kernels and the same
+ * results, except that `workspace` and `workspace_bytes` are ignored: the split
+ * partials go to a fixed scratch array of 32 MiB inside the library, one per
+ * device, which each device holds until the process ends.  The call makes no
+ * allocation of any kind.
+ *
+ * Limit: attn_decode_workspace_size(batch, heads_q, head_dim, n_splits) must
+ * not exceed 32 MiB (33554432 bytes), else ATTN_ERR_WORKSPACE.  For example,
+ * batch 16 x heads_q 32 x 64 splits at head_dim 128 needs 16.1 MiB.
+ *
+ * The scratch of a device is looked up on the first call with that device
+ * current (the device of `stream` must be current).  Every call on one device
+ * shares that device's scratch, which keeps whatever the last call wrote; the
+ * kernels write every partial before reading it, so nothing needs clearing.
+ * Calls that overlap on one device (different streams, or host threads without
+ * ordering between their streams) race on the scratch and may return wrong
+ * results; calls on one stream are ordered and safe.
+ */
+ATTN_API int attn_decode_splitkv_noalloc(const attn_decode_args* args, void* stream);
 
 /* Most nodes a decode tree may have (attn_decode_tree below). */
 #define ATTN_MAX_TREE_NODES 256

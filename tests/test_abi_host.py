@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -96,7 +96,7 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -493,6 +493,20 @@ def test_decode_rejects(lib, kw, code, msg):
     a = decode_args(**kw)
     assert lib.attn_decode_splitkv(ctypes.byref(a), None) == code
     assert msg in lib.attn_last_error().decode()
+
+
+def test_decode_noalloc_rejects(lib):
+    # Same validation as the workspace form; the workspace fields are ignored.
+    a = decode_args(n_splits=0, workspace=None, workspace_bytes=0)
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "n_splits" in lib.attn_last_error().decode()
+    # 16 x 32 heads x 128 splits x (128 + 1) x 4 bytes is just over the fixed 32 MiB scratch.
+    need = lib.attn_decode_workspace_size(16, 32, 128, 128)
+    assert need > 32 << 20
+    a = decode_args(batch=16, heads_q=32, heads_kv=8, n_splits=128, workspace=None, workspace_bytes=0)
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(a), None) == B.ATTN_ERR_WORKSPACE
+    msg = lib.attn_last_error().decode()
+    assert "fixed scratch of 33554432 bytes" in msg and str(need) in msg
 
 
 def test_last_error_is_thread_local(lib):
