@@ -682,7 +682,7 @@ size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q)
 
 size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits) {
   if (batch < 1 || heads_q < 1 || n_splits < 1 || n_splits > 1024 || (head_dim != 64 && head_dim != 128)) return 0;
-  const size_t rows = (size_t)batch * heads_q * n_splits;
+  const size_t rows = (size_t)batch * heads_q * (n_splits + 1);
   const size_t o_bytes = (rows * head_dim * 4 + 255) & ~(size_t)255;
   return o_bytes + ((rows * 4 + 255) & ~(size_t)255);
 }
@@ -755,7 +755,11 @@ static int decode_splitkv(const attn_decode_args* a, void* stream, bool noalloc)
     hipError_t e = attn::noalloc_scratch(&ws);
     if (e != hipSuccess) return hip_fail(e, "attn_decode_splitkv_noalloc scratch lookup");
   }
-  const size_t rows = (size_t)a->batch * a->heads_q * a->n_splits;
+  // Stream-K (equal keys per work unit) when the lengths differ and the merge
+  // tree can hold every piece of a sequence; fixed splits otherwise.
+  p.streamk = a->seqlens && a->batch <= 1024 && (int64_t)a->batch * a->n_splits <= 1024;
+  p.n_pieces = (int64_t)a->batch * (a->n_splits + 1);
+  const size_t rows = (size_t)a->batch * a->heads_q * (a->n_splits + 1);
   p.part_o = (float*)ws;
   p.part_lse = (float*)((char*)ws + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
   hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);

@@ -137,8 +137,14 @@ struct DecodeParams {
   int n_splits;
   int64_t split_len;
   float scale, scale_log2;
-  float* part_o;    // [B, Hq, n_splits, D]
-  float* part_lse;  // [B, Hq, n_splits]
+  float* part_o;    // fixed splits: [B, Hq, n_splits, D]; stream-K: [Hq, n_pieces, D]
+  float* part_lse;  // fixed splits: [B, Hq, n_splits]; stream-K: [Hq, n_pieces]
+  // Equal-key work units over sequences of different lengths (seqlens given,
+  // B <= 1024 and B * n_splits <= 1024); n_pieces = B * (n_splits + 1) rows
+  // of partials per query head, more than the U + B - 1 pieces there can be.
+  int streamk;
+  int64_t n_pieces;
+  int sk_granule;  // stream-K units per (key/value head, head slice) in one round of resident workgroups
   uint16_t* o;
   int64_t o_sb, o_sh;
   float* lse;

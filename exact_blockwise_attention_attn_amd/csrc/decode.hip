@@ -55,8 +55,13 @@ struct KvTile {
   VT v[4];          // V: keys 4 j + g, features (D / 16) l16 ..
 };
 
-template <int D>
-__global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, int n_qblk) {
+// One partial: keys [k_begin, k_begin + n_keys) of sequence b for the query
+// heads h0 .. h0 + nq - 1 (one group slice of key/value head hk), written to
+// row row(q) of the partials for query q of the slice.  Every thread of the
+// workgroup calls it with the same arguments; it ends with the partial written.
+template <int D, class Row>
+__device__ __forceinline__ void split_piece(const DecodeParams& prm, int b, int hk, int h0, int nq, int64_t k_begin,
+                                            int n_keys, Row row) {
   constexpr int NKK = D / 32;  // MFMA k-steps over the features
   constexpr int FPV = D / 16;  // V features per lane
   __shared__ __attribute__((aligned(16))) f32x4 pex[NW][KW];  // P of 4 queries per key
@@ -65,20 +70,6 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  int lin = blockIdx.x;
-  const int sp = lin % prm.n_splits;
-  lin /= prm.n_splits;
-  const int qblk = lin % n_qblk;
-  lin /= n_qblk;
-  const int hk = lin % prm.Hkv;
-  const int b = lin / prm.Hkv;
-  const int h0 = hk * prm.group + qblk * QPW;
-  const int nq = min(QPW, prm.group - qblk * QPW);
-
-  int64_t Lb = prm.L;
-  if (prm.seqlens) Lb = min<int64_t>(max<int64_t>(prm.seqlens[b], 0), prm.L);
-  const int64_t k_begin = (int64_t)sp * prm.split_len;
-  const int n_keys = (int)max<int64_t>(0, min<int64_t>(k_begin + prm.split_len, Lb) - k_begin);
   const int n_tiles = (n_keys + KW - 1) / KW;
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
 
@@ -220,10 +211,154 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
         o = fmaf(f, o_s[w][q][d], o);
       }
     }
-    const int h = h0 + q;
-    const int64_t prow = ((int64_t)b * prm.Hq + h) * prm.n_splits + sp;
+    const int64_t prow = row(q);
     prm.part_o[prow * D + d] = (tot > 0.f) ? o / tot : 0.f;
     if (d == 0) prm.part_lse[prow] = (M == neg_inf()) ? neg_inf() : fmaf(M, prm.scale, logf(tot));
+  }
+  // The next piece of the workgroup reuses the LDS buffers.
+  __syncthreads();
+}
+
+// Fixed splits: workgroup (b, hk, slice, split sp) takes keys
+// [sp * split_len, (sp + 1) * split_len) of sequence b.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, int n_qblk) {
+  int lin = blockIdx.x;
+  const int sp = lin % prm.n_splits;
+  lin /= prm.n_splits;
+  const int qblk = lin % n_qblk;
+  lin /= n_qblk;
+  const int hk = lin % prm.Hkv;
+  const int b = lin / prm.Hkv;
+  const int h0 = hk * prm.group + qblk * QPW;
+  const int nq = min(QPW, prm.group - qblk * QPW);
+  int64_t Lb = prm.L;
+  if (prm.seqlens) Lb = min<int64_t>(max<int64_t>(prm.seqlens[b], 0), prm.L);
+  const int64_t k_begin = (int64_t)sp * prm.split_len;
+  const int n_keys = (int)max<int64_t>(0, min<int64_t>(k_begin + prm.split_len, Lb) - k_begin);
+  split_piece<D>(prm, b, hk, h0, nq, k_begin, n_keys,
+                 [&](int q) { return ((int64_t)b * prm.Hq + h0 + q) * prm.n_splits + sp; });
+}
+
+// Equal-key work units (stream-K) for sequences of different lengths.  The
+// keys of all sequences, in sequence order, form one range of T keys per
+// key/value head; work unit u takes keys [u c, (u + 1) c) of it, so every unit
+// reads the same number of keys whatever the lengths and no short or empty
+// units trail the grid.  The number of units, Ue <= U = B * n_splits (the
+// grid), is made from T: about kUnitKeys keys per unit, rounded up to a whole
+// number of rounds of the workgroups the device holds at once (sk_granule units
+// per (key/value head, head slice)); c = ceil(T / Ue), and units past the last
+// exit at once.  A unit whose range crosses the end of a sequence writes one partial
+// ("piece") per sequence it touches.  Pieces are numbered in key order: a new
+// piece starts at every unit start and at every sequence start that falls
+// strictly inside a unit, so the piece holding key x is
+//   piece(x) = floor(x / c) + cnt[b(x)],
+// with b(x) the sequence of x and cnt[b] the number of sequence starts
+// pref[b'] (1 <= b' <= b, pref[b'] > pref[b' - 1]) that are not multiples of
+// c.  A sequence's pieces are then consecutive, and the tree kernel merges them
+// in key order.  There are fewer than U + B pieces, stored at row
+// h * n_pieces + piece for query head h.
+constexpr int kMaxStreamB = 1024;  // sequences a stream-K call may have
+// Keys per work unit aimed at.  On the uneven 16 x 8K.k-token benchmark cache
+// (A/B in alternating processes on one MI355X): 1536 keys 0.799 ms, 2048
+// 0.790, 3072 0.767, 4096 0.754, 6144 0.760; fixed 2048-key splits 0.857 ms.
+constexpr int64_t kUnitKeys = 4096;
+
+struct StreamK {
+  int64_t c;  // keys per work unit
+  int64_t T;  // total keys
+};
+
+__device__ __forceinline__ int64_t streamk_unit_keys(const DecodeParams& prm, int64_t T) {
+  const int64_t U = (int64_t)prm.B * prm.n_splits, g = prm.sk_granule;
+  int64_t ue = ((T + kUnitKeys - 1) / kUnitKeys + g - 1) / g * g;
+  ue = min<int64_t>(max<int64_t>(ue, 1), U);
+  return max<int64_t>(1, (T + ue - 1) / ue);
+}
+
+// Prefix sums of the clamped lengths (pref[0 .. B]) and the boundary counts
+// cnt[0 .. B - 1] in LDS.  Every thread of the workgroup calls it; it ends
+// with a barrier after which both arrays are complete.
+// With first_unit >= 0 (a split workgroup's unit), a unit past the last
+// returns before the boundary counts are made (its caller exits).
+__device__ __forceinline__ StreamK streamk_tables(const DecodeParams& prm, int64_t* pref, int* cnt,
+                                                  int64_t first_unit = -1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = prm.B;
+  if (tid < 64) {
+    int64_t carry = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int i = base + lane;
+      int64_t x = i < B ? min<int64_t>(max<int64_t>(prm.seqlens[i], 0), prm.L) : 0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (i < B) pref[i + 1] = carry + x;
+      carry += __shfl(x, 63, 64);
+    }
+    if (lane == 0) pref[0] = 0;
+  }
+  __syncthreads();
+  StreamK sk;
+  sk.T = pref[B];
+  sk.c = streamk_unit_keys(prm, sk.T);
+  if (first_unit >= 0 && first_unit * sk.c >= sk.T) return sk;  // a unit past the last: nothing to do
+  if (tid < 64) {
+    int carry = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int i = base + lane;
+      int f = 0;
+      if (i >= 1 && i < B) f = (pref[i] > pref[i - 1] && pref[i] % sk.c != 0) ? 1 : 0;
+      int x = f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (i < B) cnt[i] = carry + x;
+      carry += __shfl(x, 63, 64);
+    }
+  }
+  __syncthreads();
+  return sk;
+}
+
+// The sequence holding key x of the concatenated range (pref[b] <= x < pref[b + 1]).
+__device__ __forceinline__ int seq_of(const int64_t* pref, int B, int64_t x) {
+  int lo = 0, hi = B - 1;  // the last b with pref[b] <= x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void decode_streamk_kernel(DecodeParams prm, int n_qblk) {
+  __shared__ int64_t pref[kMaxStreamB + 1];
+  __shared__ int cnt[kMaxStreamB];
+  const int64_t U = (int64_t)prm.B * prm.n_splits;
+  int lin = blockIdx.x;
+  const int64_t u = lin % U;
+  lin /= (int)U;
+  const int qblk = lin % n_qblk;
+  const int hk = lin / n_qblk;
+  const int h0 = hk * prm.group + qblk * QPW;
+  const int nq = min(QPW, prm.group - qblk * QPW);
+  const StreamK sk = streamk_tables(prm, pref, cnt, u);
+  const int64_t s = u * sk.c, e = min(s + sk.c, sk.T);
+  if (s >= e) return;
+  int b = seq_of(pref, prm.B, s);
+  for (int64_t x = s; x < e;) {
+    while (pref[b + 1] <= x) ++b;  // skip sequences that end at x (empty ones included)
+    const int64_t seg_end = min(e, pref[b + 1]);
+    const int64_t piece = x / sk.c + cnt[b];
+    split_piece<D>(prm, b, hk, h0, nq, x - pref[b], (int)(seg_end - x),
+                   [&](int q) { return (int64_t)(h0 + q) * prm.n_pieces + piece; });
+    x = seg_end;
   }
 }
 
@@ -237,7 +372,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeParams prm, i
 // are all independent (a chain of pairwise merges in registers would wait on
 // each load in turn).  Rows whose splits are all empty get O = 0, LSE = -inf.
 constexpr int TREE_NT = 512;
-constexpr int kMaxNodes = 2 * 1024;  // nodes of all levels for up to 1024 splits
+constexpr int kMaxNodes = 2 * 1024 + 16;  // nodes of all levels for up to 1025 partials
 
 template <int D>
 __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) {
@@ -248,9 +383,20 @@ __global__ __launch_bounds__(TREE_NT) void decode_tree_kernel(DecodeParams prm) 
   __shared__ float red[NC][D];
   const int tid = threadIdx.x, d = tid % D, c = tid / D;
   const int h = blockIdx.x % prm.Hq, b = blockIdx.x / prm.Hq;
-  const int n = prm.n_splits;
-  const int64_t base = ((int64_t)b * prm.Hq + h) * n;
+  int n = prm.n_splits;
+  int64_t base = ((int64_t)b * prm.Hq + h) * n;
+  if (prm.streamk) {
+    // Sequence b's pieces: ids piece(pref[b]) .. piece(pref[b + 1] - 1), all
+    // in one run (none for an empty sequence).
+    __shared__ int64_t pref[kMaxStreamB + 1];
+    __shared__ int cnt[kMaxStreamB];
+    const StreamK sk = streamk_tables(prm, pref, cnt);
+    const int64_t lo = pref[b], hi = pref[b + 1];
+    n = hi > lo ? (int)((hi - 1) / sk.c - lo / sk.c + 1) : 0;
+    base = (int64_t)h * prm.n_pieces + (hi > lo ? lo / sk.c + cnt[b] : 0);
+  }
   for (int i = tid; i < n; i += TREE_NT) lv[i] = prm.part_lse[base + i];
+  if (n == 0 && tid == 0) lv[0] = neg_inf();  // a sequence with no keys: O = 0, LSE = -inf
   __syncthreads();
   int off = 0, m = n;  // this level's nodes are lv[off .. off + m)
   while (m > 1) {
@@ -312,6 +458,23 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cus[kMaxDevices];
+hipError_t g_cu_err[kMaxDevices];
+
+// Compute units of the current device (queried once per device).
+hipError_t device_cus(int* cus) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_cu_once[dev], [dev] {
+    g_cu_err[dev] = hipDeviceGetAttribute(&g_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+  });
+  *cus = g_cus[dev];
+  return g_cu_err[dev];
+}
+
 std::once_flag g_scratch_once[kMaxDevices];
 void* g_scratch_ptr[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
@@ -335,14 +498,30 @@ int64_t items_decode(const DecodeParams& p) {
   return std::max((int64_t)p.B * p.Hkv * n_qblk * p.n_splits * NT, (int64_t)p.B * p.Hq * TREE_NT);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& p0, int D, hipStream_t s) {
+  DecodeParams p = p0;
   const int n_qblk = (p.group + QPW - 1) / QPW;
-  const int64_t grid = (int64_t)p.B * p.Hkv * n_qblk * p.n_splits;
+  if (p.streamk) {
+    // Stream-K units per (key/value head, head slice) in one round of the
+    // workgroups resident at once (two per CU).
+    int cus = 0;
+    hipError_t e = device_cus(&cus);
+    if (e != hipSuccess) return e;
+    p.sk_granule = max(1, 2 * cus / max(1, p.Hkv * n_qblk));
+  }
+  const int64_t grid = (int64_t)p.B * p.Hkv * n_qblk * p.n_splits;  // the same count in both modes
   if (grid == 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL(decode_split_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
+  if (p.streamk) {
+    if (D == 128)
+      hipLaunchKernelGGL(decode_streamk_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
+    else
+      hipLaunchKernelGGL(decode_streamk_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL(decode_split_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
+    else
+      hipLaunchKernelGGL(decode_split_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, n_qblk);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 tg((unsigned)((int64_t)p.B * p.Hq));

@@ -72,7 +72,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -376,12 +376,22 @@ ATTN_API int attn_bwd_chunks(const attn_bwd_chunks_args* args, void* stream);
  * key/value head h / (heads_q / heads_kv).  The query attends every cached key
  * 0 .. len_b - 1 with len_b = seqlens[b] (device int32 [batch], each in
  * [0, cache_len]) or cache_len when seqlens is NULL; no causal mask applies.
- * The keys are cut into n_splits contiguous splits of ceil(cache_len / n_splits)
- * keys; each split yields a partial (O, LSE) in the workspace and the partials of
- * each (b, h) are reduced by a binary tree of adjacent pairs (an odd node is
- * carried up a level): the tree is built over the split LSEs, and O is the sum
- * of the split partials weighted by their weights in the tree's root, which is
- * the tree's result up to the order of the additions.
+ * Without seqlens, the keys are cut into n_splits contiguous splits of
+ * ceil(cache_len / n_splits) keys; each split yields a partial (O, LSE) in the
+ * workspace and the partials of each (b, h) are reduced by a binary tree of
+ * adjacent pairs (an odd node is carried up a level): the tree is built over the
+ * split LSEs, and O is the sum of the split partials weighted by their weights
+ * in the tree's root, which is the tree's result up to the order of the
+ * additions.
+ * With seqlens (sequences of different lengths) and batch * n_splits <= 1024,
+ * the work is cut into equal-key units instead (stream-K, as in the Lean
+ * Attention abstract): the keys of all sequences in order form one range per
+ * key/value head, cut into units of the same length (about 4096 keys, the
+ * number of units rounded to whole rounds of the workgroups the device holds,
+ * at most batch * n_splits).  A unit that crosses the end of a sequence yields
+ * one partial per sequence it touches, and each (b, h) reduces its partials, in
+ * key order, by the same adjacent-pair tree.  Larger batch * n_splits keep the
+ * fixed splits.  Either way the result is the exact attention up to rounding.
  * Writes o [batch, heads_q, head_dim] bf16 (strides o_stride = {batch, head}) and
  * lse [batch, heads_q] fp32.  The workspace (device memory of at least
  * attn_decode_workspace_size(...) bytes, 256-byte aligned) is overwritten.
@@ -491,7 +501,8 @@ ATTN_API size_t attn_decode_tree_workspace_size(const attn_decode_tree_args* arg
 /* Bytes of workspace attn_bwd needs for these sizes (0 on invalid sizes). */
 ATTN_API size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q);
 
-/* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes). */
+/* Bytes of workspace attn_decode_splitkv needs for these sizes (0 on invalid sizes):
+ * batch * heads_q * (n_splits + 1) partial rows of head_dim + 1 floats. */
 ATTN_API size_t attn_decode_workspace_size(int32_t batch, int32_t heads_q, int32_t head_dim, int32_t n_splits);
 
 /* Static description of a status code. */

@@ -96,12 +96,13 @@ int main(void) {
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 7
+    assert lib.attn_abi_version() == 8
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
     # O partials [16, 32, 64, 128] fp32 + LSE [16, 32, 64] fp32, each rounded up to 256 bytes.
-    assert lib.attn_decode_workspace_size(16, 32, 128, 64) == 16 * 32 * 64 * 128 * 4 + 16 * 32 * 64 * 4
+    # batch x heads_q x (n_splits + 1) rows of head_dim + 1 floats (the stream-K pieces fit in the extra row).
+    assert lib.attn_decode_workspace_size(16, 32, 128, 64) == 16 * 32 * 65 * 128 * 4 + 16 * 32 * 65 * 4
     assert lib.attn_decode_workspace_size(1, 1, 96, 4) == 0
     assert lib.attn_decode_workspace_size(1, 1, 128, 0) == 0
     # Backward statistics: 2 floats per row, rows padded to 64, total rounded to 256 bytes.

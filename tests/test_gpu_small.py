@@ -546,6 +546,18 @@ DECODE_CASES = [
     (1, 4, 1, 37, 64, 100, None),
     (2, 4, 2, 999, 128, 1000, None),
     (1, 8, 2, 700, 128, 5, [700]),
+    # Uneven lengths run as equal-key work units (stream-K) when B * n_splits <= 1024:
+    # units that span many short sequences and empty ones, every sequence empty,
+    # lengths past the cache (clamped to it), the largest unit count with one long
+    # sequence (about 1000 pieces in one merge tree) next to a one-key one, and
+    # 64 sequences of random lengths.
+    (8, 8, 2, 3000, 128, 4, [5, 0, 3000, 17, 1, 2999, 64, 0]),
+    (5, 4, 1, 1000, 64, 2, [0, 0, 0, 0, 0]),
+    (3, 8, 2, 500, 128, 16, [600, 0, 499]),
+    (2, 8, 2, 4096, 128, 512, [4096, 1]),
+    (1, 8, 2, 10000, 128, 1024, [10000]),
+    (64, 4, 4, 256, 128, 16, [int(x) for x in np.random.default_rng(3).integers(0, 257, 64)]),
+    (16, 32, 8, 2048, 64, 64, [128 * k for k in (5, 12, 1, 16, 9, 3, 14, 7, 11, 2, 15, 6, 10, 4, 13, 8)]),
 ]
 
 
@@ -558,7 +570,8 @@ def test_decode(case):
     vc, vh = seq_tensor(108, 2, Bn, L, Hkv, D, "bf16")
     q, qh = q[:, 0], qh[:, 0]
     scale = 1 / math.sqrt(D)
-    O_ref, L_ref = oracle.decode(qh, kh, vh, scale, seqlens=lens)
+    # Lengths are clamped to [0, L] by the library; the oracle takes the clamped ones.
+    O_ref, L_ref = oracle.decode(qh, kh, vh, scale, seqlens=None if lens is None else [min(x, L) for x in lens])
     o = torch.empty((Bn, Hq, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((Bn, Hq), dtype=torch.float32, device="cuda")
     ws = torch.empty(B.attn_decode_workspace_size(Bn, Hq, D, ns), dtype=torch.uint8, device="cuda")
