@@ -82,7 +82,7 @@ struct BwdParams {
   const int* cu_k;
   // Per-row statistics workspace: for each (b, h), Sq_pad floats of LSE*log2(e)
   // (+inf on rows that see no key and on padding rows) followed by Sq_pad
-  // floats of delta (0 on padding rows).  Sq_pad = Sq rounded up to 64.
+  // floats of -delta (0 on padding rows).  Sq_pad = Sq rounded up to 64.
   float* stats;
   int Sq_pad;
   float* dq_acc;  // contiguous [B, Sq, Hq, D]

@@ -172,9 +172,22 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
       const int slot = t % 3;
       f32x16 sc[2] = {f32x16{}, f32x16{}};
       if (t < n_qt) {
-        // S = Q K^T (P wavefront) or dP = dO V^T (dS wavefront): lane = key,
+        // S = Q K^T (P wavefront) or dP - delta = dO V^T - delta (dS
+        // wavefront, accumulating onto the stored -delta): lane = key,
         // registers = two 32-query blocks.
         const u16* rows = (PW ? q_s : d_s) + slot * SZ;
+        if constexpr (!PW) {
+          const float* nd = st_s[slot] + KBM;
+#pragma unroll
+          for (int qb2 = 0; qb2 < 2; ++qb2) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x4 n4 = *(const f32x4*)(nd + qb2 * 32 + g4 * 8 + lg * 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sc[qb2][g4 * 4 + e] = n4[e];
+            }
+          }
+        }
         __builtin_amdgcn_s_setprio(1);
         {
           // Operand j = 2 si + qb2, read AH ahead of the MFMA that uses it;
@@ -251,22 +264,18 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
       }
       if constexpr (!PW) {
         if (t > t_start) {
-          // dS for tile t - 1 from the published P and last step's dP, then
-          // dK^T += Q^T dS.
+          // dS for tile t - 1 from the published P and last step's dP - delta,
+          // then dK^T += Q^T dS.
           const int tp = t - 1, sp = tp % 3;
-          const float* st = st_s[sp];
           const u16* qsrc = q_s + sp * SZ;
           bf16x8 sbs[4];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
             const int qb2 = ks >> 1, o = (ks & 1) * 8;
-            // Slab ks holds queries 16*ks + 8*(e/4) + 4*lg + e%4: two groups of 4 consecutive deltas.
-            const f32x4 d0 = *(const f32x4*)(st + KBM + ks * 16 + lg * 4);
-            const f32x4 d1 = *(const f32x4*)(st + KBM + ks * 16 + 8 + lg * 4);
             float ds[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * (dp_in[qb2][o + e] - (e < 4 ? d0[e] : d1[e - 4]));
+            for (int e = 0; e < 8; ++e) ds[e] = (float)pb[e] * dp_in[qb2][o + e];
             sbs[ks] = cvt_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
           }
           __builtin_amdgcn_s_setprio(1);
@@ -460,9 +469,10 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
     }
   }
   // Statistics rows exist up to Sq_pad >= Sq; rows past Sq hold LSE = +inf, delta = 0.
+  // The workspace holds -delta.
   const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
   const float lse2 = qi < p.Sq_pad ? stb[qi] : pos_inf();
-  const float dlt = qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f;
+  const float ndlt = qi < p.Sq_pad ? stb[p.Sq_pad + qi] : 0.f;
   const float sl2 = p.scale_log2;
   RowFrag<D> rf;
   TrFrag<D> tf;
@@ -558,7 +568,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, int b, int h, int un
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] - dlt);
+      for (int i = 0; i < 16; ++i) sc[i] = sc[i] * (dp[i] + ndlt);
       const bf16x8 sb[2] = {slab8(sc, 0), slab8(sc, 8)};
       __builtin_amdgcn_s_setprio(1);
       {

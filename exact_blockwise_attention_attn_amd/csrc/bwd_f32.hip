@@ -13,10 +13,12 @@ namespace attn {
 namespace {
 
 // ---------------------------------------------------------------- prepare --
-// Fills the statistics workspace: for row i of (b, h), delta_i = sum_t dO_it O_it
-// and LSE_i * log2(e) (+inf when LSE_i = -inf, i.e. the row sees no key), plus
-// padding rows up to a multiple of 64 (LSE +inf, delta 0) so that the kernels
-// can fetch whole 64-row tiles of statistics.
+// Fills the statistics workspace: for row i of (b, h), LSE_i * log2(e) (+inf
+// when LSE_i = -inf, i.e. the row sees no key) and -delta_i with delta_i =
+// sum_t dO_it O_it, plus padding rows up to a multiple of 64 (LSE +inf, delta 0)
+// so that the kernels can fetch whole 64-row tiles of statistics.  The negated
+// delta lets the bf16 dK/dV kernel start its dP accumulator at -delta, so the
+// matrix cores form dP - delta.
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(BwdParams p) {
       l2 = (lse == neg_inf()) ? pos_inf() : lse * kLog2e;
     }
     base[i] = l2;
-    base[p.Sq_pad + i] = (i < sq) ? acc : 0.f;
+    base[p.Sq_pad + i] = (i < sq) ? -acc : 0.f;
   }
 }
 
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(QNT) void dq_f32_kernel(BwdParams p) {
     dq[f] = 0.f;
   }
   const float lse = qok ? p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss] : neg_inf();
-  const float dlt = qok ? p.stats[((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad + qi] : 0.f;
+  const float dlt = qok ? -p.stats[((int64_t)b * p.Hq + h) * 2 * p.Sq_pad + p.Sq_pad + qi] : 0.f;
   const bool live = lse != neg_inf();
   const int q_last = min(qt * FROWS + FROWS, p.Sq) - 1;
   int kv_end = p.Sk;
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(KNT) void dkdv_f32_kernel(BwdParams p) {
       if (lt < KTK) {
         const int i = i0 + lt;
         ls[g][lt] = (i < p.Sq) ? lseb[(int64_t)i * p.lse_ss] : neg_inf();
-        ds_[g][lt] = (i < p.Sq) ? dltb[i] : 0.f;
+        ds_[g][lt] = (i < p.Sq) ? -dltb[i] : 0.f;
       }
       __syncthreads();
 #pragma unroll 2

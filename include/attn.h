@@ -251,7 +251,7 @@ ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
  * The workspace (device memory of at least attn_bwd_workspace_size(...) bytes,
  * 256-byte aligned) holds the per-row statistics: for each (b, h) in row-major
  * order, Sq_pad = round_up(seqlen_q, 64) floats of LSE * log2(e) (+inf for rows
- * with LSE = -inf and for padding rows) followed by Sq_pad floats of delta (0 on
+ * with LSE = -inf and for padding rows) followed by Sq_pad floats of -delta (0 on
  * padding rows; in a packed variable-length batch b is the sequence, and rows
  * past its length are padding).  ATTN_BWD_COMPUTE_DELTA fills it; later calls for other key
  * chunks of the same o, dout and lse may reuse it without the flag.  A row with

@@ -269,10 +269,10 @@ def test_bwd(case):
     check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
     check("dK", dk, dk_ref, G_TOL, scale_by_max=True)
     check("dV", dv, dv_ref, G_TOL, scale_by_max=True)
-    # Workspace layout: per (b, h), Sq_pad rows of LSE*log2(e) then Sq_pad rows of delta.
+    # Workspace layout: per (b, h), Sq_pad rows of LSE*log2(e) then Sq_pad rows of -delta.
     sq_pad = (Sq + 63) // 64 * 64
     st = ws[: Bn * Hq * 2 * sq_pad].view(Bn, Hq, 2, sq_pad).cpu().double().numpy()
-    check("delta", st[:, :, 1, :Sq], np.einsum("bshd,bshd->bhs", doh, O_ref), G_TOL, scale_by_max=True)
+    check("-delta", st[:, :, 1, :Sq], -np.einsum("bshd,bshd->bhs", doh, O_ref), G_TOL, scale_by_max=True)
     l2_ref = np.where(np.isneginf(L_ref), np.inf, L_ref * math.log2(math.e))
     check("lse*log2e", st[:, :, 0, :Sq], l2_ref, L_TOL * math.log2(math.e))
     assert np.all(st[:, :, 0, Sq:] == np.inf) and np.all(st[:, :, 1, Sq:] == 0)
