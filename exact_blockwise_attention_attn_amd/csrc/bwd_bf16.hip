@@ -101,9 +101,13 @@ constexpr int DKV_NT = 512;
 
 template <int D, bool PW>
 __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s, float (*st_s)[256],
-                                          u32x4 (*pex)[2][4][64], const RowFrag<D>& rf, const TrFrag<D>& tf,
+                                          u32x4 (*pex)[2][4][64], RowFrag<D>& rf, TrFrag<D>& tf,
                                           int wave, int lane, int kt, int b, int hk) {
   constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
+  // Per-lane values of a tile are derived here from an opaque copy of the
+  // lane index, so they are not computed once for both tiles of a unit and
+  // kept live across the first.
+  asm volatile("" : "+v"(lane));
   const int lg = lane >> 5, pair = wave & 3;
   const int j0 = kt * KBN;
   const int kj = j0 + pair * 32 + (lane & 31);  // this lane's key
@@ -148,11 +152,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
     const u16* qb = (const u16*)p.q.ptr + (int64_t)b * p.q.sb + (int64_t)h * p.q.sh;
     const u16* dob = (const u16*)p.dout.ptr + (int64_t)b * p.dout.sb + (int64_t)h * p.dout.sh;
     const float* stb = p.stats + ((int64_t)b * p.Hq + h) * 2 * p.Sq_pad;
-    // Fetch query tile tq into slot tq % 3: Q and dO rows, and (wave 0) the 64
-    // statistics of each kind in one 1 KB run.  The loads are untracked by the
-    // compiler and waited for before the barrier that publishes the slot.
-    auto issue = [&](int tq) {
-      const int slot = tq % 3;
+    // Step t works on ring slot (t - t_start) % 3 and exchange buffer
+    // (t - t_start) % 2.  Fetch query tile tq into ring slot `slot`: Q and dO
+    // rows, and (wave 0) the 64 statistics of each kind in one 1 KB run.  The
+    // loads are untracked by the compiler and waited for before the barrier
+    // that publishes the slot.
+    auto issue = [&](int tq, int slot) {
       if (wave == 0) {
         const int part = (lane >> 4) & 1;  // lanes 0-15 LSE, 16-31 delta; 32-63 repeat them
         dma16_untracked(stb + part * p.Sq_pad + tq * KBM + 4 * (lane & 15), (lds_void*)st_s[slot]);
@@ -161,21 +166,29 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
       issue_swtile<D, 8, true>(d_s + slot * SZ, dob, p.dout.ss, tq * KBM, p.Sq, wave, lane);
     };
     if (t_start >= n_qt) continue;
-    issue(t_start);
+    issue(t_start, 0);
     wait_vm<0>();
     lds_barrier();
     f32x16 dpa[2] = {f32x16{}, f32x16{}}, dpb[2] = {f32x16{}, f32x16{}};
-    auto step = [&](int t, f32x16* dp_in, f32x16* dp_out, auto masked_c) {
+    // slot_c: the ring slot, an int or a compile-time constant (which folds
+    // into the LDS reads' immediate offsets); par_c: the exchange buffer and
+    // the dP registers' roles, always a compile-time constant.
+    auto step = [&](int t, auto slot_c, auto par_c, auto masked_c) {
+      const int slot = slot_c;
+      constexpr int par = decltype(par_c)::value;
+      rf.refresh();
+      tf.refresh();
+      f32x16* const dp_in = par ? dpb : dpa;   // dP - delta of tile t - 1
+      f32x16* const dp_out = par ? dpa : dpb;  // dP - delta of tile t
       // Tile t + 1 takes the slot of tile t - 2, last read (by the dS
       // wavefront) before the previous barrier.
-      if (t + 1 < n_qt) issue(t + 1);
-      const int slot = t % 3;
+      if (t + 1 < n_qt) issue(t + 1, slot == 2 ? 0 : slot + 1);
       f32x16 sc[2] = {f32x16{}, f32x16{}};
       if (t < n_qt) {
         // S = Q K^T (P wavefront) or dP - delta = dO V^T - delta (dS
         // wavefront, accumulating onto the stored -delta): lane = key,
         // registers = two 32-query blocks.
-        const u16* rows = (PW ? q_s : d_s) + slot * SZ;
+        const int tile_o = slot * SZ * 2;  // byte offset of the slot in either ring
         if constexpr (!PW) {
           const float* nd = st_s[slot] + KBM;
 #pragma unroll
@@ -195,11 +208,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
           constexpr int NJ = 2 * NS, AH = KV_AHEAD;
           bf16x8 f[NJ];
 #pragma unroll
-          for (int j = 0; j < AH; ++j) f[j] = rf.get(rows, j & 1, j >> 1);
+          for (int j = 0; j < AH; ++j) f[j] = rf.get_at(tile_o, j & 1, j >> 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
-            if (j + AH < NJ) f[j + AH] = rf.get(rows, (j + AH) & 1, (j + AH) >> 1);
+            if (j + AH < NJ) f[j + AH] = rf.get_at(tile_o, (j + AH) & 1, (j + AH) >> 1);
             sc[j & 1] = mfma32(f[j], kv[j >> 1], sc[j & 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -225,7 +238,8 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
             // Causal mask: query i0 + q is hidden from this lane's key when
             // q < key_lim - i0.  The sign of q - (key_lim - i0) selects it as a
             // bit mask, which keeps the 32 decisions in vector registers.
-            const int rel = (int)max<int64_t>(-1, min<int64_t>(key_lim - i0, KBM));
+            const int64_t rel64 = key_lim - i0;
+            const int rel = rel64 < -1 ? -1 : (rel64 > KBM ? KBM : (int)rel64);
 #pragma unroll
             for (int qb2 = 0; qb2 < 2; ++qb2) {
 #pragma unroll
@@ -238,23 +252,22 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
           }
           // P in bf16, one B operand per 16-query slab: published for the
           // partner and used right away for dV^T += dO^T P.
-          const u16* dsrc = d_s + slot * SZ;
           bf16x8 pb[4];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             pb[ks] = slab8(sc[ks >> 1], (ks & 1) * 8);
-            pex[pair][t & 1][ks][lane] = __builtin_bit_cast(u32x4, pb[ks]);
+            pex[pair][par][ks][lane] = __builtin_bit_cast(u32x4, pb[ks]);
           }
           __builtin_amdgcn_s_setprio(1);
           {
             constexpr int NJ = 4 * NDB, AH = KV_AHEAD_T;
             bf16x8 f[NJ];
 #pragma unroll
-            for (int j = 0; j < AH; ++j) f[j] = tf.get(dsrc, j / NDB, j % NDB);
+            for (int j = 0; j < AH; ++j) f[j] = tf.get_at(tile_o, j / NDB, j % NDB);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-              if (j + AH < NJ) f[j + AH] = tf.get(dsrc, (j + AH) / NDB, (j + AH) % NDB);
+              if (j + AH < NJ) f[j + AH] = tf.get_at(tile_o, (j + AH) / NDB, (j + AH) % NDB);
               acc[j % NDB] = mfma32(f[j], pb[j / NDB], acc[j % NDB]);
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -266,12 +279,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
         if (t > t_start) {
           // dS for tile t - 1 from the published P and last step's dP - delta,
           // then dK^T += Q^T dS.
-          const int tp = t - 1, sp = tp % 3;
-          const u16* qsrc = q_s + sp * SZ;
+          const int sp = slot == 0 ? 2 : slot - 1;
+          const int prev_o = sp * SZ * 2;
           bf16x8 sbs[4];
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][tp & 1][ks][lane]);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pex[pair][par ^ 1][ks][lane]);
             const int qb2 = ks >> 1, o = (ks & 1) * 8;
             float ds[8];
 #pragma unroll
@@ -283,11 +296,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
             constexpr int NJ = 4 * NDB, AH = KV_AHEAD_T;
             bf16x8 f[NJ];
 #pragma unroll
-            for (int j = 0; j < AH; ++j) f[j] = tf.get(qsrc, j / NDB, j % NDB);
+            for (int j = 0; j < AH; ++j) f[j] = tf.get_at(prev_o, j / NDB, j % NDB);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-              if (j + AH < NJ) f[j + AH] = tf.get(qsrc, (j + AH) / NDB, (j + AH) % NDB);
+              if (j + AH < NJ) f[j + AH] = tf.get_at(prev_o, (j + AH) / NDB, (j + AH) % NDB);
               acc[j % NDB] = mfma32(f[j], sbs[j / NDB], acc[j % NDB]);
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -298,16 +311,33 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, u16* q_s, u16* d_s
       wait_vm<0>();  // tile t + 1, the only load in flight, is needed next step
       lds_barrier();
     };
-    // Steps go in pairs so that dpa and dpb keep their roles; the masked
-    // pairs come first (masking a tile that needs none keeps every entry).
+    // The masked steps come first, in pairs (runtime ring slot), and run on
+    // until the step count is a multiple of six (masking a tile that needs
+    // none keeps every entry).  The unmasked steps then run six at a time,
+    // so every ring slot and exchange buffer is a compile-time constant.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
     int t = t_start;
-    for (; t <= n_qt && t < t_mask; t += 2) {
-      step(t, dpa, dpb, std::true_type{});
-      if (t + 1 <= n_qt) step(t + 1, dpb, dpa, std::true_type{});
+    for (; t <= n_qt && (t < t_mask || (t - t_start) % 6 != 0); t += 2) {
+      const int s0 = (t - t_start) % 3;
+      step(t, s0, P0{}, std::true_type{});
+      if (t + 1 <= n_qt) step(t + 1, s0 == 2 ? 0 : s0 + 1, P1{}, std::true_type{});
     }
-    for (; t <= n_qt; t += 2) {
-      step(t, dpa, dpb, std::false_type{});
-      if (t + 1 <= n_qt) step(t + 1, dpb, dpa, std::false_type{});
+    for (; t <= n_qt; t += 6) {
+      step(t, S0{}, P0{}, std::false_type{});
+      if (t + 1 > n_qt) break;
+      step(t + 1, S1{}, P1{}, std::false_type{});
+      if (t + 2 > n_qt) break;
+      step(t + 2, S2{}, P0{}, std::false_type{});
+      if (t + 3 > n_qt) break;
+      step(t + 3, S0{}, P1{}, std::false_type{});
+      if (t + 4 > n_qt) break;
+      step(t + 4, S1{}, P0{}, std::false_type{});
+      if (t + 5 > n_qt) break;
+      step(t + 5, S2{}, P1{}, std::false_type{});
     }
   }
 
@@ -344,6 +374,10 @@ __device__ __forceinline__ void dkdv_unit(const BwdParams& p, u16* q_s, u16* d_s
   TrFrag<D> tf;
   rf.init(lane);
   tf.init(lane);
+  // The P wavefront reads Q rows and dO transposed, the dS wavefront dO rows
+  // and Q transposed.
+  rf.rebase(PW ? q_s : d_s);
+  tf.rebase(PW ? d_s : q_s);
   const int last = p.n_ktiles - 1 - unit;
   const int n = (p.balanced && last != unit) ? 2 : 1;
   for (int k = 0; k < n; ++k) dkdv_tile<D, PW>(p, q_s, d_s, st_s, pex, rf, tf, wave, lane, k == 0 ? unit : last, b, hk);
@@ -353,7 +387,7 @@ template <int D>
 __global__ __launch_bounds__(DKV_NT) void dkdv_bf16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) u16 q_s[3 * SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 d_s[3 * SwTile<D>::SIZE];
-  // [slot] [0, 64): LSE in log2 units, [64, 128): delta, [128, 256): unused
+  // [slot] [0, 64): LSE in log2 units, [64, 128): -delta, [128, 256): unused
   __shared__ __attribute__((aligned(16))) float st_s[3][256];
   __shared__ __attribute__((aligned(16))) u32x4 pex_s[4][2][4][64];  // [pair][step parity][slab][lane]
   // The wavefront index is uniform across the wavefront; say so, so that the

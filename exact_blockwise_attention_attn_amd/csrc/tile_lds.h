@@ -21,6 +21,12 @@ namespace attn {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
 typedef void __attribute__((address_space(3))) lds_void;
+typedef u32x4 __attribute__((address_space(3))) lds_u32x4;
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const lds_void*)p;
+}
 
 template <int D>
 struct SwTile {
@@ -148,19 +154,40 @@ struct TileSrc {
   }
 };
 
-// Per-lane offsets of the row-read operand fragments: row (32*blk + lane%32),
+// Per-lane byte offsets of the row-read operand fragments: row (32*blk + lane%32),
 // logical chunk 2*s + lane/32, for s = 0 .. D/16-1.  The block of 32 rows adds
-// 32*D elements (an immediate), since the swizzle repeats every 16 rows.
+// 64*D bytes (an immediate), since the swizzle repeats every 16 rows.  Byte
+// offsets let a tile base that is a compile-time constant fold into the LDS
+// read's immediate offset with no vector instruction.
 template <int D>
 struct RowFrag {
   int off[D / 16];
   __device__ __forceinline__ void init(int lane) {
     const int lr = lane & 31, lg = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) off[s] = sw_off<D>(lr, (2 * s + lg) * 8);
+    for (int s = 0; s < D / 16; ++s) off[s] = 2 * sw_off<D>(lr, (2 * s + lg) * 8);
   }
   __device__ __forceinline__ bf16x8 get(const u16* t, int blk, int s) const {
-    return as_bf16x8(*(const u32x4*)(t + blk * 32 * D + off[s]));
+    return as_bf16x8(*(const u32x4*)((const char*)t + blk * 64 * D + off[s]));
+  }
+  // Based form: rebase(t) adds the LDS address of tensor t to the offsets
+  // once; get_at(o, ...) then reads the tile o bytes past t.  A constant o
+  // below 64 KB becomes the LDS read's immediate offset even where the
+  // tensor itself sits above the 64 KB an immediate can reach.
+  __device__ __forceinline__ void rebase(const u16* t) {
+    const unsigned a = lds_addr(t);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) off[s] += (int)a;
+  }
+  __device__ __forceinline__ bf16x8 get_at(int o, int blk, int s) const {
+    return as_bf16x8(*(const lds_u32x4*)(uintptr_t)(unsigned)(o + blk * 64 * D + off[s]));
+  }
+  // Make the offsets opaque to the compiler at this point (no instruction):
+  // addresses derived from them after it cannot be hoisted above it, where each
+  // (tile base, fragment) pair would otherwise hold a register of its own.
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(off[s]));
   }
 };
 
@@ -169,22 +196,43 @@ struct RowFrag {
 // slab + 8h + 4*(q/2) + s/4 at feature 32*db + 16*(q%2) + 4*(s%4); the
 // transposing read hands lane (32*(q/2) + 16*(q%2) + s) feature 32*db + 16*(q%2) + s
 // of rows slab + 8h + 4*(q/2) + {0..3}: the k-slot order of an operand that
-// comes straight out of an MFMA accumulator.  Slabs add 16*D (an immediate).
+// comes straight out of an MFMA accumulator.  Slabs add 32*D bytes (an immediate).
 template <int D>
 struct TrFrag {
-  int off[2][D / 32];
+  int off[2][D / 32];  // bytes
   __device__ __forceinline__ void init(int lane) {
     const int q16 = lane >> 4, s16 = lane & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-        off[h][db] = sw_off<D>(8 * h + 4 * (q16 >> 1) + (s16 >> 2), db * 32 + 16 * (q16 & 1) + 4 * (s16 & 3));
+        off[h][db] = 2 * sw_off<D>(8 * h + 4 * (q16 >> 1) + (s16 >> 2), db * 32 + 16 * (q16 & 1) + 4 * (s16 & 3));
   }
   __device__ __forceinline__ bf16x8 get(const u16* t, int slab, int db) const {
-    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + slab * 16 * D + off[0][db]));
-    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + slab * 16 * D + off[1][db]));
+    const char* tb = (const char*)t + slab * 32 * D;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + off[0][db]));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tb + off[1][db]));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // Based form, as in RowFrag.
+  __device__ __forceinline__ void rebase(const u16* t) {
+    const unsigned a = lds_addr(t);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) off[h][db] += (int)a;
+  }
+  __device__ __forceinline__ bf16x8 get_at(int o, int slab, int db) const {
+    const int tb = o + slab * 32 * D;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(unsigned)(tb + off[0][db]));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(unsigned)(tb + off[1][db]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(off[h][db]));
   }
 };
 
