@@ -40,9 +40,9 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # HBM bytes per backward call of the causal 32K workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # runs of its kernels (statistics + dK/dV + dQ), FETCH_SIZE scaled by 2 and WRITE_SIZE by 1 as a plain 1 GiB
-# copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md): 13.87 GB read + 2.79 GB written.  Set to
+# copy calibrates them (profiles/causal_fwdbwd_32k_hbm_traffic.md): 14.20 GB read + 2.79 GB written.  Set to
 # None whenever these kernels change, until they are measured again.
-BWD_CALL_HBM_BYTES = 16655852544
+BWD_CALL_HBM_BYTES = 16987541152
 HBM_PEAK_GBS = 8000.0
 
 
