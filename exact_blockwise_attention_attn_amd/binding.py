@@ -40,6 +40,7 @@ ATTN_BWD_COMPUTE_DELTA = 1 << 0
 ATTN_BWD_DQ_OVERWRITE = 1 << 1
 ATTN_BWD_FINALIZE_DQ = 1 << 2
 ATTN_BWD_BALANCED = 1 << 3
+ATTN_BWD_DETERMINISTIC = 1 << 4
 
 
 class FwdArgs(ctypes.Structure):
@@ -402,7 +403,7 @@ def attn_merge_lse(o_parts, lse_parts, o_out, lse_out, *, tree=False, stream=Non
 
 def attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, *, dq=None, q_pos0=0, k_pos0=0, causal=False,
              scale=0.0, compute_delta=False, dq_overwrite=False, finalize_dq=False, balanced=False,
-             stream=None) -> None:
+             deterministic=False, stream=None) -> None:
     """Backward for one key chunk; see include/attn.h for the contract."""
     a = BwdArgs()
     a.struct_size = ctypes.sizeof(BwdArgs)
@@ -424,7 +425,8 @@ def attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, *, dq=None, q_pos
     a.causal = int(bool(causal))
     a.scale = float(scale)
     a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
-               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0)
+               | (ATTN_BWD_DETERMINISTIC if deterministic else 0))
     _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
 
 
@@ -441,7 +443,8 @@ def _chunk_strides(ts, what):
 
 def attn_bwd_chunks(q, k_chunks, v_chunks, o, dout, lse, workspace, dq_acc, dk_chunks, dv_chunks, *,
                     chunk_pos0, dq=None, q_pos0=0, causal=False, scale=0.0, compute_delta=False,
-                    dq_overwrite=False, finalize_dq=False, balanced=False, stream=None) -> None:
+                    dq_overwrite=False, finalize_dq=False, balanced=False, deterministic=False,
+                    stream=None) -> None:
     """Backward of q over a list of key/value chunks ([B, len_c, Hkv, D] bf16 each), dK/dV per chunk; see include/attn.h."""
     n = len(k_chunks)
     assert len(v_chunks) == n and len(dk_chunks) == n and len(dv_chunks) == n and len(chunk_pos0) == n
@@ -472,7 +475,8 @@ def attn_bwd_chunks(q, k_chunks, v_chunks, o, dout, lse, workspace, dq_acc, dk_c
     a.causal = int(bool(causal))
     a.scale = float(scale)
     a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
-               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0)
+               | (ATTN_BWD_DETERMINISTIC if deterministic else 0))
     _check(load().attn_bwd_chunks(ctypes.byref(a), _stream(stream)))
 
 
@@ -516,7 +520,7 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, m
 
 def attn_bwd_varlen(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                     max_seqlen_k, *, dq=None, causal=False, scale=0.0, compute_delta=False, dq_overwrite=False,
-                    finalize_dq=False, balanced=False, stream=None) -> None:
+                    finalize_dq=False, balanced=False, deterministic=False, stream=None) -> None:
     """Packed variable-length batch backward; layouts as attn_fwd_varlen, dq_acc fp32 [total_q, Hq, D]."""
     _check_offsets(cu_seqlens_q, "cu_seqlens_q")
     _check_offsets(cu_seqlens_k, "cu_seqlens_k")
@@ -541,7 +545,8 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, cu_seqlens
     a.causal = int(bool(causal))
     a.scale = float(scale)
     a.flags = ((ATTN_BWD_COMPUTE_DELTA if compute_delta else 0) | (ATTN_BWD_DQ_OVERWRITE if dq_overwrite else 0)
-               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0))
+               | (ATTN_BWD_FINALIZE_DQ if finalize_dq else 0) | (ATTN_BWD_BALANCED if balanced else 0)
+               | (ATTN_BWD_DETERMINISTIC if deterministic else 0))
     a.cu_seqlens_q, a.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
     _check(load().attn_bwd(ctypes.byref(a), _stream(stream)))
 

@@ -339,7 +339,8 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
     return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_bwd_args));
   if (a->dtype != ATTN_DTYPE_BF16 && a->dtype != ATTN_DTYPE_F32)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported", a->dtype);
-  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED;
+  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED |
+                         ATTN_BWD_DETERMINISTIC;
   if (a->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
   TRY(check_dims(a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim));
   float scale;
@@ -427,7 +428,8 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   if (a->struct_size < sizeof(attn_bwd_chunks_args))
     return fail(ATTN_ERR_INVALID_ARG, "struct_size %u < %zu", a->struct_size, sizeof(attn_bwd_chunks_args));
   if (a->dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype %u is not supported (bf16 only)", a->dtype);
-  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED;
+  const uint32_t known = ATTN_BWD_COMPUTE_DELTA | ATTN_BWD_DQ_OVERWRITE | ATTN_BWD_FINALIZE_DQ | ATTN_BWD_BALANCED |
+                         ATTN_BWD_DETERMINISTIC;
   if (a->flags & ~known) return fail(ATTN_ERR_INVALID_ARG, "unknown flag bits 0x%x", a->flags);
   if (a->n_chunks < 0 || a->n_chunks > ATTN_MAX_CHUNKS)
     return fail(ATTN_ERR_INVALID_ARG, "n_chunks must be in [0, %d]", ATTN_MAX_CHUNKS);

@@ -72,7 +72,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 8
+#define ATTN_ABI_VERSION 9
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -236,6 +236,9 @@ ATTN_API int attn_merge_lse(const attn_merge_args* args, void* stream);
 #define ATTN_BWD_DQ_OVERWRITE (1u << 1)  /* dq_acc = this chunk's dQ instead of dq_acc += it */
 #define ATTN_BWD_FINALIZE_DQ (1u << 2)   /* after accumulating, write dq = dq_acc in `dtype` */
 #define ATTN_BWD_BALANCED (1u << 3)      /* causal work order pairing early and late key tiles */
+/* Ask for results that do not depend on scheduling (no floating-point atomics).  Every backward
+ * call of this library is deterministic, so the flag is accepted and changes nothing. */
+#define ATTN_BWD_DETERMINISTIC (1u << 4)
 
 /*
  * attn_bwd: gradients of sum(dO * O) for one chunk of keys.

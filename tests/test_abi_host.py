@@ -95,8 +95,22 @@ int main(void) {
             assert getattr(cls[t], f).offset == int(val), key
 
 
+def test_header_constants_match_binding():
+    """Every integer #define of include/attn.h that the binding names has the same value there."""
+    text = open(HEADER).read()
+    defs = {}
+    for m in re.finditer(r"#define (ATTN_[A-Z0-9_]+) +(\(1u << (\d+)\)|(\d+))", text):
+        defs[m.group(1)] = (1 << int(m.group(3))) if m.group(3) else int(m.group(4))
+    checked = 0
+    for name, val in defs.items():
+        if hasattr(B, name):
+            assert getattr(B, name) == val, name
+            checked += 1
+    assert "ATTN_BWD_DETERMINISTIC" in defs and checked >= 10, (checked, sorted(defs))
+
+
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 8
+    assert lib.attn_abi_version() == 9
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
     assert lib.attn_status_string(99) == b"unknown status"
@@ -228,6 +242,8 @@ def bwd_args(**kw):
 BWD_BAD = [
     (dict(flags=1 << 9), B.ATTN_ERR_INVALID_ARG, "flag"),
     (dict(dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
+    # The DETERMINISTIC bit passes flag validation: the error is the next one checked.
+    (dict(flags=B.ATTN_BWD_DETERMINISTIC, dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
     (dict(lse=FAKE + 4), B.ATTN_ERR_UNSUPPORTED, "aligned"),
     (dict(workspace=None), B.ATTN_ERR_WORKSPACE, "workspace of 1024 bytes"),
     (dict(workspace_bytes=1023), B.ATTN_ERR_WORKSPACE, "1023 given"),
@@ -362,6 +378,7 @@ BWD_CHUNKS_BAD = [
     (dict(dtype=B.ATTN_DTYPE_F32), B.ATTN_ERR_UNSUPPORTED, "bf16 only"),
     (dict(flags=1 << 9), B.ATTN_ERR_INVALID_ARG, "flag"),
     (dict(dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
+    (dict(flags=B.ATTN_BWD_DETERMINISTIC, dq_acc=None), B.ATTN_ERR_INVALID_ARG, "dq_acc"),
     (dict(workspace_bytes=1023), B.ATTN_ERR_WORKSPACE, "1023 given"),
     (dict(workspace=FAKE + 16), B.ATTN_ERR_WORKSPACE, "256-byte"),
     (dict(dq=None, flags=B.ATTN_BWD_FINALIZE_DQ), B.ATTN_ERR_INVALID_ARG, "dq is NULL"),

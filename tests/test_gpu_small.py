@@ -521,9 +521,16 @@ def test_bwd_deterministic():
     o, lse = shard.causal_attention_forward(q, k, v)
     r1 = shard.causal_attention_backward(q, k, v, o, do, lse)
     r2 = shard.causal_attention_backward(q, k, v, o, do, lse)
+    # The DETERMINISTIC flag is accepted and changes nothing.
+    dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
+    dq_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = shard.bwd_workspace(1, 2, 300, q.device)
+    B.attn_bwd(q, k, v, o, do, lse, ws, dq_acc, dk, dv, dq=dq, causal=True, compute_delta=True,
+               dq_overwrite=True, finalize_dq=True, balanced=True, deterministic=True)
     torch.cuda.synchronize()
-    for a, b in zip(r1, r2):
+    for a, b, c in zip(r1, r2, (dq, dk, dv)):
         assert torch.equal(a, b)
+        assert torch.equal(a, c)
 
 
 # (B, Hq, Hkv, L, D, n_splits, seqlens)
