@@ -41,6 +41,10 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 def check(name: str, got, ref, atol: float, *, scale_by_max: bool = False):
     """Max-abs check; the bound is atol, or atol * max(1, max|ref|) when scale_by_max.
 
+    With scale_by_max the relative Frobenius error over the finite entries must
+    also stay below atol (skipped when the reference is all zero): the scaled
+    absolute bound alone is loose where |ref| is large, and the relative bound
+    catches a wrong result that stays small.
     Non-finite entries (e.g. LSE = -inf of rows that see no key) must match exactly.
     Returns (max-abs error, rms of the reference).
     """
@@ -60,6 +64,10 @@ def check(name: str, got, ref, atol: float, *, scale_by_max: bool = False):
     rms = float(np.sqrt(np.mean(ref[fr] ** 2)))
     log(f"  {name}: max|err| {err:.3e} (tol {tol:.1e}) max|ref| {mx:.3e} rms(ref) {rms:.3e}")
     assert err <= tol, f"{name}: max abs error {err:.4e} > {tol:.1e} (max|ref| {mx:.3e})"
+    if scale_by_max and rms > 0.0:
+        rel = float(np.linalg.norm(got[fr] - ref[fr]) / np.linalg.norm(ref[fr]))
+        log(f"  {name}: relative Frobenius error {rel:.3e} (tol {atol:.1e})")
+        assert rel <= atol, f"{name}: relative Frobenius error {rel:.4e} > {atol:.1e}"
     return err, rms
 
 
