@@ -13,7 +13,7 @@
 //   and dK^T += Q^T dS straight from registers.  Each group of 32 keys is
 //   served by a pair of wavefronts, one producing P and dV, the other dS and dK
 //   (see below).  Query and dO tiles stream from HBM into LDS (global_load_lds,
-//   double buffered); the transposed operands Q^T, dO^T are read from the same
+//   a 3-stage ring); the transposed operands Q^T, dO^T are read from the same
 //   row-major tiles with ds_read_b64_tr_b16.
 //
 //   dQ kernel (query-outer).  A workgroup owns 128 queries (32 per wavefront
@@ -90,8 +90,9 @@ __device__ __forceinline__ bf16x8 slab8(const f32x16& a, int o) {
 //     forms S = Q K^T for tile t (one key per lane), P = exp(S - LSE) with the
 //     mask, hands P to its partner through LDS and runs dV^T += dO^T P;
 //   * the "dS" wavefront (w >= 4) holds V and accumulates dK: it forms
-//     dP = dO V^T for tile t, and for tile t - 1 (one step behind, so that P
-//     is already published) reads P, forms dS = P (dP - delta) and runs
+//     dP - delta = dO V^T - delta for tile t (its accumulator starts at the
+//     stored -delta), and for tile t - 1 (one step behind, so that P is
+//     already published) reads P, forms dS = P (dP - delta) and runs
 //     dK^T += Q^T dS.
 // Both carry 32 contractions per tile; the exponentials of one overlap the
 // contractions of the other on their shared SIMD.  One LDS-only barrier per
