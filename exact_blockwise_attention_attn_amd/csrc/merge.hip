@@ -54,18 +54,24 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p) {
     for (int i = 0; i < p.n_parts; ++i) {
       float xl = lp[(int64_t)i * p.lse_part_stride];
       f32x4 xo = *(const f32x4*)(op + (int64_t)i * p.o_part_stride);
+      // Carry the new subtree up the stack until it finds a free level.  A
+      // flag instead of a break keeps every stack index a compile-time
+      // constant, so the stack lives in registers.
+      bool carry = true;
 #pragma unroll
       for (int k = 0; k < kMaxLevels; ++k) {
-        if (pending & (1u << k)) {
-          merge2(sl[k], so[k], xl, xo);  // left = earlier subtree
-          xl = sl[k];
-          xo = so[k];
-          pending &= ~(1u << k);
-        } else {
-          sl[k] = xl;
-          so[k] = xo;
-          pending |= 1u << k;
-          break;
+        if (carry) {
+          if (pending & (1u << k)) {
+            merge2(sl[k], so[k], xl, xo);  // left = earlier subtree
+            xl = sl[k];
+            xo = so[k];
+            pending &= ~(1u << k);
+          } else {
+            sl[k] = xl;
+            so[k] = xo;
+            pending |= 1u << k;
+            carry = false;
+          }
         }
       }
     }
