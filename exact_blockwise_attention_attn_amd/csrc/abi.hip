@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <string>
@@ -33,6 +35,19 @@ int ok() {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// Success of a compute call: its work is enqueued on `stream`.  With the
+// environment variable ATTN_DEBUG_SYNC set (to anything but "0"), the call
+// first waits for the stream, so a failure of its kernels is reported here, by
+// the call that caused it, instead of at the caller's next synchronisation.
+int enqueued(void* stream, const char* what) {
+  const char* v = getenv("ATTN_DEBUG_SYNC");
+  if (v && *v && strcmp(v, "0") != 0) {
+    const hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return ok();
 }
 
 size_t elem_size(uint32_t dtype) { return dtype == ATTN_DTYPE_F32 ? 4 : 2; }
@@ -203,7 +218,7 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   hipError_t e = a->dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(p, a->head_dim, s)
                                              : attn::launch_fwd_f32(p, a->head_dim, s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_partial launch");
-  return ok();
+  return enqueued(stream, "attn_fwd_partial (ATTN_DEBUG_SYNC)");
 }
 
 int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
@@ -285,7 +300,7 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   TRY(check_items(attn::items_fwd_bf16(p), "attn_fwd_chunks"));
   hipError_t e = attn::launch_fwd_chunks_bf16(p, ct, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunks launch");
-  return ok();
+  return enqueued(stream, "attn_fwd_chunks (ATTN_DEBUG_SYNC)");
 }
 
 int attn_merge_lse(const attn_merge_args* a, void* stream) {
@@ -330,7 +345,7 @@ int attn_merge_lse(const attn_merge_args* a, void* stream) {
   TRY(check_items(attn::items_merge(p, a->head_dim), "attn_merge_lse"));
   hipError_t e = attn::launch_merge(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_merge_lse launch");
-  return ok();
+  return enqueued(stream, "attn_merge_lse (ATTN_DEBUG_SYNC)");
 }
 
 int attn_bwd(const attn_bwd_args* a, void* stream) {
@@ -420,7 +435,7 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   const int run_dq = has_q && (!invisible || p.dq_overwrite || finalize);
   e = bf16 ? attn::launch_bwd_bf16(p, D, run_dq, s) : attn::launch_bwd_f32(p, D, run_dq, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
-  return ok();
+  return enqueued(stream, "attn_bwd (ATTN_DEBUG_SYNC)");
 }
 
 int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
@@ -533,7 +548,7 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   // Without queries the dK/dV kernel writes zeros for every chunk and no dQ pass runs.
   e = attn::launch_bwd_chunks_bf16(p, ct, a->head_dim, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunks launch");
-  return ok();
+  return enqueued(stream, "attn_bwd_chunks (ATTN_DEBUG_SYNC)");
 }
 
 }  // extern "C"
@@ -673,7 +688,7 @@ int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
   hipError_t e = attn::launch_tree_decode(p, tt, a->n_queries, a->o, a->o_stride[0], a->o_stride[1], a->lse,
                                           a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode_tree launch");
-  return ok();
+  return enqueued(stream, "attn_decode_tree (ATTN_DEBUG_SYNC)");
 }
 
 size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
@@ -766,7 +781,7 @@ static int decode_splitkv(const attn_decode_args* a, void* stream, bool noalloc)
   p.part_lse = (float*)((char*)ws + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
   hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, noalloc ? "attn_decode_splitkv_noalloc launch" : "attn_decode_splitkv launch");
-  return ok();
+  return enqueued(stream, noalloc ? "attn_decode_splitkv_noalloc (ATTN_DEBUG_SYNC)" : "attn_decode_splitkv (ATTN_DEBUG_SYNC)");
 }
 
 int attn_decode_splitkv(const attn_decode_args* a, void* stream) { return decode_splitkv(a, stream, false); }

@@ -42,7 +42,11 @@
  *     retains a pointer past the call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Success means the work is enqueued on `stream`; nothing synchronises.
- *     Device-side faults surface at the caller's next synchronisation.
+ *     Device-side faults surface at the caller's next synchronisation.  For
+ *     debugging, the environment variable ATTN_DEBUG_SYNC (set, and not "0";
+ *     read on every call) makes each compute call wait for `stream` before it
+ *     returns, so that a failure of its kernels is returned as ATTN_ERR_HIP by
+ *     the call itself.
  *   - Every argument is checked on the host before anything is enqueued; on
  *     error the call returns a nonzero status, enqueues nothing, leaves every
  *     output untouched and records a message for attn_last_error().  This

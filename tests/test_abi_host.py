@@ -538,3 +538,12 @@ def test_last_error_is_thread_local(lib):
     t.join()
     assert seen == [b""]
     assert b"head_dim" in lib.attn_last_error()
+
+
+def test_debug_sync_keeps_host_validation(lib, monkeypatch):
+    """With ATTN_DEBUG_SYNC set, invalid calls are still rejected on the host, before anything is
+    enqueued or synchronised (the fake pointers are never touched)."""
+    monkeypatch.setenv("ATTN_DEBUG_SYNC", "1")
+    a = bwd_args(dq_acc=None)
+    assert lib.attn_bwd(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "dq_acc" in lib.attn_last_error().decode()

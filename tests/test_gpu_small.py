@@ -533,6 +533,30 @@ def test_bwd_deterministic():
         assert torch.equal(a, c)
 
 
+def test_debug_sync_same_results(monkeypatch):
+    """ATTN_DEBUG_SYNC only adds a wait: forward, backward and decode results are unchanged bit for bit."""
+    log("ATTN_DEBUG_SYNC")
+    (q, k, v), _ = _inputs(108, 1, 200, 200, 2, 2, 128, "bf16")
+    do, _ = seq_tensor(108, 3, 1, 200, 2, 128, "bf16")
+
+    def run():
+        o, lse = shard.causal_attention_forward(q, k, v)
+        grads = shard.causal_attention_backward(q, k, v, o, do, lse)
+        qd = q[:, 0].contiguous()  # [1, 2, 128] decode queries over the cache k, v
+        od = torch.empty_like(qd)
+        ld = torch.empty((1, 2), dtype=torch.float32, device=q.device)
+        ws = torch.empty(B.attn_decode_workspace_size(1, 2, 128, 4), dtype=torch.uint8, device=q.device)
+        B.attn_decode_splitkv(qd, k, v, od, ld, ws, n_splits=4)
+        torch.cuda.synchronize()
+        return (o, lse, *grads, od, ld)
+
+    ref = run()
+    monkeypatch.setenv("ATTN_DEBUG_SYNC", "1")
+    got = run()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
 # (B, Hq, Hkv, L, D, n_splits, seqlens)
 DECODE_CASES = [
     (2, 8, 2, 1000, 128, 8, None),
