@@ -190,7 +190,8 @@ class AttnError(RuntimeError):
 
 
 def lib_path() -> str:
-    return _build.LIB_PATH
+    """The in-tree libattn.so, or the library named by ATTN_LIBRARY (e.g. the host-ASan build)."""
+    return os.environ.get("ATTN_LIBRARY") or _build.LIB_PATH
 
 
 def load(build_if_missing: bool = True) -> ctypes.CDLL:

@@ -1,10 +1,17 @@
 """Build libattn.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m exact_blockwise_attention_attn_amd.build [--verbose]
+    python -m exact_blockwise_attention_attn_amd.build [--verbose] [--host-asan]
 
 Every source is compiled to an object under ``_build/`` in parallel, then
 linked into ``exact_blockwise_attention_attn_amd/libattn.so`` (replaced
 atomically).  Packed fp32 VALU instructions are disabled for all device code.
+
+``--host-asan`` instead builds ``_build/libattn_host_asan.so``, with the host
+code of the C ABI (argument validation, table building) under AddressSanitizer
+and the device code unchanged.  The host tests run against it with
+
+    ATTN_LIBRARY=<that path> LD_PRELOAD=<hipcc -print-file-name=libclang_rt.asan-x86_64.so> \
+        ASAN_OPTIONS=detect_leaks=0 python -m pytest tests/test_abi_host.py
 """
 
 from __future__ import annotations
@@ -20,6 +27,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
+HOST_ASAN_LIB_PATH = os.path.join(BUILD_DIR, "libattn_host_asan.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -44,9 +52,14 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-only AddressSanitizer for the C ABI's host code (each sanitizer flag
+# applies to the host pass only, never to device code).
+HOST_ASAN_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def _compile(src: str, verbose: bool, extra=(), out_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -73,6 +86,23 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def build_host_asan(jobs: int | None = None) -> str:
+    """Build _build/libattn_host_asan.so: abi.hip's host code under AddressSanitizer, every
+    other object as in build().  Returns its path."""
+    out_dir = os.path.join(BUILD_DIR, "host_asan")
+    os.makedirs(out_dir, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, False, HOST_ASAN_FLAGS if s == "abi.hip" else (), out_dir),
+                           SOURCES))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan", *HOST_ASAN_FLAGS[:2], *objs,
+           "-o", HOST_ASAN_LIB_PATH]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    return HOST_ASAN_LIB_PATH
 
 
 def resource_usage(sources=None) -> dict:
@@ -116,8 +146,9 @@ def resource_usage(sources=None) -> dict:
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--verbose", action="store_true", help="print kernel register/LDS usage")
+    ap.add_argument("--host-asan", action="store_true", help="build the host-AddressSanitizer library instead")
     args = ap.parse_args()
-    print(build(verbose=args.verbose))
+    print(build_host_asan() if args.host_asan else build(verbose=args.verbose))
 
 
 if __name__ == "__main__":

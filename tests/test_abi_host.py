@@ -547,3 +547,11 @@ def test_debug_sync_keeps_host_validation(lib, monkeypatch):
     a = bwd_args(dq_acc=None)
     assert lib.attn_bwd(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
     assert "dq_acc" in lib.attn_last_error().decode()
+
+
+def test_library_override(monkeypatch):
+    """ATTN_LIBRARY names the library the binding loads (the host-ASan build, say); unset, the in-tree one."""
+    monkeypatch.delenv("ATTN_LIBRARY", raising=False)
+    assert B.lib_path().endswith(os.path.join("exact_blockwise_attention_attn_amd", "libattn.so"))
+    monkeypatch.setenv("ATTN_LIBRARY", "/some/other/libattn.so")
+    assert B.lib_path() == "/some/other/libattn.so"
