@@ -112,6 +112,10 @@ FUSED_CASES = [
     (1, 96, 2, 2, 128, (128, 64), (5000, 0), 200, True, True),
     # the shard layout: 8 chunks of 64 keys, queries in the middle of the range
     (1, 256, 2, 2, 128, (64,) * 8, tuple(64 * i for i in range(8)), 192, True, True),
+    # the most chunks a table takes (64): ragged lengths 0..69 at consecutive positions, the
+    # queries' diagonal inside the range, so chunks are fully visible, partly visible and skipped
+    (1, 128, 2, 2, 128, tuple((37 * i) % 70 for i in range(64)),
+     tuple(sum((37 * j) % 70 for j in range(i)) for i in range(64)), 1000, True, True),
 ]
 
 
@@ -462,6 +466,10 @@ TREE_CASES = [
     _chain_tree(),
     # d = 64 with GQA 4: 70 queries x 4 heads = 280 packed rows under the root (three tiles)
     (70, 8, 2, 64, 3000, ((0, 2500, 0, 70), (2500, 300, 0, 35), (2800, 200, 35, 70))),
+    # the most nodes a tree takes (256): a 9,000-key root over 255 queries and one 10-key leaf
+    # per query.  Cut into 2,048-key segments the nodes need 260 table entries, so the host
+    # doubles the segment length until they fit (16,384 keys: 256 entries).
+    (255, 4, 2, 128, 9000 + 255 * 10, ((0, 9000, 0, 255),) + tuple((9000 + 10 * i, 10, i, i + 1) for i in range(255))),
 ]
 
 
