@@ -12,6 +12,9 @@ Prints one JSON line.  Besides the contract fields it carries:
   roofline      the backward call (the dominant cost): algorithmic FLOPs per call
                 over its average duration, timed with HIP events on the stream it
                 runs on, against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  peak_on_device  the bf16 MFMA peak recomputed from rocminfo (compute units x 4096
+                FLOP/clk x maximum shader clock), beside the published 2.5 PFLOP/s
+                that the fractions use;
   kernels       per-call timings (forward call, backward call);
   secondary     the other workloads: the 128K sequence shard forward over 32
                 chunks, its backward, and split-KV GQA decode (GB/s of K/V,
@@ -363,6 +366,27 @@ def bench_decode(args, stream):
                                "frac_of_copy": u_bytes / tu / 1e6 / copy_gbs}}
 
 
+def _device_peak():
+    """The bf16 MFMA peak recomputed from the device: compute units x 4096 FLOP/clk x the maximum
+    shader clock, both read from rocminfo (None when it is not available)."""
+    import re
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in out.split("Agent ")[1:]:
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"compute_units": cus, "max_sclk_mhz": clk, "mfma_bf16_tflops": cus * 4096 * clk / 1e6}
+    return None
+
+
 def _host_facts():
     facts = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": []}
     try:
@@ -550,6 +574,7 @@ def main():
         "config": {"workload": "causal_fwdbwd_32k", "batch": m["B"], "heads": m["H"], "seq_len": m["S"],
                    "head_dim": m["D"], "causal": True, "schedule": "balanced", "parallelism": "single GPU"},
         "frac_of_mfma_peak": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "peak_on_device": _device_peak(),
         "roofline": {"bound": "mfma", "kernel": "attn_bwd call (statistics + dK/dV + dQ kernels)",
                      "achieved": round(bwd_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": BWD_CALL_HBM_BYTES},
