@@ -37,6 +37,20 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// With the environment variable ATTN_LOG set (to anything but "0"), every
+// compute call that enqueues work writes one line to stderr naming the call
+// and its sizes.  Read on every call.
+void log_call(const char* fmt, ...) {
+  const char* v = getenv("ATTN_LOG");
+  if (!v || !*v || strcmp(v, "0") == 0) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[attn] %s\n", buf);
+}
+
 // Success of a compute call: its work is enqueued on `stream`.  With the
 // environment variable ATTN_DEBUG_SYNC set (to anything but "0"), the call
 // first waits for the stream, so a failure of its kernels is reported here, by
@@ -218,6 +232,9 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   hipError_t e = a->dtype == ATTN_DTYPE_BF16 ? attn::launch_fwd_bf16(p, a->head_dim, s)
                                              : attn::launch_fwd_f32(p, a->head_dim, s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_partial launch");
+  log_call("attn_fwd_partial dtype=%u batch=%d heads_q=%d heads_kv=%d seqlen_q=%d seqlen_k=%d head_dim=%d causal=%d "
+           "flags=0x%x varlen=%d stream=%p", a->dtype, a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k,
+           a->head_dim, a->causal, a->flags, a->cu_seqlens_q != nullptr, stream);
   return enqueued(stream, "attn_fwd_partial (ATTN_DEBUG_SYNC)");
 }
 
@@ -300,6 +317,9 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   TRY(check_items(attn::items_fwd_bf16(p), "attn_fwd_chunks"));
   hipError_t e = attn::launch_fwd_chunks_bf16(p, ct, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd_chunks launch");
+  log_call("attn_fwd_chunks batch=%d heads_q=%d heads_kv=%d seqlen_q=%d head_dim=%d n_chunks=%d causal=%d flags=0x%x "
+           "stream=%p", a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->head_dim, a->n_chunks, a->causal, a->flags,
+           stream);
   return enqueued(stream, "attn_fwd_chunks (ATTN_DEBUG_SYNC)");
 }
 
@@ -345,6 +365,8 @@ int attn_merge_lse(const attn_merge_args* a, void* stream) {
   TRY(check_items(attn::items_merge(p, a->head_dim), "attn_merge_lse"));
   hipError_t e = attn::launch_merge(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_merge_lse launch");
+  log_call("attn_merge_lse n_parts=%d batch=%d seqlen=%d heads=%d head_dim=%d mode=%u stream=%p", a->n_parts, a->batch,
+           a->seqlen, a->heads, a->head_dim, a->mode, stream);
   return enqueued(stream, "attn_merge_lse (ATTN_DEBUG_SYNC)");
 }
 
@@ -435,6 +457,9 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   const int run_dq = has_q && (!invisible || p.dq_overwrite || finalize);
   e = bf16 ? attn::launch_bwd_bf16(p, D, run_dq, s) : attn::launch_bwd_f32(p, D, run_dq, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd launch");
+  log_call("attn_bwd dtype=%u batch=%d heads_q=%d heads_kv=%d seqlen_q=%d seqlen_k=%d head_dim=%d causal=%d flags=0x%x "
+           "varlen=%d stream=%p", a->dtype, a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim,
+           a->causal, a->flags, a->cu_seqlens_q != nullptr, stream);
   return enqueued(stream, "attn_bwd (ATTN_DEBUG_SYNC)");
 }
 
@@ -548,6 +573,9 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   // Without queries the dK/dV kernel writes zeros for every chunk and no dQ pass runs.
   e = attn::launch_bwd_chunks_bf16(p, ct, a->head_dim, s);
   if (e != hipSuccess) return hip_fail(e, "attn_bwd_chunks launch");
+  log_call("attn_bwd_chunks batch=%d heads_q=%d heads_kv=%d seqlen_q=%d head_dim=%d n_chunks=%d causal=%d flags=0x%x "
+           "stream=%p", a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->head_dim, a->n_chunks, a->causal, a->flags,
+           stream);
   return enqueued(stream, "attn_bwd_chunks (ATTN_DEBUG_SYNC)");
 }
 
@@ -688,6 +716,8 @@ int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
   hipError_t e = attn::launch_tree_decode(p, tt, a->n_queries, a->o, a->o_stride[0], a->o_stride[1], a->lse,
                                           a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode_tree launch");
+  log_call("attn_decode_tree n_queries=%d heads_q=%d heads_kv=%d head_dim=%d n_nodes=%d segments=%d stream=%p",
+           a->n_queries, a->heads_q, a->heads_kv, a->head_dim, a->n_nodes, tt.n, stream);
   return enqueued(stream, "attn_decode_tree (ATTN_DEBUG_SYNC)");
 }
 
@@ -781,6 +811,9 @@ static int decode_splitkv(const attn_decode_args* a, void* stream, bool noalloc)
   p.part_lse = (float*)((char*)ws + ((rows * a->head_dim * 4 + 255) & ~(size_t)255));
   hipError_t e = attn::launch_decode(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, noalloc ? "attn_decode_splitkv_noalloc launch" : "attn_decode_splitkv launch");
+  log_call("%s batch=%d heads_q=%d heads_kv=%d head_dim=%d cache_len=%lld n_splits=%d seqlens=%d streamk=%d stream=%p",
+           noalloc ? "attn_decode_splitkv_noalloc" : "attn_decode_splitkv", a->batch, a->heads_q, a->heads_kv,
+           a->head_dim, (long long)a->cache_len, a->n_splits, a->seqlens != nullptr, p.streamk, stream);
   return enqueued(stream, noalloc ? "attn_decode_splitkv_noalloc (ATTN_DEBUG_SYNC)" : "attn_decode_splitkv (ATTN_DEBUG_SYNC)");
 }
 

@@ -106,9 +106,10 @@ __device__ __forceinline__ SeqHeadUnit varlen_order(int bid, int H, int n_units)
 }
 
 // Log-sum-exp merge of (La, Oa) with (Lb, Ob); -inf parts contribute nothing.
+// A NaN on either side makes both weights and L NaN (fmaxf alone would drop it).
 __device__ __forceinline__ void merge_weights(float La, float Lb, float& wa, float& wb, float& L) {
   float mx = fmaxf(La, Lb);
-  if (mx == neg_inf()) {
+  if ((La == neg_inf()) & (Lb == neg_inf())) {
     wa = 0.f;
     wb = 0.f;
     L = neg_inf();

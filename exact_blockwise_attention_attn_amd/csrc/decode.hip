@@ -202,18 +202,19 @@ __device__ __forceinline__ void split_piece(const DecodeParams& prm, int b, int 
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, m_s[w][q]);
+    // Weight 0 for a wavefront whose stabiliser is still -inf; only an exactly
+    // zero sum is an empty split, so a NaN score reaches the partial.
     float tot = 0.f, o = 0.f;
-    if (M != neg_inf()) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = exp2_fast((m_s[w][q] - M) * prm.scale_log2);
-        tot = fmaf(f, l_s[w][q], tot);
-        o = fmaf(f, o_s[w][q][d], o);
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float f = (m_s[w][q] == neg_inf()) ? 0.f : exp2_fast((m_s[w][q] - M) * prm.scale_log2);
+      tot = fmaf(f, l_s[w][q], tot);
+      o = fmaf(f, o_s[w][q][d], o);
     }
+    const bool empty = tot == 0.f;
     const int64_t prow = row(q);
-    prm.part_o[prow * D + d] = (tot > 0.f) ? o / tot : 0.f;
-    if (d == 0) prm.part_lse[prow] = (M == neg_inf()) ? neg_inf() : fmaf(M, prm.scale, logf(tot));
+    prm.part_o[prow * D + d] = empty ? 0.f : o / tot;
+    if (d == 0) prm.part_lse[prow] = empty ? neg_inf() : fmaf(M, prm.scale, logf(tot));
   }
   // The next piece of the workgroup reuses the LDS buffers.
   __syncthreads();

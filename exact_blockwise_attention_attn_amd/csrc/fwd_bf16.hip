@@ -157,8 +157,11 @@ __device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x16* oacc
   constexpr int NDB = D / 32;
   const float l_tot = half_sum(st.l);
   if (!qok) return;
-  const float lse_this = (l_tot > 0.f) ? fmaf(st.m, p.scale, logf(l_tot)) : neg_inf();
-  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  // Only an exactly zero sum is a row with no visible key; a NaN score keeps
+  // the sum NaN and so reaches the row's O and LSE.
+  const bool empty = l_tot == 0.f;
+  const float lse_this = empty ? neg_inf() : fmaf(st.m, p.scale, logf(l_tot));
+  const float inv = empty ? 0.f : 1.0f / l_tot;
   float* lse_ptr = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss;
   float w_old = 0.f, w_new = 1.f, L = lse_this;
   if (p.accumulate) merge_weights(*lse_ptr, lse_this, w_old, w_new, L);
@@ -396,18 +399,18 @@ __global__ __launch_bounds__(D) void tree_merge_kernel(const float* po, const fl
   __syncthreads();
   float M = neg_inf();
   for (int k = 0; k < K; ++k) M = fmaxf(M, lv[k]);
+  // An empty partial (LSE -inf) has weight 0 even when every partial is
+  // empty; a NaN LSE gives NaN weights, so it reaches O and the LSE.
   float S = 0.f, O = 0.f;
-  if (M != neg_inf()) {
 #pragma unroll 8
-    for (int k = 0; k < K; ++k) {
-      const float w = expf(lv[k] - M);  // 0 for an empty partial
-      S += w;
-      O = fmaf(w, po[((int64_t)ent[k] * Hq + h) * D + t], O);
-    }
+  for (int k = 0; k < K; ++k) {
+    const float w = (lv[k] == neg_inf()) ? 0.f : expf(lv[k] - M);
+    S += w;
+    O = fmaf(w, po[((int64_t)ent[k] * Hq + h) * D + t], O);
   }
-  const bool any = S > 0.f;
-  out_o[(int64_t)i * o_sq + (int64_t)h * o_sh + t] = f32_to_bf16(any ? O / S : 0.f);
-  if (t == 0) out_lse[(int64_t)i * Hq + h] = any ? M + logf(S) : neg_inf();
+  const bool empty = S == 0.f;
+  out_o[(int64_t)i * o_sq + (int64_t)h * o_sh + t] = f32_to_bf16(empty ? 0.f : O / S);
+  if (t == 0) out_lse[(int64_t)i * Hq + h] = empty ? neg_inf() : M + logf(S);
 }
 
 // ------------------------------------------------------ fused chunk table --

@@ -116,19 +116,21 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdParams p) {
   l_run = 0.f;
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
-  if (M != neg_inf()) {
 #pragma unroll
-    for (int k = 0; k < KSPL; ++k) {
-      const float w = expf(m_s[k][r] - M);  // 0 for a group that saw no key
-      l_run = fmaf(w, l_s[k][r], l_run);
+  for (int k = 0; k < KSPL; ++k) {
+    // Weight 0 for a group whose stabiliser is still -inf (it saw no key, or
+    // only NaN scores: its NaN sum then survives 0 * NaN).
+    const float w = (m_s[k][r] == neg_inf()) ? 0.f : expf(m_s[k][r] - M);
+    l_run = fmaf(w, l_s[k][r], l_run);
 #pragma unroll
-      for (int f = 0; f < F; ++f) acc[f] = fmaf(w, accs[(k * BM + r) * D + f0 + f], acc[f]);
-    }
+    for (int f = 0; f < F; ++f) acc[f] = fmaf(w, accs[(k * BM + r) * D + f0 + f], acc[f]);
   }
   m_run = M;
   if (!qok) return;
-  const float lse_this = (m_run == neg_inf()) ? neg_inf() : m_run + logf(l_run);
-  const float inv = (l_run > 0.f) ? 1.0f / l_run : 0.f;
+  // Only an exactly zero sum is a row with no visible key; NaN stays NaN.
+  const bool empty = l_run == 0.f;
+  const float lse_this = empty ? neg_inf() : m_run + logf(l_run);
+  const float inv = empty ? 0.f : 1.0f / l_run;
   float* lse_ptr = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + (int64_t)qi * p.lse_ss;
   // The row's 16 lanes are in one wavefront: all read the running LSE before lane 0 writes it.
   float w_old = 0.f, w_new = 1.f, L = lse_this;

@@ -555,3 +555,11 @@ def test_library_override(monkeypatch):
     assert B.lib_path().endswith(os.path.join("exact_blockwise_attention_attn_amd", "libattn.so"))
     monkeypatch.setenv("ATTN_LIBRARY", "/some/other/libattn.so")
     assert B.lib_path() == "/some/other/libattn.so"
+
+
+def test_log_only_on_enqueue(lib, monkeypatch, capfd):
+    """ATTN_LOG logs calls that enqueue work; a call rejected on the host logs nothing."""
+    monkeypatch.setenv("ATTN_LOG", "1")
+    a = bwd_args(dq_acc=None)
+    assert lib.attn_bwd(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "[attn]" not in capfd.readouterr().err

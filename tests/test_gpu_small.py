@@ -565,6 +565,124 @@ def test_debug_sync_same_results(monkeypatch):
         assert torch.equal(a, b)
 
 
+def test_log_line(monkeypatch, capfd):
+    """ATTN_LOG writes one line per enqueued call, naming the call and its sizes."""
+    (q, k, v), _ = _inputs(108, 1, 70, 90, 2, 1, 64, "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, 70), dtype=torch.float32, device="cuda")
+    monkeypatch.setenv("ATTN_LOG", "1")
+    B.attn_fwd_partial(q, k, v, o, lse, causal=True)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert "[attn] attn_fwd_partial dtype=1 batch=1 heads_q=2 heads_kv=1 seqlen_q=70 seqlen_k=90 head_dim=64 causal=1" in err
+
+
+def test_nan_propagates_where_visible():
+    """A NaN in one key row reaches exactly the rows that see that key (causal), and no other output
+    changes: rows before it are bitwise equal to the clean run (hidden keys are masked out, never read
+    into the softmax)."""
+    log("NaN propagation")
+    (q, k, v), _ = _inputs(115, 1, 192, 192, 2, 2, 128, "bf16")
+    o0, l0 = shard.causal_attention_forward(q, k, v)
+    j = 100
+    k2 = k.clone()
+    k2[0, j, 1, 5] = float("nan")
+    o1, l1 = shard.causal_attention_forward(q, k2, v)
+    torch.cuda.synchronize()
+    # head 1, rows i >= j see key j: all NaN; rows before it and head 0 are unchanged bit for bit.
+    assert torch.isnan(o1[0, j:, 1]).all() and torch.isnan(l1[0, 1, j:]).all()
+    assert torch.equal(o1[0, :j, 1], o0[0, :j, 1]) and torch.equal(l1[0, 1, :j], l0[0, 1, :j])
+    assert torch.equal(o1[0, :, 0], o0[0, :, 0]) and torch.equal(l1[0, 0], l0[0, 0])
+
+
+
+def test_nan_propagates_other_paths():
+    """The same rule on the fp32 forward, the fused chunk table, the LSE merge and split-KV decode: a NaN
+    reaches the outputs that depend on it and changes nothing else bit for bit."""
+    log("NaN propagation: fp32 forward, chunks, merge, decode")
+    j = 100
+    # fp32 forward, causal.
+    (q, k, v), _ = _inputs(116, 1, 192, 192, 2, 2, 64, "f32")
+    o0, l0 = torch.empty_like(q), torch.empty((1, 2, 192), dtype=torch.float32, device="cuda")
+    B.attn_fwd_partial(q, k, v, o0, l0, causal=True)
+    k2 = k.clone()
+    k2[0, j, 1, 5] = float("nan")
+    o1, l1 = torch.empty_like(q), torch.empty_like(l0)
+    B.attn_fwd_partial(q, k2, v, o1, l1, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(o1[0, j:, 1]).all() and torch.isnan(l1[0, 1, j:]).all()
+    assert torch.equal(o1[0, :j, 1], o0[0, :j, 1]) and torch.equal(l1[0, 1, :j], l0[0, 1, :j])
+    assert torch.equal(o1[0, :, 0], o0[0, :, 0]) and torch.equal(l1[0, 0], l0[0, 0])
+
+    # Fused chunk table: two chunks of 96 keys at positions 0 and 96; the NaN is global key 100.
+    (q, k, v), _ = _inputs(117, 1, 192, 192, 2, 2, 128, "bf16")
+    ks, vs = [k[:, :96], k[:, 96:]], [v[:, :96], v[:, 96:]]
+    k2 = k.clone()
+    k2[0, j, 1, 5] = float("nan")
+    ks2 = [k2[:, :96], k2[:, 96:]]
+    outs = []
+    for kk in (ks, ks2):
+        o = torch.empty((1, 192, 2, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((1, 2, 192), dtype=torch.float32, device="cuda")
+        B.attn_fwd_chunks(q, kk, vs, o, lse, chunk_pos0=[0, 96], q_pos0=0, causal=True)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    (o0, l0), (o1, l1) = outs
+    assert torch.isnan(o1[0, j:, 1]).all() and torch.isnan(l1[0, 1, j:]).all()
+    assert torch.equal(o1[0, :j, 1], o0[0, :j, 1]) and torch.equal(l1[0, 1, :j], l0[0, 1, :j])
+    assert torch.equal(o1[0, :, 0], o0[0, :, 0]) and torch.equal(l1[0, 0], l0[0, 0])
+
+    # LSE merge: a NaN LSE in one part poisons exactly its row, also next to an empty (-inf) part.
+    rng = np.random.default_rng(118)
+    O = torch.from_numpy(rng.standard_normal((3, 1, 20, 2, 64)).astype(np.float32)).cuda()
+    L = torch.from_numpy(rng.standard_normal((3, 1, 2, 20)).astype(np.float32)).cuda()
+    L[1, 0, 0, 3] = -float("inf")
+    O[1, 0, 3, 0] = 0.0
+    L2 = L.clone()
+    L2[2, 0, 1, 7] = float("nan")
+    L2[0, 0, 0, 3] = float("nan")  # row (h 0, s 3): NaN beside an empty part
+    for tree in (False, True):
+        res = []
+        for LL in (L, L2):
+            o = torch.empty((1, 20, 2, 64), dtype=torch.float32, device="cuda")
+            lse = torch.empty((1, 2, 20), dtype=torch.float32, device="cuda")
+            B.attn_merge_lse(O, LL, o, lse, tree=tree)
+            res.append((o, lse))
+        torch.cuda.synchronize()
+        (o0, l0), (o1, l1) = res
+        bad = torch.zeros((2, 20), dtype=torch.bool, device="cuda")
+        bad[1, 7] = bad[0, 3] = True
+        assert torch.isnan(l1[0][bad]).all() and torch.isnan(o1[0].permute(1, 0, 2)[bad]).all()
+        assert torch.equal(l1[0][~bad], l0[0][~bad])
+        assert torch.equal(o1[0].permute(1, 0, 2)[~bad], o0[0].permute(1, 0, 2)[~bad])
+
+    # Split-KV decode (GQA 4 -> 2): a NaN key of kv head 1 in sequence 0 reaches query heads 2 and 3 of
+    # sequence 0; with that sequence cut before the key, nothing changes.
+    q, _ = seq_tensor(119, 0, 2, 1, 4, 128, "bf16")
+    kc, _ = seq_tensor(119, 1, 2, 1000, 2, 128, "bf16")
+    vc, _ = seq_tensor(119, 2, 2, 1000, 2, 128, "bf16")
+    q = q[:, 0]
+    kc2 = kc.clone()
+    kc2[0, 500, 1, 3] = float("nan")
+    ws = torch.empty(B.attn_decode_workspace_size(2, 4, 128, 8), dtype=torch.uint8, device="cuda")
+    for lens in (None, [400, 1000]):
+        sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+        res = []
+        for kk in (kc, kc2):
+            o = torch.empty((2, 4, 128), dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty((2, 4), dtype=torch.float32, device="cuda")
+            B.attn_decode_splitkv(q, kk, vc, o, lse, ws, n_splits=8, seqlens=sl)
+            torch.cuda.synchronize()
+            res.append((o, lse))
+        (o0, l0), (o1, l1) = res
+        if lens is None:
+            assert torch.isnan(o1[0, 2:]).all() and torch.isnan(l1[0, 2:]).all()
+            assert torch.equal(o1[0, :2], o0[0, :2]) and torch.equal(l1[0, :2], l0[0, :2])
+            assert torch.equal(o1[1], o0[1]) and torch.equal(l1[1], l0[1])
+        else:
+            assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
 # (B, Hq, Hkv, L, D, n_splits, seqlens)
 DECODE_CASES = [
     (2, 8, 2, 1000, 128, 8, None),
