@@ -30,6 +30,7 @@ ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_WORKSPACE = 3
 ATTN_ERR_HIP = 4
+ATTN_ERR_NONFINITE = 5
 ATTN_DTYPE_F32 = 0
 ATTN_DTYPE_BF16 = 1
 ATTN_FWD_ACCUMULATE = 1 << 0

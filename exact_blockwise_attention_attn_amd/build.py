@@ -39,6 +39,7 @@ SOURCES = [
     "bwd_bf16.hip",
     "bwd_f32.hip",
     "decode.hip",
+    "check.hip",
 ]
 
 COMMON_FLAGS = [

@@ -51,15 +51,116 @@ void log_call(const char* fmt, ...) {
   fprintf(stderr, "[attn] %s\n", buf);
 }
 
-// Success of a compute call: its work is enqueued on `stream`.  With the
-// environment variable ATTN_DEBUG_SYNC set (to anything but "0"), the call
-// first waits for the stream, so a failure of its kernels is reported here, by
-// the call that caused it, instead of at the caller's next synchronisation.
-int enqueued(void* stream, const char* what) {
-  const char* v = getenv("ATTN_DEBUG_SYNC");
-  if (v && *v && strcmp(v, "0") != 0) {
-    const hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, what);
+bool env_on(const char* name) {
+  const char* v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+// The outputs a compute call writes, for the non-finite scan (collected only
+// while ATTN_CHECK_FINITE is set).  Each is up to four dimensions with element
+// strides; an error message names dimensions first .. first + nd - 1 with
+// `label`.  A packed variable-length tensor takes its row count (dimension 1)
+// from cu[batch] on the device.
+struct Outputs {
+  bool on = env_on("ATTN_CHECK_FINITE");
+  int n = 0;
+  char name[attn::kMaxFiniteViews][24];
+  const char* label[attn::kMaxFiniteViews];
+  int first[attn::kMaxFiniteViews], nd[attn::kMaxFiniteViews];
+  const int32_t* cu[attn::kMaxFiniteViews];
+  int cu_batch[attn::kMaxFiniteViews];
+  attn::FiniteView v[attn::kMaxFiniteViews];
+
+  void add(const char* nm, const char* lab, int first_dim, int n_dims, const void* p, bool f32,
+           const int64_t (&dims)[4], const int64_t (&st)[4], bool neg_inf_ok, const int32_t* cu_rows = nullptr,
+           int batch = 0) {
+    if (!on || n >= attn::kMaxFiniteViews || !p) return;
+    snprintf(name[n], sizeof name[n], "%s", nm);
+    label[n] = lab;
+    first[n] = first_dim;
+    nd[n] = n_dims;
+    cu[n] = cu_rows;
+    cu_batch[n] = batch;
+    attn::FiniteView& f = v[n++];
+    f.ptr = p;
+    for (int k = 0; k < 4; ++k) f.n[k] = dims[k], f.st[k] = st[k];
+    f.f32 = f32;
+    f.allow_neg_inf = neg_inf_ok;
+  }
+  // A [batch, seq, heads, head_dim] tensor with three element strides; packed
+  // (cu_rows != NULL): [rows, heads, head_dim], batch stride ignored.
+  void bshd(const char* nm, const void* p, uint32_t dtype, int64_t b, int64_t sq, int64_t h, int64_t d,
+            const int64_t* st, const int32_t* cu_rows = nullptr) {
+    if (cu_rows)
+      add(nm, "(row, head, dim)", 1, 3, p, dtype == ATTN_DTYPE_F32, {1, 0, h, d}, {0, st[1], st[2], 1}, false,
+          cu_rows, (int)b);
+    else
+      add(nm, "(batch, seq, head, dim)", 0, 4, p, dtype == ATTN_DTYPE_F32, {b, sq, h, d}, {st[0], st[1], st[2], 1},
+          false);
+  }
+  // LSE, contiguous [batch, heads, seq] fp32 (packed: [rows, heads]); -inf is allowed.
+  void lse(const float* p, int64_t b, int64_t h, int64_t sq, const int32_t* cu_rows = nullptr) {
+    if (cu_rows)
+      add("lse", "(row, head)", 1, 2, p, true, {1, 0, h, 1}, {0, h, 1, 0}, true, cu_rows, (int)b);
+    else
+      add("lse", "(batch, head, seq)", 0, 3, p, true, {b, h, sq, 1}, {h * sq, sq, 1, 0}, true);
+  }
+  // A decode output o [rows, heads, head_dim] (strides o_st) and lse [rows, heads].
+  void decode(const char* rows_name, const void* o, const int64_t* o_st, const float* l, int64_t rows, int64_t h,
+              int64_t d) {
+    const bool q = rows_name[0] == 'q';
+    add("o", q ? "(query, head, dim)" : "(batch, head, dim)", 1, 3, o, false, {1, rows, h, d},
+        {0, o_st[0], o_st[1], 1}, false);
+    add("lse", q ? "(query, head)" : "(batch, head)", 1, 2, l, true, {1, rows, h, 1}, {0, h, 1, 0}, true);
+  }
+};
+
+// Success of a compute call: its work is enqueued on `stream`.
+//  - With the environment variable ATTN_DEBUG_SYNC set (to anything but "0"),
+//    the call first waits for the stream, so a failure of its kernels is
+//    reported here, by the call that caused it, instead of at the caller's
+//    next synchronisation.
+//  - With ATTN_CHECK_FINITE set (likewise), the call scans the outputs it wrote
+//    after its kernels, waits, and returns ATTN_ERR_NONFINITE naming the first
+//    NaN or infinity it finds (an LSE of -inf is a row with no visible key and
+//    is allowed).  A running result read with ATTN_FWD_ACCUMULATE is scanned
+//    as part of the output it becomes.
+// Both are read on every call.
+int enqueued(void* stream, const char* call, const Outputs* outs = nullptr) {
+  hipStream_t s = (hipStream_t)stream;
+  if (env_on("ATTN_DEBUG_SYNC")) {
+    const hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s (ATTN_DEBUG_SYNC): HIP error %d (%s)", call, (int)e,
+                                     hipGetErrorString(e));
+  }
+  if (outs && outs->on && outs->n > 0) {
+    attn::FiniteView v[attn::kMaxFiniteViews];
+    int64_t first[attn::kMaxFiniteViews];
+    for (int i = 0; i < outs->n; ++i) {
+      v[i] = outs->v[i];
+      if (outs->cu[i]) {
+        int32_t rows = 0;
+        hipError_t e = hipMemcpyAsync(&rows, outs->cu[i] + outs->cu_batch[i], sizeof rows, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s (ATTN_CHECK_FINITE): HIP error %d (%s)", call, (int)e,
+                                         hipGetErrorString(e));
+        v[i].n[1] = rows > 0 ? rows : 0;
+      }
+    }
+    const hipError_t e = attn::finite_scan(v, outs->n, s, first);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s (ATTN_CHECK_FINITE): HIP error %d (%s)", call, (int)e,
+                                     hipGetErrorString(e));
+    for (int i = 0; i < outs->n; ++i) {
+      if (first[i] < 0) continue;
+      int64_t idx[4], r = first[i];
+      for (int k = 3; k >= 0; --k) idx[k] = r % v[i].n[k], r /= v[i].n[k];
+      char at[96];
+      int len = snprintf(at, sizeof at, "(");
+      for (int k = 0; k < outs->nd[i]; ++k)
+        len += snprintf(at + len, sizeof at - len, k ? ", %lld" : "%lld", (long long)idx[outs->first[i] + k]);
+      snprintf(at + len, sizeof at - len, ")");
+      return fail(ATTN_ERR_NONFINITE, "%s: non-finite value in %s at %s = %s", call, outs->name[i], outs->label[i], at);
+    }
   }
   return ok();
 }
@@ -159,6 +260,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported";
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP error";
+    case ATTN_ERR_NONFINITE: return "non-finite output (ATTN_CHECK_FINITE)";
     default: return "unknown status";
   }
 }
@@ -235,7 +337,13 @@ int attn_fwd_partial(const attn_fwd_args* a, void* stream) {
   log_call("attn_fwd_partial dtype=%u batch=%d heads_q=%d heads_kv=%d seqlen_q=%d seqlen_k=%d head_dim=%d causal=%d "
            "flags=0x%x varlen=%d stream=%p", a->dtype, a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k,
            a->head_dim, a->causal, a->flags, a->cu_seqlens_q != nullptr, stream);
-  return enqueued(stream, "attn_fwd_partial (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  const int32_t* cu_q = varlen ? a->cu_seqlens_q : nullptr;
+  outs.bshd("o", a->o, a->o_dtype, a->batch, a->seqlen_q, a->heads_q, a->head_dim, a->o_stride, cu_q);
+  outs.lse(a->lse, a->batch, a->heads_q, a->seqlen_q, cu_q);
+  outs.bshd("o_final", a->o_final, ATTN_DTYPE_BF16, a->batch, a->seqlen_q, a->heads_q, a->head_dim,
+            a->o_final_stride, cu_q);
+  return enqueued(stream, "attn_fwd_partial", &outs);
 }
 
 int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
@@ -320,7 +428,12 @@ int attn_fwd_chunks(const attn_fwd_chunks_args* a, void* stream) {
   log_call("attn_fwd_chunks batch=%d heads_q=%d heads_kv=%d seqlen_q=%d head_dim=%d n_chunks=%d causal=%d flags=0x%x "
            "stream=%p", a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->head_dim, a->n_chunks, a->causal, a->flags,
            stream);
-  return enqueued(stream, "attn_fwd_chunks (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  outs.bshd("o", a->o, a->o_dtype, a->batch, a->seqlen_q, a->heads_q, a->head_dim, a->o_stride);
+  outs.lse(a->lse, a->batch, a->heads_q, a->seqlen_q);
+  outs.bshd("o_final", a->o_final, ATTN_DTYPE_BF16, a->batch, a->seqlen_q, a->heads_q, a->head_dim,
+            a->o_final_stride);
+  return enqueued(stream, "attn_fwd_chunks", &outs);
 }
 
 int attn_merge_lse(const attn_merge_args* a, void* stream) {
@@ -367,7 +480,10 @@ int attn_merge_lse(const attn_merge_args* a, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "attn_merge_lse launch");
   log_call("attn_merge_lse n_parts=%d batch=%d seqlen=%d heads=%d head_dim=%d mode=%u stream=%p", a->n_parts, a->batch,
            a->seqlen, a->heads, a->head_dim, a->mode, stream);
-  return enqueued(stream, "attn_merge_lse (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  outs.bshd("o_out", a->o_out, a->o_out_dtype, a->batch, a->seqlen, a->heads, a->head_dim, a->o_out_stride);
+  outs.lse(a->lse_out, a->batch, a->heads, a->seqlen);
+  return enqueued(stream, "attn_merge_lse", &outs);
 }
 
 int attn_bwd(const attn_bwd_args* a, void* stream) {
@@ -460,7 +576,17 @@ int attn_bwd(const attn_bwd_args* a, void* stream) {
   log_call("attn_bwd dtype=%u batch=%d heads_q=%d heads_kv=%d seqlen_q=%d seqlen_k=%d head_dim=%d causal=%d flags=0x%x "
            "varlen=%d stream=%p", a->dtype, a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->seqlen_k, a->head_dim,
            a->causal, a->flags, a->cu_seqlens_q != nullptr, stream);
-  return enqueued(stream, "attn_bwd (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  const int32_t* cu_q = varlen ? a->cu_seqlens_q : nullptr;
+  const int32_t* cu_k = varlen ? a->cu_seqlens_k : nullptr;
+  if (has_q) {
+    const int64_t acc_st[3] = {(int64_t)a->seqlen_q * a->heads_q * D, (int64_t)a->heads_q * D, D};
+    outs.bshd("dq_acc", a->dq_acc, ATTN_DTYPE_F32, a->batch, a->seqlen_q, a->heads_q, D, acc_st, cu_q);
+    if (finalize) outs.bshd("dq", a->dq, a->dtype, a->batch, a->seqlen_q, a->heads_q, D, a->dq_stride, cu_q);
+  }
+  outs.bshd("dk", a->dk, a->dtype, a->batch, a->seqlen_k, a->heads_kv, D, a->dk_stride, cu_k);
+  outs.bshd("dv", a->dv, a->dtype, a->batch, a->seqlen_k, a->heads_kv, D, a->dv_stride, cu_k);
+  return enqueued(stream, "attn_bwd", &outs);
 }
 
 int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
@@ -576,7 +702,23 @@ int attn_bwd_chunks(const attn_bwd_chunks_args* a, void* stream) {
   log_call("attn_bwd_chunks batch=%d heads_q=%d heads_kv=%d seqlen_q=%d head_dim=%d n_chunks=%d causal=%d flags=0x%x "
            "stream=%p", a->batch, a->heads_q, a->heads_kv, a->seqlen_q, a->head_dim, a->n_chunks, a->causal, a->flags,
            stream);
-  return enqueued(stream, "attn_bwd_chunks (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  const int D = a->head_dim;
+  if (has_q) {
+    const int64_t acc_st[3] = {(int64_t)a->seqlen_q * a->heads_q * D, (int64_t)a->heads_q * D, D};
+    outs.bshd("dq_acc", a->dq_acc, ATTN_DTYPE_F32, a->batch, a->seqlen_q, a->heads_q, D, acc_st);
+    if (finalize) outs.bshd("dq", a->dq, a->dtype, a->batch, a->seqlen_q, a->heads_q, D, a->dq_stride);
+  }
+  for (int c = 0; c < ct.kv.n; ++c) {
+    const int64_t dks[3] = {ct.dkb[c], a->dk_stride[1], a->dk_stride[2]};
+    const int64_t dvs[3] = {ct.dvb[c], a->dv_stride[1], a->dv_stride[2]};
+    char name[24];
+    snprintf(name, sizeof name, "dk (chunk entry %d)", c);
+    outs.bshd(name, ct.dk[c], a->dtype, a->batch, ct.kv.len[c], a->heads_kv, D, dks);
+    snprintf(name, sizeof name, "dv (chunk entry %d)", c);
+    outs.bshd(name, ct.dv[c], a->dtype, a->batch, ct.kv.len[c], a->heads_kv, D, dvs);
+  }
+  return enqueued(stream, "attn_bwd_chunks", &outs);
 }
 
 }  // extern "C"
@@ -718,7 +860,9 @@ int attn_decode_tree(const attn_decode_tree_args* a, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "attn_decode_tree launch");
   log_call("attn_decode_tree n_queries=%d heads_q=%d heads_kv=%d head_dim=%d n_nodes=%d segments=%d stream=%p",
            a->n_queries, a->heads_q, a->heads_kv, a->head_dim, a->n_nodes, tt.n, stream);
-  return enqueued(stream, "attn_decode_tree (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  outs.decode("query", a->o, a->o_stride, a->lse, a->n_queries, a->heads_q, a->head_dim);
+  return enqueued(stream, "attn_decode_tree", &outs);
 }
 
 size_t attn_bwd_workspace_size(int32_t batch, int32_t heads_q, int32_t seqlen_q) {
@@ -814,7 +958,9 @@ static int decode_splitkv(const attn_decode_args* a, void* stream, bool noalloc)
   log_call("%s batch=%d heads_q=%d heads_kv=%d head_dim=%d cache_len=%lld n_splits=%d seqlens=%d streamk=%d stream=%p",
            noalloc ? "attn_decode_splitkv_noalloc" : "attn_decode_splitkv", a->batch, a->heads_q, a->heads_kv,
            a->head_dim, (long long)a->cache_len, a->n_splits, a->seqlens != nullptr, p.streamk, stream);
-  return enqueued(stream, noalloc ? "attn_decode_splitkv_noalloc (ATTN_DEBUG_SYNC)" : "attn_decode_splitkv (ATTN_DEBUG_SYNC)");
+  Outputs outs;
+  outs.decode("batch", a->o, a->o_stride, a->lse, a->batch, a->heads_q, a->head_dim);
+  return enqueued(stream, noalloc ? "attn_decode_splitkv_noalloc" : "attn_decode_splitkv", &outs);
 }
 
 int attn_decode_splitkv(const attn_decode_args* a, void* stream) { return decode_splitkv(a, stream, false); }

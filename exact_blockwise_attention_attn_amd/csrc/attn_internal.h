@@ -197,4 +197,20 @@ hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_tree_decode(const FwdParams& p, const TreeTable& t, int n_q, void* out_o, int64_t out_o_sq,
                               int64_t out_o_sh, float* out_lse, int D, hipStream_t s);
 
+// Debug scan of a call's outputs for non-finite values.  A view is up to four
+// dimensions n[0..3] with element strides st[0..3] (unused dimensions have
+// n = 1); the flat index of an element is row-major over n.
+struct FiniteView {
+  const void* ptr;
+  int64_t n[4];
+  int64_t st[4];
+  int f32;            // element type fp32 (else bf16)
+  int allow_neg_inf;  // -inf is a legitimate value (the LSE of a row with no visible key)
+};
+constexpr int kMaxFiniteViews = 2 * kMaxChunks + 4;
+// Scans the views on s and waits for s; first[i] is the flat index of view i's
+// first NaN or infinity (-inf excepted where allowed), or -1 if it has none.
+// Calls are serialised within the process (they share one device buffer).
+hipError_t finite_scan(const FiniteView* v, int n, hipStream_t s, int64_t* first);
+
 }  // namespace attn

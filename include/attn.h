@@ -46,7 +46,17 @@
  *     debugging, the environment variable ATTN_DEBUG_SYNC (set, and not "0";
  *     read on every call) makes each compute call wait for `stream` before it
  *     returns, so that a failure of its kernels is returned as ATTN_ERR_HIP by
- *     the call itself.
+ *     the call itself.  ATTN_CHECK_FINITE (set, and not "0"; read on every
+ *     call) makes each compute call scan the outputs it wrote (o, lse, o_final,
+ *     dq_acc, dq, dk, dv) after its kernels, wait for `stream`, and return
+ *     ATTN_ERR_NONFINITE if one holds a NaN or an infinity, naming the tensor
+ *     and the index of the first such element in attn_last_error().  An LSE of
+ *     -inf (a row with no visible key) is not an error.  NaN inputs propagate
+ *     to the outputs that depend on them (see the definitions above), so this
+ *     also reports non-finite inputs where they are read.  The scan shares one
+ *     small device buffer per device; checked calls are serialised within the
+ *     process.  ATTN_LOG (set, and not "0") writes one line to stderr per
+ *     enqueued call, naming the call and its sizes.
  *   - Every argument is checked on the host before anything is enqueued; on
  *     error the call returns a nonzero status, enqueues nothing, leaves every
  *     output untouched and records a message for attn_last_error().  This
@@ -56,9 +66,13 @@
  *   - Argument structs start with struct_size = sizeof(the struct).
  *   - head_dim must be 64 or 128.  Scale 0 means 1/sqrt(head_dim); otherwise it
  *     must be finite and positive.
- *   - The library keeps no mutable global state; calls are thread-safe.
- *   - Scratch memory is always caller-provided (a workspace argument sized by
- *     attn_*_workspace_size); the library never allocates.
+ *   - The library keeps no mutable global state apart from two fixed device
+ *     buffers (the scratch of attn_decode_splitkv_noalloc and the result
+ *     buffer of the ATTN_CHECK_FINITE scan); calls are thread-safe, except
+ *     that attn_decode_splitkv_noalloc calls overlapping on one device race.
+ *   - Scratch memory is caller-provided (a workspace argument sized by
+ *     attn_*_workspace_size), apart from the two fixed buffers above; the
+ *     library never allocates.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -76,7 +90,7 @@ extern "C" {
 #define ATTN_API
 #endif
 
-#define ATTN_ABI_VERSION 9
+#define ATTN_ABI_VERSION 10
 
 /* Status codes. */
 #define ATTN_OK 0
@@ -84,6 +98,7 @@ extern "C" {
 #define ATTN_ERR_UNSUPPORTED 2 /* valid request outside what is built (head_dim, dtype, alignment) */
 #define ATTN_ERR_WORKSPACE 3   /* workspace missing or too small */
 #define ATTN_ERR_HIP 4         /* a HIP launch failed; attn_last_error() holds the HIP message */
+#define ATTN_ERR_NONFINITE 5   /* ATTN_CHECK_FINITE found a NaN or infinity in an output */
 
 /* Element types. */
 #define ATTN_DTYPE_F32 0

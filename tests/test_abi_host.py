@@ -110,9 +110,10 @@ def test_header_constants_match_binding():
 
 
 def test_helpers(lib):
-    assert lib.attn_abi_version() == 9
+    assert lib.attn_abi_version() == 10
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(3) == b"workspace missing or too small"
+    assert lib.attn_status_string(5) == b"non-finite output (ATTN_CHECK_FINITE)"
     assert lib.attn_status_string(99) == b"unknown status"
     # O partials [16, 32, 64, 128] fp32 + LSE [16, 32, 64] fp32, each rounded up to 256 bytes.
     # batch x heads_q x (n_splits + 1) rows of head_dim + 1 floats (the stream-K pieces fit in the extra row).
@@ -563,3 +564,12 @@ def test_log_only_on_enqueue(lib, monkeypatch, capfd):
     a = bwd_args(dq_acc=None)
     assert lib.attn_bwd(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
     assert "[attn]" not in capfd.readouterr().err
+
+
+def test_check_finite_keeps_host_validation(lib, monkeypatch):
+    """With ATTN_CHECK_FINITE set, invalid calls are still rejected on the host before any scan (the fake
+    pointers are never touched)."""
+    monkeypatch.setenv("ATTN_CHECK_FINITE", "1")
+    a = bwd_args(dq_acc=None)
+    assert lib.attn_bwd(ctypes.byref(a), None) == B.ATTN_ERR_INVALID_ARG
+    assert "dq_acc" in lib.attn_last_error().decode()

@@ -683,6 +683,53 @@ def test_nan_propagates_other_paths():
             assert torch.equal(o1, o0) and torch.equal(l1, l0)
 
 
+
+def test_check_finite_reports(monkeypatch):
+    """ATTN_CHECK_FINITE: clean calls return normally with unchanged results; a NaN input makes the call that
+    writes the first non-finite output fail with ATTN_ERR_NONFINITE, naming the tensor and the index."""
+    log("ATTN_CHECK_FINITE")
+    (q, k, v), _ = _inputs(120, 1, 192, 192, 2, 2, 128, "bf16")
+    do, _ = seq_tensor(120, 3, 1, 192, 2, 128, "bf16")
+    o0, l0 = shard.causal_attention_forward(q, k, v)
+    g0 = shard.causal_attention_backward(q, k, v, o0, do, l0)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("ATTN_CHECK_FINITE", "1")
+    # Clean inputs (fully masked rows give LSE -inf, which is allowed): no error, same bits.
+    o1, l1 = shard.causal_attention_forward(q, k, v)
+    g1 = shard.causal_attention_backward(q, k, v, o1, do, l1)
+    for a, b in zip((o0, l0, *g0), (o1, l1, *g1)):
+        assert torch.equal(a, b)
+    lm = torch.empty((1, 2, 192), dtype=torch.float32, device="cuda")
+    om = torch.empty((1, 192, 2, 128), dtype=torch.float32, device="cuda")
+    B.attn_fwd_partial(q, k, v, om, lm, q_pos0=0, k_pos0=150, causal=True)  # rows 0..149 see no key
+    assert torch.isinf(lm[0, :, :150]).all()
+    # A NaN key (row 100, head 1): the forward reports o at the first row that sees it.
+    k2 = k.clone()
+    k2[0, 100, 1, 5] = float("nan")
+    with pytest.raises(B.AttnError) as ei:
+        shard.causal_attention_forward(q, k2, v)
+    assert ei.value.status == B.ATTN_ERR_NONFINITE
+    assert "attn_fwd_partial: non-finite value in o at (batch, seq, head, dim) = (0, 100, 1, 0)" in str(ei.value)
+    # A NaN in dout (row 7, head 0): the backward reports dq_acc at the first row that holds one.
+    do2 = do.clone()
+    do2[0, 7, 0, 3] = float("nan")
+    with pytest.raises(B.AttnError) as ei:
+        shard.causal_attention_backward(q, k, v, o0, do2, l0)
+    assert ei.value.status == B.ATTN_ERR_NONFINITE
+    assert "attn_bwd: non-finite value in dq_acc at (batch, seq, head, dim) = (0, 7, 0, 0)" in str(ei.value)
+    # Decode over a cache with one NaN value element (key 30, head 0, dim 9): o of query head 0 at dim 9.
+    qd = q[:, 0].contiguous()
+    v2 = v.clone()
+    v2[0, 30, 0, 9] = float("nan")
+    od = torch.empty_like(qd)
+    ld = torch.empty((1, 2), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.attn_decode_workspace_size(1, 2, 128, 4), dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.AttnError) as ei:
+        B.attn_decode_splitkv(qd, k, v2, od, ld, ws, n_splits=4)
+    assert "attn_decode_splitkv: non-finite value in o at (batch, head, dim) = (0, 0, 9)" in str(ei.value)
+    monkeypatch.delenv("ATTN_CHECK_FINITE")
+
+
 # (B, Hq, Hkv, L, D, n_splits, seqlens)
 DECODE_CASES = [
     (2, 8, 2, 1000, 128, 8, None),
