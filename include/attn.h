@@ -27,6 +27,10 @@
  *   s_ij = scale * q_i . k_j, LSE_i = ln sum_{visible j} exp(s_ij) (natural log),
  *   O_i = sum_{visible j} exp(s_ij - LSE_i) v_j.
  *   A row with no visible key has O_i = 0 and LSE_i = -inf (the merge identity).
+ *   NaN propagates as in these formulas: a NaN score that a row sees makes the
+ *   row's O and LSE NaN, and a key a row does not see never enters its softmax.
+ *   (A non-finite value row that the causal mask hides but that shares a
+ *   64-key tile with keys the row sees reaches the row's O through 0 * NaN.)
  *
  * Conventions shared by every entry point:
  *   - Tensors of shape [batch, seq, heads, head_dim] are given by a base pointer
@@ -228,7 +232,8 @@ ATTN_API int attn_fwd_chunks(const attn_fwd_chunks_args* args, void* stream);
  * (element strides o_stride) and LSE_c [batch, heads, seqlen] fp32 at
  * lse_parts + c * lse_part_stride.  With m = max_c LSE_c:
  * LSE = m + ln sum_c exp(LSE_c - m) and O = sum_c exp(LSE_c - LSE) O_c; parts
- * with LSE_c = -inf contribute nothing and an all -inf row gives O = 0, LSE = -inf.
+ * with LSE_c = -inf contribute nothing and an all -inf row gives O = 0, LSE = -inf;
+ * a NaN LSE_c makes the row's O and LSE NaN.
  * o_out may be fp32 or bf16; it may alias part 0 exactly (same pointer and
  * strides, fp32), and lse_out may alias part 0's LSE.  No other overlap.
  */
