@@ -16,6 +16,10 @@ Prints one JSON line.  Besides the contract fields it carries:
                 FLOP/clk x maximum shader clock), beside the published 2.5 PFLOP/s
                 that the fractions use;
   kernels       per-call timings (forward call, backward call);
+  device_state  socket power and shader clocks (amd-smi samples) over a window of
+                the same steps after the timed ones, with that window's
+                throughput: the MFMA kernels run at the chip's power limit, so
+                their speed follows the clock it holds, which varies by box;
   secondary     the other workloads: the 128K sequence shard forward over 32
                 chunks, its backward, and split-KV GQA decode (GB/s of K/V,
                 also as a fraction of a plain 1 GiB device copy's bandwidth);
@@ -137,7 +141,91 @@ def bench_main(args, stream):
 
         (t_fu, t_bu), _ = time_calls([fwd_u, bwd_u], max(2, args.steps // 3), 1, stream)
         res["unbalanced"] = {"fwd_ms": t_fu, "bwd_ms": t_bu}
+        # The chip's socket power and shader clocks under the same steps, in a window of their own
+        # after the timed ones: the MFMA rates follow the clock the chip holds at its power limit,
+        # which differs from box to box.
+        res["device_state"] = sustained_device_state([fwd, bwd], f_fwd + f_bwd, stream)
     return res
+
+
+def parse_smi_metric_csv(text):
+    """(socket power W, [shader clock MHz of each XCD]) of every data row of `amd-smi metric -p -c --csv`."""
+    rows, header = [], None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split(",")]
+        if not line.strip():
+            continue
+        if cells[0] == "gpu":
+            header = cells
+            continue
+        if header is None or len(cells) != len(header):
+            continue
+        rec = dict(zip(header, cells))
+        try:
+            power = float(rec["socket_power"])
+        except (KeyError, ValueError):
+            continue
+        clocks = []
+        for name, val in rec.items():
+            parts = name.split("_")
+            if len(parts) == 3 and parts[0] == "gfx" and parts[2] == "clk":
+                try:
+                    clocks.append(float(val))
+                except ValueError:
+                    pass
+        rows.append((power, clocks))
+    return rows
+
+
+def sustained_device_state(fns, flops_step, stream, seconds=4.0):
+    """Repeat the step for `seconds` while `amd-smi` samples socket power and shader clocks
+    (None if amd-smi is not available); also the throughput over the same window."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                out = subprocess.run([smi, "metric", "-p", "-c", "--csv"], capture_output=True, text=True,
+                                     timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            samples.extend(parse_smi_metric_csv(out))
+            stop.wait(0.25)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    torch.cuda.synchronize()
+    th.start()
+    t0, steps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        steps += 1
+    elapsed = time.perf_counter() - t0
+    stop.set()
+    th.join(timeout=15)
+    # The first sample can predate the load; keep those taken under it (above half the busiest power).
+    busy = [x for x in samples if samples and x[0] > 0.5 * max(p for p, _ in samples)]
+    if not busy:
+        return None
+    power = sorted(p for p, _ in busy)
+    clocks = sorted(c for _, cs in busy for c in cs)
+
+    def stats(v):
+        return {"min": v[0], "median": v[len(v) // 2], "max": v[-1]}
+
+    return {"samples": len(busy), "window_s": round(elapsed, 2), "steps": steps,
+            "tflops": round(flops_step * steps / elapsed / 1e12, 1), "socket_power_w": stats(power),
+            "shader_clock_mhz": stats(clocks) if clocks else None}
 
 
 def bench_shard(args, stream, do_bwd):
@@ -578,6 +666,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_bwd call (statistics + dK/dV + dQ kernels)",
                      "achieved": round(bwd_achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": BWD_CALL_HBM_BYTES},
+        "device_state": m.get("device_state"),
         "kernels": {"fwd_call_ms": round(m["fwd_ms"], 3), "bwd_call_ms": round(m["bwd_ms"], 3),
                     "fwd_tflops": round(m["fwd_tflops"], 2), "bwd_tflops": round(m["bwd_tflops"], 2),
                     "event_ms_per_step": round(m["event_ms"], 3),

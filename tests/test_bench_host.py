@@ -38,3 +38,14 @@ def test_host_facts():
     assert facts["affinity_cores"] == len(os.sched_getaffinity(0))
     assert isinstance(facts["cpu_model"], str) and facts["cpu_model"]
     assert isinstance(facts["blas"], list)
+
+
+def test_smi_metric_parse():
+    """The amd-smi CSV reader takes socket power and the per-XCD shader clocks (not their limits), skips
+    repeated headers, blank lines and rows whose power is not a number."""
+    b = _bench_module()
+    hdr = "gpu,socket_power,gfx_voltage,gfx_0_clk,gfx_0_min_clk,gfx_0_max_clk,gfx_1_clk,gfx_1_min_clk,mem_0_clk"
+    text = "\n".join([hdr, "0,250,N/A,157,142,2400,158,142,2000", "", hdr, "0,1343,N/A,1894,500,2400,1787,500,2000",
+                      "0,N/A,N/A,1,2,3,4,5,6", "0,1350,N/A,1900"])
+    assert b.parse_smi_metric_csv(text) == [(250.0, [157.0, 158.0]), (1343.0, [1894.0, 1787.0])]
+    assert b.parse_smi_metric_csv("") == []
