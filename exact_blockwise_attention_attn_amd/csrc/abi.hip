@@ -771,7 +771,6 @@ bool tree_table(const attn_decode_tree_args* a, attn::TreeTable* tt, int64_t* en
       tt->q_end[e] = a->q_end[n];
       tt->e0[e] = (int)*entries;
       *entries += a->q_end[n] - a->q_begin[n];
-      tt->max_q = std::max(tt->max_q, a->q_end[n] - a->q_begin[n]);
     }
   }
   if (*entries > 0x7fffffffLL / std::max(1, a->heads_q)) {

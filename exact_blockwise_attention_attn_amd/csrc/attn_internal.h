@@ -120,8 +120,10 @@ struct TreeTable {
   int kv_len[kMaxTreeNodes];
   int q_begin[kMaxTreeNodes], q_end[kMaxTreeNodes];
   int e0[kMaxTreeNodes];
+  // Row tiles of the per-segment pass before segment i (filled by the launcher):
+  // segment i owns tiles u0[i] .. u0[i + 1] - 1, one per 128 rows it holds.
+  int u0[kMaxTreeNodes + 1];
   int n;
-  int max_q;  // most queries of any node
 };
 
 struct DecodeParams {

@@ -345,20 +345,43 @@ __global__ __launch_bounds__(NT, 2) void fwd_varlen_kernel(FwdParams p) {
 // forward, and writes a partial (O, LSE) per (node, query, head).  Pass 2
 // merges each query's partials in node order.
 
+//
+// The grid holds only tiles that have rows: (segment, row tile) pairs are
+// numbered through the prefix u0, in segment order, so the long tiles of the
+// nodes near the root are dispatched first and no workgroup exits empty.  (A
+// grid padded to the largest node's tile count interleaves empty workgroups
+// with live ones; the dispatcher then spreads the live ones unevenly over the
+// shader engines, and leaf tiles waited for the root's to finish instead of
+// taking the CUs' free slots.)  Key/value heads go round the XCDs.
 template <int D>
 __global__ __launch_bounds__(NT, 2) void tree_fwd_kernel(FwdParams p, TreeTable tt) {
   __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 v0s[SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 k1s[SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 v1s[SwTile<D>::SIZE];
-  const SeqHeadUnit w = varlen_order(blockIdx.x, p.Hkv, p.n_units);
-  const int n = w.b, hk = w.h, unit = w.unit;
+  constexpr int kXcd = 8;
+  const int bid = blockIdx.x;
+  int hk, idx;
+  if (p.Hkv % kXcd == 0) {
+    const int hpx = p.Hkv / kXcd, s_ = bid / kXcd;
+    hk = (s_ % hpx) * kXcd + bid % kXcd;
+    idx = s_ / hpx;
+  } else {
+    hk = bid % p.Hkv;
+    idx = bid / p.Hkv;
+  }
+  int n = 0, hi = tt.n - 1;  // the segment holding tile idx: the last n with u0[n] <= idx
+  while (n < hi) {
+    const int mid = (n + hi + 1) >> 1;
+    if (tt.u0[mid] <= idx) n = mid;
+    else hi = mid - 1;
+  }
+  const int unit = idx - tt.u0[n];
   const int h0 = hk * p.group;
   FwdParams s = p;
   s.Sq = (tt.q_end[n] - tt.q_begin[n]) * p.group;  // rows: (query, head in group)
   s.Sk = tt.kv_len[n];
   s.n_qtiles = (s.Sq + BM - 1) / BM;
-  if (unit >= s.n_qtiles) return;
   s.o.ptr = (float*)p.o.ptr + (int64_t)tt.e0[n] * p.o.ss;
   s.lse = p.lse + (int64_t)tt.e0[n] * p.lse_ss;
   const u16* qb = (const u16*)p.q.ptr + (int64_t)tt.q_begin[n] * p.q.ss + (int64_t)h0 * p.q.sh;
@@ -574,9 +597,19 @@ int64_t items_fwd_bf16(const FwdParams& p) {
   return (int64_t)p.B * p.Hq * n_units * NT;
 }
 
+// Row tiles of the tree pass over all segments; with u0, fills the prefix.
+static int64_t tree_tiles(const TreeTable& tt, int group, int* u0) {
+  int64_t t = 0;
+  for (int i = 0; i < tt.n; ++i) {
+    if (u0) u0[i] = (int)t;
+    t += ((int64_t)(tt.q_end[i] - tt.q_begin[i]) * group + BM - 1) / BM;
+  }
+  if (u0) u0[tt.n] = (int)t;
+  return t;
+}
+
 int64_t items_tree_decode(const FwdParams& p, const TreeTable& tt, int n_q, int D) {
-  const int64_t n_units = ((int64_t)tt.max_q * p.group + BM - 1) / BM;
-  return std::max<int64_t>((int64_t)tt.n * p.Hkv * n_units * NT, (int64_t)n_q * p.Hq * D);
+  return std::max<int64_t>(tree_tiles(tt, p.group, nullptr) * p.Hkv * NT, (int64_t)n_q * p.Hq * D);
 }
 
 hipError_t launch_fwd_chunks_bf16(const FwdParams& p0, const ChunkTable& ct, int D, hipStream_t s) {
@@ -615,13 +648,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
 hipError_t launch_tree_decode(const FwdParams& p0, const TreeTable& tt, int n_q, void* out_o, int64_t out_o_sq,
                               int64_t out_o_sh, float* out_lse, int D, hipStream_t s) {
   FwdParams p = p0;
-  p.n_units = (int)(((int64_t)tt.max_q * p.group + BM - 1) / BM);
-  const int64_t grid = (int64_t)tt.n * p.Hkv * p.n_units;
+  TreeTable t = tt;
+  const int64_t grid = tree_tiles(t, p.group, t.u0) * p.Hkv;
   if (grid > 0) {
     if (D == 128)
-      hipLaunchKernelGGL(tree_fwd_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, tt);
+      hipLaunchKernelGGL(tree_fwd_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, t);
     else
-      hipLaunchKernelGGL(tree_fwd_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, tt);
+      hipLaunchKernelGGL(tree_fwd_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
