@@ -403,6 +403,27 @@ def attn_merge_lse(o_parts, lse_parts, o_out, lse_out, *, tree=False, stream=Non
     _check(load().attn_merge_lse(ctypes.byref(a), _stream(stream)))
 
 
+def attn_merge_lse_pair(o_a, lse_a, o_b, lse_b, o_out, lse_out, *, tree=False, stream=None) -> None:
+    """Two partials in separate buffers (fp32 o [B,S,H,D] with equal strides, lse [B,H,S] contiguous), merged
+    as parts 0 (a) and 1 (b): the part strides are the buffers' distance in elements, negative if b lies
+    below a."""
+    assert o_a.dtype == o_b.dtype == torch.float32 and o_a.shape == o_b.shape and o_a.stride() == o_b.stride()
+    assert lse_a.shape == lse_b.shape and lse_a.is_contiguous() and lse_b.is_contiguous()
+    do, dl = o_b.data_ptr() - o_a.data_ptr(), lse_b.data_ptr() - lse_a.data_ptr()
+    assert do % 4 == 0 and dl % 4 == 0
+    B, S, H, D = o_a.shape
+    a = MergeArgs()
+    a.struct_size = ctypes.sizeof(MergeArgs)
+    a.n_parts, a.batch, a.seqlen, a.heads, a.head_dim = 2, B, S, H, D
+    a.o_parts, a.o_part_stride = _ptr(o_a), do // 4
+    a.o_stride = I64x3(o_a.stride(0), o_a.stride(1), o_a.stride(2))
+    a.lse_parts, a.lse_part_stride = _ptr(lse_a), dl // 4
+    a.o_out, a.o_out_stride, a.o_out_dtype = _ptr(o_out), _strides3(o_out), _dtype_code(o_out)
+    a.lse_out = _ptr(lse_out)
+    a.mode = ATTN_MERGE_TREE if tree else ATTN_MERGE_SEQUENTIAL
+    _check(load().attn_merge_lse(ctypes.byref(a), _stream(stream)))
+
+
 def attn_bwd(q, k, v, o, dout, lse, workspace, dq_acc, dk, dv, *, dq=None, q_pos0=0, k_pos0=0, causal=False,
              scale=0.0, compute_delta=False, dq_overwrite=False, finalize_dq=False, balanced=False,
              deterministic=False, stream=None) -> None:

@@ -455,8 +455,8 @@ int attn_merge_lse(const attn_merge_args* a, void* stream) {
   if (any && (!a->lse_parts || !a->lse_out)) return fail(ATTN_ERR_INVALID_ARG, "lse_parts or lse_out is NULL");
   if (any && (!aligned16(a->lse_parts) || !aligned16(a->lse_out)))
     return fail(ATTN_ERR_UNSUPPORTED, "lse_parts or lse_out is not 16-byte aligned");
-  if (a->n_parts > 1 && (a->o_part_stride <= 0 || a->lse_part_stride <= 0))
-    return fail(ATTN_ERR_INVALID_ARG, "part strides must be positive");
+  if (a->n_parts > 1 && (a->o_part_stride == 0 || a->lse_part_stride == 0))
+    return fail(ATTN_ERR_INVALID_ARG, "part strides must be nonzero");
   if ((a->o_part_stride * 4) % 16) return fail(ATTN_ERR_UNSUPPORTED, "o_part_stride breaks 16-byte alignment");
   if (!any) return ok();
   attn::MergeParams p{};

@@ -234,6 +234,11 @@ ATTN_API int attn_fwd_chunks(const attn_fwd_chunks_args* args, void* stream);
  * LSE = m + ln sum_c exp(LSE_c - m) and O = sum_c exp(LSE_c - LSE) O_c; parts
  * with LSE_c = -inf contribute nothing and an all -inf row gives O = 0, LSE = -inf;
  * a NaN LSE_c makes the row's O and LSE NaN.
+ * The part strides are element offsets between consecutive parts (nonzero
+ * when n_parts > 1) and may be negative, so two partials in separate buffers A
+ * and B (same strides, both 16-byte aligned) are merged as a pair with
+ * o_parts = A and o_part_stride = B - A in fp32 elements (likewise for the
+ * LSE); this is the two-pointer form of the merge.
  * o_out may be fp32 or bf16; it may alias part 0 exactly (same pointer and
  * strides, fp32), and lse_out may alias part 0's LSE.  No other overlap.
  */

@@ -210,6 +210,8 @@ MERGE_BAD = [
     (dict(head_dim=32), B.ATTN_ERR_UNSUPPORTED, "head_dim"),
     (dict(lse_out=None), B.ATTN_ERR_INVALID_ARG, "NULL"),
     (dict(o_part_stride=0), B.ATTN_ERR_INVALID_ARG, "part strides"),
+    (dict(lse_part_stride=0), B.ATTN_ERR_INVALID_ARG, "part strides"),
+    (dict(o_part_stride=-6), B.ATTN_ERR_UNSUPPORTED, "o_part_stride"),
     (dict(o_out_dtype=9), B.ATTN_ERR_UNSUPPORTED, "o_out_dtype"),
     # One thread per 4 features: 2^20 rows x 1024 heads x 32 threads = 2^35 work-items.
     (dict(n_parts=1, seqlen=1 << 20, heads=1024, head_dim=128, o_stride=B.I64x3(0, 1024 * 128, 128),

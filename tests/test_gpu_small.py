@@ -237,6 +237,35 @@ def test_merge_kernel(n, tree, D):
     check("merge LSE aliased", l_parts[0], L_ref, 1e-5)
 
 
+
+def test_merge_pair_separate_buffers():
+    """The two-pointer form: two partials in separately allocated buffers merged through a part stride equal
+    to their distance (positive or negative), bit for bit as the same two parts stacked in one array."""
+    log("merge of two separate buffers")
+    Bn, S, H, D = 2, 45, 3, 128
+    rng = np.random.default_rng(123)
+    mk = lambda *sh: torch.from_numpy(rng.standard_normal(sh).astype(np.float32)).cuda()
+    o_a, o_b = mk(Bn, S, H, D), mk(Bn, S, H, D)
+    l_a, l_b = 3 * mk(Bn, H, S), 3 * mk(Bn, H, S)
+    l_b[0, 1, :7] = -float("inf")  # part b sees no key for these rows
+    o_b[0, :7, 1] = 0.0
+    for (x, lx), (y, ly) in (((o_a, l_a), (o_b, l_b)), ((o_b, l_b), (o_a, l_a))):
+        for tree in (False, True):
+            o1, l1 = torch.empty_like(o_a), torch.empty_like(l_a)
+            B.attn_merge_lse_pair(x, lx, y, ly, o1, l1, tree=tree)
+            o2, l2 = torch.empty_like(o_a), torch.empty_like(l_a)
+            B.attn_merge_lse(torch.stack([x, y]), torch.stack([lx, ly]), o2, l2, tree=tree)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert o_a.data_ptr() != o_b.data_ptr()  # so one of the two orders above has a negative part stride
+    O_ref, L_ref = oracle.merge([(to_np(o_a), to_np(l_a).transpose(0, 2, 1)), (to_np(o_b), to_np(l_b).transpose(0, 2, 1))])
+    o1, l1 = torch.empty_like(o_a), torch.empty_like(l_a)
+    B.attn_merge_lse_pair(o_a, l_a, o_b, l_b, o1, l1)
+    torch.cuda.synchronize()
+    check("pair merge O", o1, O_ref, 1e-5, scale_by_max=True)
+    check("pair merge LSE", l1, L_ref.transpose(0, 2, 1), 1e-5)
+
+
 # (Sq, Sk, D, causal, q_pos0, k_pos0, B, Hq, Hkv, dtype, balanced)
 BWD_CASES = [
     (1, 1, 128, False, 0, 0, 1, 1, 1, "bf16", False),
