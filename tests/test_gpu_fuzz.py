@@ -71,3 +71,140 @@ def test_fuzz_fwd_bwd(case):
     check("dQ", dq, dq_ref, tol or G_TOL, scale_by_max=True)
     check("dK", dk, dk_ref, tol or G_TOL, scale_by_max=True)
     check("dV", dv, dv_ref, tol or G_TOL, scale_by_max=True)
+
+
+def _decode_cases(n=24, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        Bn = int(rng.integers(1, 7))
+        L = int(rng.integers(1, 6001))
+        D = int(rng.choice([64, 128]))
+        ns = int(rng.integers(1, 301))
+        lens = None if i % 3 == 0 else [int(x) for x in rng.integers(0, L + 51, Bn)]
+        out.append((Bn, Hq, Hkv, L, D, ns, lens, i % 4 == 3))
+    return out
+
+
+DECODE_CASES = _decode_cases()
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(i) for i in range(len(DECODE_CASES))])
+def test_fuzz_decode(case):
+    Bn, Hq, Hkv, L, D, ns, lens, noalloc = case
+    log(f"fuzz decode {case}")
+    q, qh = seq_tensor(131, 0, Bn, 1, Hq, D, "bf16")
+    kc, kh = seq_tensor(131, 1, Bn, L, Hkv, D, "bf16")
+    vc, vh = seq_tensor(131, 2, Bn, L, Hkv, D, "bf16")
+    q, qh = q[:, 0], qh[:, 0]
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = oracle.decode(qh, kh, vh, scale, seqlens=None if lens is None else [min(x, L) for x in lens])
+    o = torch.full((Bn, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Bn, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    if noalloc and B.attn_decode_workspace_size(Bn, Hq, D, ns) <= 32 << 20:
+        B.attn_decode_splitkv_noalloc(q, kc, vc, o, lse, n_splits=ns, seqlens=sl)
+    else:
+        ws = torch.empty(B.attn_decode_workspace_size(Bn, Hq, D, ns), dtype=torch.uint8, device="cuda")
+        B.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=ns, seqlens=sl)
+    torch.cuda.synchronize()
+    check("decode O", o, O_ref, O_TOL, scale_by_max=True)
+    check("decode LSE", lse, L_ref, L_TOL)
+
+
+def _chunk_cases(n=16, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        Bn = int(rng.integers(1, 3))
+        Sq = int(rng.integers(1, 300))
+        D = int(rng.choice([64, 128]))
+        nc = int(rng.integers(1, 9))
+        lens = tuple(int(x) for x in rng.integers(0, 201, nc))
+        pos = tuple(int(x) for x in rng.integers(-200, 1200, nc))
+        qp = int(rng.integers(-100, 1000))
+        out.append((Bn, Sq, Hq, Hkv, D, lens, pos, qp, i % 4 != 0, bool(rng.integers(0, 2))))
+    return out
+
+
+CHUNK_CASES = _chunk_cases()
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[str(i) for i in range(len(CHUNK_CASES))])
+def test_fuzz_chunk_tables(case):
+    """attn_fwd_chunks and attn_bwd_chunks over random chunk tables (lengths 0..200, positions anywhere,
+    in any order) against the oracle's per-chunk attention merged, and its per-chunk backward from the
+    global O and LSE."""
+    from tests.test_gpu_small import _oracle_over_chunks
+
+    Bn, Sq, Hq, Hkv, D, lens, pos, qp, causal, bal = case
+    log(f"fuzz chunks {case}")
+    q, qh = seq_tensor(132, 0, Bn, Sq, Hq, D, "bf16")
+    do, doh = seq_tensor(132, 1, Bn, Sq, Hq, D, "bf16")
+    ks, vs, chunks_h = [], [], []
+    for c, L in enumerate(lens):
+        k, kh = seq_tensor(132, 10 + 2 * c, Bn, L, Hkv, D, "bf16")
+        v, vh = seq_tensor(132, 11 + 2 * c, Bn, L, Hkv, D, "bf16")
+        ks.append(k)
+        vs.append(v)
+        chunks_h.append((kh, vh, pos[c]))
+    scale = 1 / math.sqrt(D)
+    O_ref, L_ref = _oracle_over_chunks(qh, chunks_h, scale, causal, qp)
+    dq_ref = np.zeros(qh.shape)
+    dkv_ref = []
+    for kh, vh, p0 in chunks_h:
+        if kh.shape[1] == 0:
+            dkv_ref.append((np.zeros(kh.shape), np.zeros(vh.shape)))
+            continue
+        a, bk, bv = oracle.attention_backward(qh, kh, vh, O_ref, doh, L_ref, scale, causal, qp, p0)
+        dq_ref += a
+        dkv_ref.append((bk, bv))
+    o = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Bn, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_fwd_chunks(q, ks, vs, o, lse, chunk_pos0=pos, q_pos0=qp, causal=causal, balanced=bal)
+    dks = [torch.full_like(k, float("nan")) for k in ks]
+    dvs = [torch.full_like(v, float("nan")) for v in vs]
+    dq = torch.full_like(q, float("nan"))
+    dq_acc = torch.full((Bn, Sq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((B.attn_bwd_workspace_size(Bn, Hq, Sq) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.attn_bwd_chunks(q, ks, vs, o, do, lse, ws, dq_acc, dks, dvs, chunk_pos0=pos, dq=dq, q_pos0=qp, causal=causal,
+                      compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=bal)
+    torch.cuda.synchronize()
+    check("O", o, O_ref, O_TOL, scale_by_max=True)
+    check("LSE", lse, L_ref, L_TOL)
+    check("dQ", dq, dq_ref, G_TOL, scale_by_max=True)
+    for c, ((bk, bv), dk, dv) in enumerate(zip(dkv_ref, dks, dvs)):
+        check(f"dK[{c}]", dk, bk, G_TOL, scale_by_max=True)
+        check(f"dV[{c}]", dv, bv, G_TOL, scale_by_max=True)
+
+
+def _varlen_cases(n=12, seed=2029):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        nseq = int(rng.integers(1, 9))
+        lens = []
+        for _ in range(nseq):
+            lk = int(rng.integers(0, 400))
+            lq = lk if rng.random() < 0.5 else int(rng.integers(0, lk + 60))
+            lens.append((lq, lk))
+        out.append((tuple(lens), Hq, Hkv, int(rng.choice([64, 128])), i % 4 != 0, bool(rng.integers(0, 2))))
+    return out
+
+
+VARLEN_CASES = _varlen_cases()
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[str(i) for i in range(len(VARLEN_CASES))])
+def test_fuzz_varlen(case):
+    """Packed variable-length batches with random lengths (empty sequences, more queries than keys),
+    forward and backward, against the oracle on each sequence alone."""
+    from tests.test_gpu_small import test_varlen_fwd_bwd
+
+    test_varlen_fwd_bwd(case)
