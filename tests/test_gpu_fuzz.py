@@ -208,3 +208,34 @@ def test_fuzz_varlen(case):
     from tests.test_gpu_small import test_varlen_fwd_bwd
 
     test_varlen_fwd_bwd(case)
+
+
+def _tree_cases(n=10, seed=2030):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        nq = int(rng.integers(1, 60))
+        L = int(rng.integers(1, 8000))
+        nodes = []
+        for _ in range(int(rng.integers(1, 40))):
+            kl = int(rng.integers(0, min(L, 3000) + 1))
+            ks = int(rng.integers(0, L - kl + 1))
+            qb = int(rng.integers(0, nq))
+            qe = int(rng.integers(qb, nq + 1))
+            nodes.append((ks, kl, qb, qe))
+        out.append((nq, Hq, Hkv, int(rng.choice([64, 128])), L, tuple(nodes)))
+    return out
+
+
+TREE_CASES = _tree_cases()
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=[str(i) for i in range(len(TREE_CASES))])
+def test_fuzz_decode_tree(case):
+    """Random node sets (overlapping key ranges, empty nodes and query ranges, queries no node covers)
+    against the oracle over each query's concatenated node keys."""
+    from tests.test_gpu_small import test_decode_tree
+
+    test_decode_tree(case)
