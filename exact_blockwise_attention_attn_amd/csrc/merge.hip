@@ -46,9 +46,10 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p) {
   f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
   // The parts are read U at a time, all loads issued before the batch is
   // folded in part order (the arithmetic is that of one part at a time): with
-  // one load in flight per fold the pass was latency-bound (4.74 against
-  // 5.0 TB/s on 17 parts of 64 MiB).  Indices past the last part re-read it
-  // and are not folded.
+  // one load in flight per fold the pass was latency-bound (4.75 TB/s on 17
+  // parts of 64 MiB; 5.0 batched, 5.15 with the sequential mode's batches
+  // double-buffered).  Indices past the last part re-read it and are not
+  // folded.
   constexpr int U = 8;
   float xl[U];
   f32x4 xo[U];
@@ -61,11 +62,17 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeParams p) {
     }
   };
   if (!p.tree) {
+    // Double-buffered: the next batch's loads are issued before this one is folded.
+    load_batch(0);
     for (int i0 = 0; i0 < p.n_parts; i0 += U) {
-      load_batch(i0);
+      float cl[U];
+      f32x4 co[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cl[u] = xl[u], co[u] = xo[u];
+      if (i0 + U < p.n_parts) load_batch(i0 + U);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i0 + u < p.n_parts) merge2(L, O, xl[u], xo[u]);
+        if (i0 + u < p.n_parts) merge2(L, O, cl[u], co[u]);
     }
   } else {
     float sl[kMaxLevels];
