@@ -59,8 +59,10 @@
  *     to the outputs that depend on them (see the definitions above), so this
  *     also reports non-finite inputs where they are read.  The scan shares one
  *     small device buffer per device; checked calls are serialised within the
- *     process.  ATTN_LOG (set, and not "0") writes one line to stderr per
- *     enqueued call, naming the call and its sizes.
+ *     process.  Both variables make calls wait for `stream`, so neither may be
+ *     set while `stream` is being captured into a graph.  ATTN_LOG (set, and
+ *     not "0") writes one line to stderr per enqueued call, naming the call and
+ *     its sizes.
  *   - Every argument is checked on the host before anything is enqueued; on
  *     error the call returns a nonzero status, enqueues nothing, leaves every
  *     output untouched and records a message for attn_last_error().  This
