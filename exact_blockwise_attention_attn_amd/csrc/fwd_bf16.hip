@@ -6,8 +6,10 @@
 // blockwise computation of ring-style attention, as a partial (O, LSE).
 //
 // Layout of the work:
-//   * one workgroup = 4 wavefronts = 128 queries of one (batch, head); each
-//     wavefront owns 32 queries; two workgroups share a CU;
+//   * each wavefront owns 32 queries of one (batch, head); a workgroup of 8
+//     wavefronts (256 queries, one per CU) in the dense and chunk-table
+//     kernels, of 4 (128 queries, two per CU) in the variable-length and tree
+//     kernels;
 //   * key and value tiles of 64 rows go straight from HBM to LDS
 //     (global_load_lds, no register staging), double buffered: the next tile
 //     streams in while the current one is used.  Chunks are swizzled so both
@@ -34,9 +36,17 @@
 namespace attn {
 namespace {
 
-constexpr int BM = 128;  // queries per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup
+// A wavefront owns 32 query rows.  The dense and chunk-table kernels run 8
+// wavefronts (256 rows share each key/value tile in LDS, half the tile loads
+// per query of 4 wavefronts); the variable-length and tree kernels run 4 (128
+// rows), since their short sequences and small nodes would leave larger tiles
+// mostly empty.
+constexpr int NW_DENSE = 8, NW_SHORT = 4;
+constexpr int BM = 32 * NW_SHORT;  // query rows per workgroup, variable-length and tree kernels
+constexpr int NT = 64 * NW_SHORT;  // threads per workgroup, variable-length and tree kernels
+constexpr int BM_D = 32 * NW_DENSE;  // the same, dense and chunk-table kernels
+constexpr int NT_D = 64 * NW_DENSE;
+constexpr int BN = 64;  // keys per tile
 #ifndef SB_AHEAD_PV
 #define SB_AHEAD_PV 3
 #endif
@@ -193,7 +203,7 @@ __device__ __forceinline__ void fwd_store(const FwdParams& p, const f32x16* oacc
 // h.  With PACK (non-causal only) the rows are the queries of a whole GQA group:
 // row r is query r / group of head h + r % group, so the group's heads share
 // every key and value tile, and p.Sq counts rows (queries x group).
-template <int D, bool PACK = false>
+template <int D, int NW, bool PACK = false>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s, u16* k1s, u16* v1s, int qt, int b,
                                          int h, const u16* qb, const u16* kb, const u16* vb) {
   constexpr int NS = D / 16;
@@ -201,7 +211,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 31, lg = lane >> 5;
 
-  const int q0 = qt * BM;
+  const int q0 = qt * 32 * NW;
   const int qi = q0 + wave * 32 + lr;
   const bool qok = qi < p.Sq;
   int q_row = qi, h_row = h;  // query and head of this lane's row
@@ -212,7 +222,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
 
   // Keys [0, kv_end) are visible to some query of this tile; keys [0, full_end)
   // to all of them.  Causal visibility: key j is visible to query i iff j <= delta + i.
-  const int q_last = min(q0 + BM, p.Sq) - 1;
+  const int q_last = min(q0 + 32 * NW, p.Sq) - 1;
   int kv_end = p.Sk, full_end = p.Sk;
   int64_t lim64 = (int64_t)p.Sk - 1;
   if (!PACK && p.causal) {
@@ -221,7 +231,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
     lim64 = min<int64_t>(p.delta + qi, lim64);
   }
   const int n_tiles = (kv_end + BN - 1) / BN;
-  TileSrc<D, 4> ksrc, vsrc;
+  TileSrc<D, NW> ksrc, vsrc;
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
   auto issue = [&](u16* ks, u16* vs, int key0) {
@@ -269,7 +279,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, u16* k0s, u16* v0s,
 }
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NT_D) void fwd_bf16_kernel(FwdParams p) {
   // Two separate LDS objects per buffer so the compiler can tell the tile being
   // read from the tile being filled.
   __shared__ __attribute__((aligned(16))) u16 k0s[SwTile<D>::SIZE];
@@ -287,12 +297,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdParams p) {
   if (p.balanced) {
     // Pair an early and a late query tile so every workgroup carries the same causal work.
     const int t0 = unit, t1 = p.n_qtiles - 1 - unit;
-    fwd_tile<D>(p, k0s, v0s, k1s, v1s, t1, b, h, qb, kb, vb);
-    if (t0 != t1) fwd_tile<D>(p, k0s, v0s, k1s, v1s, t0, b, h, qb, kb, vb);
+    fwd_tile<D, NW_DENSE>(p, k0s, v0s, k1s, v1s, t1, b, h, qb, kb, vb);
+    if (t0 != t1) fwd_tile<D, NW_DENSE>(p, k0s, v0s, k1s, v1s, t0, b, h, qb, kb, vb);
   } else {
     // Causal: heaviest tiles first, so the light ones fill the tail.
     const int qt = p.causal ? p.n_qtiles - 1 - unit : unit;
-    fwd_tile<D>(p, k0s, v0s, k1s, v1s, qt, b, h, qb, kb, vb);
+    fwd_tile<D, NW_DENSE>(p, k0s, v0s, k1s, v1s, qt, b, h, qb, kb, vb);
   }
 }
 
@@ -326,12 +336,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_varlen_kernel(FwdParams p) {
   if (p.balanced) {
     const int t0 = unit, t1 = s.n_qtiles - 1 - unit;
     if (t1 < t0) return;
-    fwd_tile<D>(s, k0s, v0s, k1s, v1s, t1, 0, h, qb, kb, vb);
-    if (t0 != t1) fwd_tile<D>(s, k0s, v0s, k1s, v1s, t0, 0, h, qb, kb, vb);
+    fwd_tile<D, NW_SHORT>(s, k0s, v0s, k1s, v1s, t1, 0, h, qb, kb, vb);
+    if (t0 != t1) fwd_tile<D, NW_SHORT>(s, k0s, v0s, k1s, v1s, t0, 0, h, qb, kb, vb);
   } else {
     if (unit >= s.n_qtiles) return;
     const int qt = p.causal ? s.n_qtiles - 1 - unit : unit;
-    fwd_tile<D>(s, k0s, v0s, k1s, v1s, qt, 0, h, qb, kb, vb);
+    fwd_tile<D, NW_SHORT>(s, k0s, v0s, k1s, v1s, qt, 0, h, qb, kb, vb);
   }
 }
 
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(NT, 2) void tree_fwd_kernel(FwdParams p, TreeTable 
   const u16* qb = (const u16*)p.q.ptr + (int64_t)tt.q_begin[n] * p.q.ss + (int64_t)h0 * p.q.sh;
   const u16* kb = (const u16*)p.k.ptr + tt.kv_start[n] * p.k.ss + (int64_t)hk * p.k.sh;
   const u16* vb = (const u16*)p.v.ptr + tt.kv_start[n] * p.v.ss + (int64_t)hk * p.v.sh;
-  fwd_tile<D, true>(s, k0s, v0s, k1s, v1s, unit, 0, h0, qb, kb, vb);
+  fwd_tile<D, NW_SHORT, true>(s, k0s, v0s, k1s, v1s, unit, 0, h0, qb, kb, vb);
 }
 
 // One workgroup per (query, head), one thread per feature.  The first
@@ -455,16 +465,16 @@ __device__ __forceinline__ void wait_vm() {
 // Barrier for LDS data only; the tile prefetch stays in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTable& ct, u16* k_s, u16* v_s, int qt,
                                                int b, int h, int hk, const u16* qb) {
   constexpr int NS = D / 16, NDB = D / 32, SZ = SwTile<D>::SIZE;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 31, lg = lane >> 5;
-  const int q0 = qt * BM;
+  const int q0 = qt * 32 * NW;
   const int qi = q0 + wave * 32 + lr;
   const bool qok = qi < p.Sq;
-  const int q_last = min(q0 + BM, p.Sq) - 1;
+  const int q_last = min(q0 + 32 * NW, p.Sq) - 1;
 
   // Keys [0, kv_end) of chunk c are visible to some query of this tile, keys
   // [0, full_end) to all of them.
@@ -505,7 +515,7 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
   rf.init(lane);
   tf.init(lane);
 
-  TileSrc<D, 4> ksrc, vsrc;
+  TileSrc<D, NW> ksrc, vsrc;
   ksrc.init(p.k.ss, wave, lane);
   vsrc.init(p.v.ss, wave, lane);
   // What the steps need of a chunk, read from the table once per chunk (the
@@ -570,7 +580,7 @@ __device__ __forceinline__ void fwd_chunk_tile(const FwdParams& p, const ChunkTa
 }
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void fwd_chunks_kernel(FwdParams p, ChunkTable ct) {
+__global__ __launch_bounds__(NT_D) void fwd_chunks_kernel(FwdParams p, ChunkTable ct) {
   __shared__ __attribute__((aligned(16))) u16 k_s[2 * SwTile<D>::SIZE];
   __shared__ __attribute__((aligned(16))) u16 v_s[2 * SwTile<D>::SIZE];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -585,16 +595,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_chunks_kernel(FwdParams p, ChunkTab
   const int n = (p.balanced && last != unit) ? 2 : 1;
   for (int k = 0; k < n; ++k) {
     const int qt = p.balanced ? (k == 0 ? last : unit) : (p.causal ? last : unit);
-    fwd_chunk_tile<D>(p, ct, k_s, v_s, qt, b, h, hk, qb);
+    fwd_chunk_tile<D, NW_DENSE>(p, ct, k_s, v_s, qt, b, h, hk, qb);
   }
 }
 
 }  // namespace
 
 int64_t items_fwd_bf16(const FwdParams& p) {
-  const int64_t n_qtiles = (p.Sq + BM - 1) / BM;
+  const int bm = p.cu_q ? BM : BM_D, nt = p.cu_q ? NT : NT_D;
+  const int64_t n_qtiles = (p.Sq + bm - 1) / bm;
   const int64_t n_units = p.balanced ? (n_qtiles + 1) / 2 : n_qtiles;
-  return (int64_t)p.B * p.Hq * n_units * NT;
+  return (int64_t)p.B * p.Hq * n_units * nt;
 }
 
 // Row tiles of the tree pass over all segments; with u0, fills the prefix.
@@ -614,20 +625,21 @@ int64_t items_tree_decode(const FwdParams& p, const TreeTable& tt, int n_q, int 
 
 hipError_t launch_fwd_chunks_bf16(const FwdParams& p0, const ChunkTable& ct, int D, hipStream_t s) {
   FwdParams p = p0;
-  p.n_qtiles = (p.Sq + BM - 1) / BM;
+  p.n_qtiles = (p.Sq + BM_D - 1) / BM_D;
   p.n_units = p.balanced ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   const int64_t grid = (int64_t)p.B * p.Hq * p.n_units;
   if (grid == 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL(fwd_chunks_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p, ct);
+    hipLaunchKernelGGL(fwd_chunks_kernel<128>, dim3((unsigned)grid), dim3(NT_D), 0, s, p, ct);
   else
-    hipLaunchKernelGGL(fwd_chunks_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p, ct);
+    hipLaunchKernelGGL(fwd_chunks_kernel<64>, dim3((unsigned)grid), dim3(NT_D), 0, s, p, ct);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
   FwdParams p = p0;
-  p.n_qtiles = (p.Sq + BM - 1) / BM;
+  const int bm = p.cu_q ? BM : BM_D;
+  p.n_qtiles = (p.Sq + bm - 1) / bm;
   p.n_units = p.balanced ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   const int64_t grid = (int64_t)p.B * p.Hq * p.n_units;
   if (grid == 0) return hipSuccess;
@@ -639,9 +651,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p0, int D, hipStream_t s) {
     return hipGetLastError();
   }
   if (D == 128)
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(NT_D), 0, s, p);
   else
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(NT_D), 0, s, p);
   return hipGetLastError();
 }
 
