@@ -28,6 +28,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 HOST_ASAN_LIB_PATH = os.path.join(BUILD_DIR, "libattn_host_asan.so")
+# A plain C program that drives the library through its C ABI (examples/c_forward.c).
+C_EXAMPLE_SRC = os.path.join(PKG, "examples", "c_forward.c")
+C_EXAMPLE_PATH = os.path.join(PKG, "bin", "c_forward")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -86,7 +90,22 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_c_example()
     return LIB_PATH
+
+
+def build_c_example() -> str:
+    """Compile examples/c_forward.c with the system C compiler against include/attn.h, the HIP runtime
+    and the in-tree libattn.so (found next to the binary's directory at run time)."""
+    os.makedirs(os.path.dirname(C_EXAMPLE_PATH), exist_ok=True)
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), C_EXAMPLE_SRC,
+           "-o", C_EXAMPLE_PATH, "-L", PKG, "-lattn", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C example build failed:\n{res.stdout}\n{res.stderr}")
+    return C_EXAMPLE_PATH
 
 
 def build_host_asan(jobs: int | None = None) -> str:
