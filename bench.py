@@ -21,8 +21,12 @@ Prints one JSON line.  Besides the contract fields it carries:
                 throughput: the MFMA kernels run at the chip's power limit, so
                 their speed follows the clock it holds, which varies by box;
   secondary     the other workloads: the 128K sequence shard forward over 32
-                chunks, its backward, and split-KV GQA decode (GB/s of K/V,
-                also as a fraction of a plain 1 GiB device copy's bandwidth);
+                chunks, its backward, split-KV GQA decode (GB/s of K/V, also
+                as a fraction of a plain 1 GiB device copy's bandwidth), the
+                fp32 workload, the packed variable-length batch and tree
+                decode; each timed as the median of its calls (HIP events,
+                at least 10 timed calls after 3 warm-up ones; 20 for decode,
+                100 for the fp32 workload);
   cpu_baseline  the fp64 oracle, unmodified, on bounded samples of each workload
                 on the host's cores (value: one full (batch, head) of the
                 causal 32K workload, forward + backward), with the host's
@@ -80,8 +84,9 @@ def randn_bf16(shape, gen):
     return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
 
 
-def time_calls(fns, steps, warmup, stream):
-    """Run each step's calls in order; returns per-call average ms and the wall ms per step."""
+def time_calls(fns, steps, warmup, stream, stat="mean"):
+    """Run each step's calls in order; returns per-call ms (the mean over the steps, or the median with
+    stat="median") and the wall ms per step."""
     import torch
 
     for _ in range(warmup):
@@ -98,7 +103,11 @@ def time_calls(fns, steps, warmup, stream):
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps for i in range(len(fns))]
+    times = [sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) for i in range(len(fns))]
+    if stat == "median":
+        per = [t[(steps - 1) // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2]) for t in times]
+    else:
+        per = [sum(t) / steps for t in times]
     return per, wall
 
 
@@ -269,7 +278,8 @@ def bench_shard(args, stream, do_bwd):
 
     f_fwd = 4.0 * SQ * SK * D * H / 2.0  # the stated convention: halved for causal
     if not do_bwd:
-        (t, tf, tp, tm), _ = time_calls([fwd, fwd_fused, partials, merge], max(3, args.steps), 1, stream)
+        (t, tf, tp, tm), _ = time_calls([fwd, fwd_fused, partials, merge], max(10, args.steps), 3, stream,
+                                        stat="median")
         # The headline figure is the chunk loop as one call over the chunk table (attn_fwd_chunks); the
         # chained per-chunk calls and the partials-then-merge form are reported beside it.
         return {"workload": "shard_fwd_128k", "method": "attn_fwd_chunks over the 32-chunk table", "ms": tf,
@@ -294,7 +304,7 @@ def bench_shard(args, stream, do_bwd):
         shard.shard_backward_fused(q, k, v, o, do, lse, CH, q_pos0=QP, causal=True, stream=stream, dq=dq, dk=dk,
                                    dv=dv, dq_acc=dq_acc, workspace=ws)
 
-    (t, tf), _ = time_calls([bwd, bwd_fused], max(3, args.steps), 1, stream)
+    (t, tf), _ = time_calls([bwd, bwd_fused], max(10, args.steps), 3, stream, stat="median")
     f_bwd = 2.5 * f_fwd
     return {"workload": "shard_bwd_128k", "method": "attn_bwd_chunks over the 32-chunk table", "ms": tf,
             "tflops": f_bwd / tf / 1e9, "frac_mfma": f_bwd / tf / 1e9 / MFMA_BF16_PEAK_TFLOPS,
@@ -326,7 +336,7 @@ def bench_fp32_small(args, stream):
     def bwd():
         shard.shard_backward(q, k, v, o, do, lse, CH, stream=stream, dq=dq, dk=dk, dv=dv, dq_acc=dq_acc, workspace=ws)
 
-    (tf, tb), _ = time_calls([fwd, bwd], 100, 10, stream)
+    (tf, tb), _ = time_calls([fwd, bwd], 100, 10, stream, stat="median")
     return {"workload": "fp32_s256_4chunks", "fwd_us": tf * 1e3, "bwd_us": tb * 1e3,
             "note": "4 chained chunk calls each way; latency-bound, no roofline"}
 
@@ -358,7 +368,7 @@ def bench_varlen(args, stream):
         binding.attn_bwd_varlen(q, k, v, o, do, lse, ws, dq_acc, dk, dv, cu, cu, mx, mx, dq=dq, causal=True,
                                 compute_delta=True, dq_overwrite=True, finalize_dq=True, balanced=True, stream=stream)
 
-    (tf, tb), _ = time_calls([fwd, bwd], max(3, args.steps), 1, stream)
+    (tf, tb), _ = time_calls([fwd, bwd], max(10, args.steps), 3, stream, stat="median")
     f_fwd = sum(causal_flops(1, H, L, D) for L in lens)
     f_bwd = 2.5 * f_fwd
     return {"workload": "varlen_packed_70k", "sequences": len(lens), "tokens": T, "fwd_ms": tf, "bwd_ms": tb,
@@ -407,7 +417,7 @@ def bench_tree_decode(args, stream):
     def flat():
         binding.attn_decode_splitkv(q, kp, vp, o2, l2, ws2, n_splits=ns, stream=stream)
 
-    (tt, tf), _ = time_calls([tree, flat], max(10, args.steps), 3, stream)
+    (tt, tf), _ = time_calls([tree, flat], max(20, args.steps), 3, stream, stat="median")
     uniq = 2.0 * L * Hkv * D * 2
     flat_bytes = 2.0 * nq * path * Hkv * D * 2
     return {"workload": "tree_decode_64q", "queries": nq, "nodes": len(nodes), "tree_ms": tt,
@@ -441,7 +451,7 @@ def bench_decode(args, stream):
     def dec_uneven():
         binding.attn_decode_splitkv(q, kc, vc, o, lse, ws, n_splits=NS, seqlens=seqlens, stream=stream)
 
-    (t, tu), _ = time_calls([dec, dec_uneven], max(10, args.steps), 3, stream)
+    (t, tu), _ = time_calls([dec, dec_uneven], max(20, args.steps), 3, stream, stat="median")
     kv_bytes = 2.0 * B * L * HKV * D * 2
     gbs = kv_bytes / t / 1e6
     u_bytes = 2.0 * sum(lens) * HKV * D * 2
